@@ -1,0 +1,348 @@
+"""Pins of the fp64 oracle against facts other than itself (CPU only).
+
+Each test fixes part of the oracle with a closed form, a brute-force scalar
+evaluation, a library special case, an invariant, or values printed in a
+published specification / on the pages (fixtures under tests/golden/).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention as oatt
+from oracle import layouts as olay
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(12345)
+
+
+# ----------------------------------------------------------------------------- E4M3
+def test_e4m3_golden_points():
+    with open(os.path.join(GOLDEN, "e4m3_points.json")) as f:
+        pts = json.load(f)["points"]
+    codes = np.array([int(c, 16) for c, _ in pts], dtype=np.uint8)
+    got = oracle.decode_e4m3(codes)
+    for (c, want), g in zip(pts, got):
+        if want == "nan":
+            assert math.isnan(g), c
+        else:
+            assert g == want and math.copysign(1, g) == math.copysign(1, want), (c, g, want)
+
+
+def test_e4m3_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.decode_e4m3(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+
+
+# ----------------------------------------------------------------------------- closed forms
+def _counts(sq, skv, causal=False, window=None):
+    """Visible-key counts per row from interval arithmetic (no mask matrix)."""
+    out = []
+    for i in range(sq):
+        ip = i + skv - sq
+        lo, hi = 0, skv - 1
+        if causal:
+            hi = min(hi, ip)
+        if window is not None:
+            wl, wr = window
+            if wl >= 0:
+                lo = max(lo, ip - wl)
+            if wr >= 0:
+                hi = min(hi, ip + wr)
+        out.append(max(0, hi - lo + 1))
+    return np.array(out)
+
+
+@pytest.mark.parametrize("sq,skv,causal,window", [
+    (17, 17, False, None), (17, 17, True, None), (9, 23, True, None), (23, 9, True, None),
+    (31, 31, False, (5, 0)), (31, 31, True, (4, 2)), (12, 40, False, (3, 7)), (16, 16, False, (0, 0)),
+])
+def test_q_zero_gives_log_count_and_mean(sq, skv, causal, window):
+    d, dv = 8, 5
+    q = np.zeros((sq, d))
+    k = rng.standard_normal((skv, d))
+    v = rng.standard_normal((skv, dv))
+    vis = oatt.visible(sq, skv, causal=causal, window=window)
+    o, lse = oatt.attend(q, k, v, 0.3, vis)
+    n = _counts(sq, skv, causal, window)
+    for i in range(sq):
+        if n[i] == 0:
+            assert lse[i] == -np.inf and np.all(o[i] == 0)
+            continue
+        assert abs(lse[i] - math.log(n[i])) < 1e-12
+        ip = i + skv - sq
+        lo = 0 if window is None or window[0] < 0 else max(0, ip - window[0])
+        mean = v[lo:lo + n[i]].mean(axis=0)
+        assert np.allclose(o[i], mean, atol=1e-12)
+
+
+def test_q_zero_block_mask_counts():
+    sq = skv = 40
+    bq, bk = 8, 16
+    nqb, nkb = 5, 3
+    bm = (rng.random((nqb, nkb)) < 0.5).astype(np.uint8)
+    bm[2, :] = 0
+    vis = oatt.visible(sq, skv, block_mask=bm, mask_block=(bq, bk))
+    o, lse = oatt.attend(np.zeros((sq, 4)), rng.standard_normal((skv, 4)), rng.standard_normal((skv, 3)), 1.0, vis)
+    for i in range(sq):
+        n = sum(min(skv, (kb + 1) * bk) - kb * bk for kb in range(nkb) if bm[i // bq, kb])
+        if n == 0:
+            assert lse[i] == -np.inf
+        else:
+            assert abs(lse[i] - math.log(n)) < 1e-12
+
+
+@pytest.mark.parametrize("slope", [0.0625, 0.5, 1.7])
+def test_alibi_q_zero_geometric_series(slope):
+    m = 37
+    r = math.exp(-slope)
+    vis = oatt.visible(m, m)
+    _, lse = oatt.attend(np.zeros((m, 4)), rng.standard_normal((m, 4)), rng.standard_normal((m, 2)),
+                         1.0, vis, alibi_slope=slope, ip=np.arange(m))
+    for i in range(m):
+        # sum_{d=0}^{i} r^d + sum_{d=1}^{m-1-i} r^d
+        closed = (1 - r ** (i + 1)) / (1 - r) + r * (1 - r ** (m - 1 - i)) / (1 - r)
+        assert abs(lse[i] - math.log(closed)) < 1e-12
+
+
+def test_constant_v_gives_constant_output():
+    sq, skv, d, dv = 19, 27, 16, 6
+    c = rng.standard_normal(dv)
+    v = np.tile(c, (skv, 1))
+    for kw in [dict(), dict(causal=True), dict(window=(3, 1))]:
+        vis = oatt.visible(sq, skv, **kw)
+        o, lse = oatt.attend(rng.standard_normal((sq, d)) * 3, rng.standard_normal((skv, d)), v, 0.25, vis,
+                             softcap=5.0, alibi_slope=0.1, ip=np.arange(sq) + skv - sq)
+        has = vis.any(axis=1)
+        assert np.allclose(o[has], c, atol=1e-12)
+
+
+def test_single_visible_key_is_exact():
+    sq, d, dv = 21, 8, 8
+    q = rng.standard_normal((sq, d))
+    k = rng.standard_normal((sq, d))
+    v = rng.standard_normal((sq, dv))
+    vis = oatt.visible(sq, sq, window=(0, 0))
+    o, lse = oatt.attend(q, k, v, 0.5, vis)
+    for i in range(sq):
+        assert np.array_equal(o[i], v[i])
+        assert abs(lse[i] - 0.5 * sum(q[i, t] * k[i, t] for t in range(d))) < 1e-12
+
+
+def test_logit_shift_moves_lse_only():
+    """An extra feature with q-value a and k-value 1 adds scale*a to every logit of
+    the row: LSE moves by scale*a and O is unchanged."""
+    sq, skv, d, dv = 11, 14, 6, 4
+    q, k, v = rng.standard_normal((sq, d)), rng.standard_normal((skv, d)), rng.standard_normal((skv, dv))
+    a = rng.standard_normal(sq) * 4
+    vis = oatt.visible(sq, skv, causal=True)
+    o1, l1 = oatt.attend(q, k, v, 0.7, vis)
+    o2, l2 = oatt.attend(np.c_[q, a], np.c_[k, np.ones(skv)], v, 0.7, vis)
+    has = vis.any(axis=1)
+    assert np.allclose(o1, o2, atol=1e-12)
+    assert np.allclose(l2[has] - l1[has], 0.7 * a[has], atol=1e-12)
+
+
+def test_key_permutation_invariance():
+    sq, skv, d, dv = 9, 30, 8, 5
+    q, k, v = rng.standard_normal((sq, d)), rng.standard_normal((skv, d)), rng.standard_normal((skv, dv))
+    perm = rng.permutation(skv)
+    vis = np.ones((sq, skv), bool)
+    o1, l1 = oatt.attend(q, k, v, 0.4, vis, softcap=3.0)
+    o2, l2 = oatt.attend(q, k[perm], v[perm], 0.4, vis, softcap=3.0)
+    assert np.allclose(o1, o2, atol=1e-13) and np.allclose(l1, l2, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- brute force
+def _brute(q, k, v, scale, causal, window, softcap, slope, bm, mb):
+    sq, skv = len(q), len(k)
+    outs, lses = [], []
+    for i in range(sq):
+        ip = i + skv - sq
+        logits = {}
+        for j in range(skv):
+            if causal and j > ip:
+                continue
+            if window is not None:
+                if window[0] >= 0 and j < ip - window[0]:
+                    continue
+                if window[1] >= 0 and j > ip + window[1]:
+                    continue
+            if bm is not None and not bm[i // mb[0]][j // mb[1]]:
+                continue
+            s = scale * math.fsum(float(q[i][t]) * float(k[j][t]) for t in range(len(q[i])))
+            if softcap is not None:
+                s = softcap * math.tanh(s / softcap)
+            if slope is not None:
+                s -= slope * abs(ip - j)
+            logits[j] = s
+        if not logits:
+            outs.append([0.0] * len(v[0]))
+            lses.append(-math.inf)
+            continue
+        mx = max(logits.values())
+        den = math.fsum(math.exp(s - mx) for s in logits.values())
+        lse = mx + math.log(den)
+        outs.append([math.fsum(math.exp(s - lse) * float(v[j][c]) for j, s in logits.items())
+                     for c in range(len(v[0]))])
+        lses.append(lse)
+    return np.array(outs), np.array(lses)
+
+
+CASES = [
+    dict(causal=False, window=None, softcap=None, slope=None, bm=False),
+    dict(causal=True, window=None, softcap=None, slope=None, bm=False),
+    dict(causal=False, window=(3, 0), softcap=None, slope=None, bm=False),
+    dict(causal=True, window=(2, 5), softcap=2.5, slope=None, bm=False),
+    dict(causal=False, window=None, softcap=None, slope=0.3, bm=False),
+    dict(causal=False, window=None, softcap=1.5, slope=0.2, bm=True),
+    dict(causal=True, window=None, softcap=None, slope=None, bm=True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("sq,skv", [(13, 13), (7, 17), (17, 5)])
+def test_brute_force_small(case, sq, skv):
+    c = CASES[case]
+    d, dv = 5, 3
+    q, k, v = rng.standard_normal((sq, d)) * 2, rng.standard_normal((skv, d)), rng.standard_normal((skv, dv))
+    mb = (4, 3)
+    bm = (rng.random((math.ceil(sq / 4), math.ceil(skv / 3))) < 0.6).astype(np.uint8) if c["bm"] else None
+    vis = oatt.visible(sq, skv, causal=c["causal"], window=c["window"], block_mask=bm, mask_block=mb)
+    o, lse = oatt.attend(q, k, v, 0.45, vis, softcap=c["softcap"], alibi_slope=c["slope"],
+                         ip=np.arange(sq) + skv - sq)
+    ob, lb = _brute(q, k, v, 0.45, c["causal"], c["window"], c["softcap"], c["slope"], bm, mb)
+    assert np.array_equal(np.isinf(lse), np.isinf(lb))
+    fin = np.isfinite(lb)
+    assert np.allclose(lse[fin], lb[fin], atol=1e-12, rtol=0)
+    assert np.allclose(o, ob, atol=1e-12, rtol=0)
+
+
+def test_matches_torch_sdpa_fp64():
+    """torch's CPU fp64 scaled_dot_product_attention with a boolean mask for O,
+    and logsumexp of the masked logits for LSE."""
+    B, Sq, Skv, Hq, Hkv, D = 2, 33, 47, 4, 2, 16
+    q = torch.randn(B, Sq, Hq, D, dtype=torch.float64)
+    k = torch.randn(B, Skv, Hkv, D, dtype=torch.float64)
+    v = torch.randn(B, Skv, Hkv, D, dtype=torch.float64)
+    for causal in (False, True):
+        o, lse = oracle.attention_dense(q.numpy(), k.numpy(), v.numpy(), dict(causal=causal))
+        mask = torch.from_numpy(oatt.visible(Sq, Skv, causal=causal))
+        kk = k.repeat_interleave(Hq // Hkv, dim=2).transpose(1, 2)
+        vv = v.repeat_interleave(Hq // Hkv, dim=2).transpose(1, 2)
+        qq = q.transpose(1, 2)
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask).transpose(1, 2)
+        logits = (qq @ kk.transpose(-1, -2)) / math.sqrt(D)
+        ref_lse = torch.logsumexp(logits.masked_fill(~mask, -math.inf), dim=-1)
+        has = mask.any(dim=-1)
+        assert torch.allclose(torch.from_numpy(o)[:, has], ref[:, has], atol=1e-12)
+        assert torch.allclose(torch.from_numpy(lse)[..., has], ref_lse[..., has], atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- degenerate mods
+def test_degenerate_mods_reduce_to_plain():
+    sq = skv = 24
+    q, k, v = rng.standard_normal((sq, 8)), rng.standard_normal((skv, 8)), rng.standard_normal((skv, 4))
+    full = np.ones((sq, skv), bool)
+    o0, l0 = oatt.attend(q, k, v, 0.5, full)
+    o1, l1 = oatt.attend(q, k, v, 0.5, full, alibi_slope=0.0, ip=np.arange(sq))
+    o2, l2 = oatt.attend(q, k, v, 0.5, full, softcap=1e30)
+    vis3 = oatt.visible(sq, skv, window=(sq, sq))
+    vis4 = oatt.visible(sq, skv, block_mask=np.ones((2, 2), np.uint8), mask_block=(16, 16))
+    for o, l in [(o1, l1), (o2, l2), oatt.attend(q, k, v, 0.5, vis3), oatt.attend(q, k, v, 0.5, vis4)]:
+        assert np.allclose(o, o0, atol=1e-13) and np.allclose(l, l0, atol=1e-13)
+    # block-causal with unit tiles is token causal
+    bc = np.tril(np.ones((sq, skv), np.uint8))
+    assert np.array_equal(oatt.visible(sq, skv, block_mask=bc, mask_block=(1, 1)),
+                          oatt.visible(sq, skv, causal=True))
+
+
+def test_lse_merge_identity():
+    sq, skv, d, dv = 15, 50, 8, 6
+    q, k, v = rng.standard_normal((sq, d)) * 2, rng.standard_normal((skv, d)), rng.standard_normal((skv, dv))
+    vis = oatt.visible(sq, skv, causal=True)
+    o, lse = oatt.attend(q, k, v, 0.5, vis)
+    cuts = [0, 7, 7, 22, 50]          # includes an empty split
+    parts = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        sub = np.zeros_like(vis)
+        sub[:, a:b] = vis[:, a:b]
+        parts.append(oatt.attend(q, k, v, 0.5, sub))
+    om, lm = oatt.lse_merge(parts)
+    fin = np.isfinite(lse)
+    assert np.array_equal(fin, np.isfinite(lm))
+    assert np.allclose(lm[fin], lse[fin], atol=1e-12) and np.allclose(om, o, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- layouts
+def _np(t):
+    return t.float().numpy().astype(np.float64) if t.dtype == torch.bfloat16 else t.numpy()
+
+
+def test_varlen_equals_per_sequence_dense():
+    import synth
+    lens = [5, 0, 33, 64, 17]
+    d = synth.make_varlen(lens, lens, 4, 2, 16, 16, seed=7)
+    o, lse = oracle.attention_varlen(_np(d["q"]), _np(d["k"]), _np(d["v"]), d["cu_q"].numpy(), d["cu_k"].numpy(),
+                                     dict(causal=True))
+    cu = d["cu_q"].numpy()
+    for b, L in enumerate(lens):
+        if L == 0:
+            continue
+        sl = slice(cu[b], cu[b + 1])
+        od, ld = oracle.attention_dense(_np(d["q"])[None, sl], _np(d["k"])[None, sl], _np(d["v"])[None, sl],
+                                        dict(causal=True))
+        assert np.array_equal(od[0], o[sl]) and np.array_equal(ld[0], lse[:, sl])
+
+
+def test_paged_gather_index_arithmetic_and_placement_invariance():
+    import synth
+    lk = [70, 3, 128, 129]
+    lq = [5, 3, 1, 40]
+    d = synth.make_paged(lq, lk, 4, 2, 24, 16, page_size=16, seed=3, extra_pages=5)
+    kc, vc = d["k_cache"].numpy(), d["v_cache"].numpy()
+    bt = d["block_table"].numpy()
+    # gather equals explicit page/slot arithmetic, bytes identical
+    t0 = 0
+    for b, L in enumerate(lk):
+        for g in range(2):
+            got = olay.gather_paged(kc, bt[b], L, g)
+            want = np.stack([oracle.decode_e4m3(kc[bt[b][j // 16], g, j % 16]) for j in range(L)])
+            assert np.array_equal(np.isnan(got), np.isnan(want)) and np.array_equal(np.nan_to_num(got), np.nan_to_num(want))
+            assert np.array_equal(kc[bt[b][np.arange(L) // 16], g, np.arange(L) % 16], d["k_logical"][t0:t0 + L, g].numpy())
+        t0 += L
+    # result equals the varlen oracle on the logical (dequantised) KV
+    kd = oracle.decode_e4m3(d["k_logical"].numpy()) * float(d["k_descale"])
+    vd = oracle.decode_e4m3(d["v_logical"].numpy()) * float(d["v_descale"])
+    cu_k = np.concatenate([[0], np.cumsum(lk)])
+    mods = dict(causal=True)
+    o1, l1 = oracle.attention_paged(_np(d["q"]), kc, vc, d["cu_q"].numpy(), d["seqlen_k"].numpy(), bt, mods,
+                                    float(d["k_descale"]), float(d["v_descale"]))
+    o2, l2 = oracle.attention_varlen(_np(d["q"]), kd, vd, d["cu_q"].numpy(), cu_k, mods)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    assert not np.isnan(o1).any()
+
+
+def test_paged_4gib_golden_geometry():
+    """The pages' >4 GiB case: a page id of ceil(2^32/8192) puts both K and V
+    byte offsets past 2^32 for Hkv=1, page 64, K width 192 and V width 128 fp8."""
+    with open(os.path.join(GOLDEN, "paged_4gib_geometry.json")) as f:
+        gd = json.load(f)
+    geo = gd["geometry"]
+    kpb = geo["Hkv"] * geo["page_size"] * geo["d_qk"] * geo["bytes_per_elem"]
+    vpb = geo["Hkv"] * geo["page_size"] * geo["d_v"] * geo["bytes_per_elem"]
+    assert kpb + vpb == gd["page_bytes_k_plus_v"]
+    assert -(-(2 ** 32) // gd["value_page_divisor"]) == gd["high_page"]
+    assert gd["high_page"] + 1 == gd["num_pages"]
+    assert gd["num_pages"] * (kpb + vpb) == gd["cache_bytes"]
+    assert round(gd["cache_bytes"] / 1e9, 1) == gd["cache_bytes_approx_gb"]
+    assert gd["high_page"] * kpb >= 2 ** 32 and gd["high_page"] * vpb >= 2 ** 32
+    assert (gd["high_page"] - 1) * vpb < 2 ** 32
