@@ -1,0 +1,26 @@
+"""MI355X (gfx950) FlashAttention forward: thin Python binding over libfa.so.
+
+The functions here only marshal torch tensors into the C ABI declared in
+include/fa.h; every step of the computation runs in the HIP kernels of
+libfa.so.  Importing this package raises if the shared library has not been
+built (python -m attention_fa_fwd_03_amd.build): there is no fallback path.
+"""
+from .binding import (  # noqa: F401
+    FaError,
+    FA_CAUSAL,
+    FA_WINDOW,
+    FA_ALIBI,
+    FA_SOFTCAP,
+    FA_BLOCK_MASK,
+    FA_BF16,
+    FA_FP8_E4M3,
+    Mods,
+    fa_fwd_dense,
+    fa_fwd_varlen,
+    fa_fwd_paged,
+    fa_fwd_paged_workspace_size,
+    fa_last_error,
+    fa_abi_version,
+    library_path,
+    lib,
+)

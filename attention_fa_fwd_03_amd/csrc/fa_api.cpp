@@ -1,0 +1,407 @@
+// Host side of libfa: argument validation, shape specialisation and launch.
+//
+// Every check here runs before the first HIP call so that a rejected call
+// enqueues nothing (and the checks can be exercised without a GPU).  Nothing
+// in this file allocates memory, synchronises, or copies between host and
+// device: all metadata is consumed on the device, with the host-side maxima
+// passed by the caller.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+constexpr int64_t kI32 = (int64_t)1 << 31;
+constexpr int kBM = 128;           // prefill query rows per workgroup
+constexpr int kBN = 64;            // prefill keys per tile
+constexpr int kDecodeRows = 32;    // decode rows (query x q-head-in-group) per wavefront
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+struct Mods {
+  uint32_t flags = 0;
+  float scale = 0.f;
+  float slope = 0.f;
+  float cap = 0.f;
+  int64_t wl = -1, wr = -1;
+  const uint8_t* bm = nullptr;
+  int64_t bq = 0, bk = 0, nqb = 0, nkb = 0;
+};
+
+int read_mods(const fa_mods* m, int64_t d_qk, int64_t max_sq, int64_t max_sk, Mods* out) {
+  Mods r;
+  if (m) {
+    const uint32_t known = FA_CAUSAL | FA_WINDOW | FA_ALIBI | FA_SOFTCAP | FA_BLOCK_MASK;
+    if (m->flags & ~known) return fail(FA_ERR_INVALID, "unknown fa_mods flag bits 0x%x", m->flags & ~known);
+    r.flags = m->flags;
+    r.scale = m->softmax_scale;
+    if (!(r.scale == r.scale)) return fail(FA_ERR_INVALID, "softmax_scale is NaN");
+    if (r.flags & FA_ALIBI) {
+      r.slope = m->alibi_slope;
+      if (!std::isfinite(r.slope)) return fail(FA_ERR_INVALID, "alibi_slope must be finite");
+    }
+    if (r.flags & FA_SOFTCAP) {
+      r.cap = m->softcap;
+      if (!(r.cap > 0.f) || !std::isfinite(r.cap)) return fail(FA_ERR_INVALID, "softcap must be finite and > 0");
+    }
+    if (r.flags & FA_WINDOW) {
+      r.wl = m->window_left;
+      r.wr = m->window_right;
+    }
+    if (r.flags & FA_BLOCK_MASK) {
+      r.bm = m->block_mask;
+      r.bq = m->mask_block_q;
+      r.bk = m->mask_block_k;
+      r.nqb = m->mask_nqb;
+      r.nkb = m->mask_nkb;
+      if (!r.bm) return fail(FA_ERR_INVALID, "FA_BLOCK_MASK set but block_mask is NULL");
+      if (r.bq <= 0 || r.bk <= 0 || r.bq % kBM != 0 || r.bk % kBN != 0)
+        return fail(FA_ERR_UNSUPPORTED, "block mask tiles must be multiples of %d (query) and %d (key), got %lld x %lld",
+                    kBM, kBN, (long long)r.bq, (long long)r.bk);
+      if (r.nqb < (max_sq + r.bq - 1) / r.bq || r.nkb < (max_sk + r.bk - 1) / r.bk)
+        return fail(FA_ERR_INVALID, "block mask geometry %lld x %lld does not cover %lld x %lld tokens",
+                    (long long)r.nqb, (long long)r.nkb, (long long)max_sq, (long long)max_sk);
+      if (r.nqb >= kI32 || r.nkb >= kI32 || r.bq >= kI32 || r.bk >= kI32)
+        return fail(FA_ERR_LIMIT, "block mask geometry exceeds int32");
+    }
+  }
+  if (!(r.scale > 0.f)) r.scale = 1.0f / std::sqrt((float)d_qk);
+  if (!std::isfinite(r.scale)) return fail(FA_ERR_INVALID, "softmax_scale must be finite");
+  *out = r;
+  return FA_OK;
+}
+
+int clamp_i32(int64_t w) {
+  if (w < 0) return -1;
+  return w >= INT_MAX / 2 ? INT_MAX / 2 : (int)w;
+}
+
+bool prefill_dims_built(int64_t dqk, int64_t dv, bool fp8, bool paged) {
+  if (fp8) return paged && ((dqk == 192 && dv == 128) || (dqk == 128 && dv == 128));
+  return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128);
+}
+
+void fill_mods(fa::PrefillArgs& a, const Mods& m) {
+  a.qk_scale = m.scale;
+  a.alibi_slope = m.slope;
+  a.softcap = m.cap;
+  a.causal = (m.flags & FA_CAUSAL) ? 1 : 0;
+  a.win_left = (m.flags & FA_WINDOW) ? clamp_i32(m.wl) : -1;
+  a.win_right = (m.flags & FA_WINDOW) ? clamp_i32(m.wr) : -1;
+  a.bmask = (m.flags & FA_BLOCK_MASK) ? m.bm : nullptr;
+  a.bm_bq = (int)m.bq;
+  a.bm_bk = (int)m.bk;
+  a.bm_nqb = (int)m.nqb;
+  a.bm_nkb = (int)m.nkb;
+}
+
+int mod_bits(const Mods& m) {
+  return ((m.flags & FA_ALIBI) ? fa::kModAlibi : 0) | ((m.flags & FA_SOFTCAP) ? fa::kModSoftcap : 0);
+}
+
+int launch_prefill(const fa::PrefillArgs& a, int64_t dqk, int64_t dv, bool fp8, bool paged, int mods,
+                   int64_t B, int64_t Hq, int64_t max_sq, hipStream_t stream) {
+  const int64_t n_bh = B * Hq;
+  const int64_t n_qt = (max_sq + kBM - 1) / kBM;
+  if (n_bh >= kI32) return fail(FA_ERR_LIMIT, "B*Hq = %lld exceeds the grid limit", (long long)n_bh);
+  if (n_qt > 65535) return fail(FA_ERR_LIMIT, "max_seqlen_q = %lld exceeds %d", (long long)max_sq, 65535 * kBM);
+  if (n_bh == 0 || n_qt == 0) return FA_OK;
+  bool supported = false;
+  hipError_t e = fa::prefill_dispatch(a, (int)dqk, (int)dv, fp8, paged, mods, (int)n_bh, (int)n_qt, stream, &supported);
+  if (!supported) return fail(FA_ERR_UNSUPPORTED, "no kernel built for d_qk=%lld d_v=%lld fp8=%d paged=%d mods=%d",
+                              (long long)dqk, (long long)dv, (int)fp8, (int)paged, mods);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+int check_common(int64_t B, int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v) {
+  if (B < 0) return fail(FA_ERR_INVALID, "B must be >= 0");
+  if (Hq <= 0 || Hkv <= 0) return fail(FA_ERR_INVALID, "head counts must be positive (Hq=%lld Hkv=%lld)", (long long)Hq, (long long)Hkv);
+  if (Hq % Hkv != 0) return fail(FA_ERR_INVALID, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
+  if (d_qk <= 0 || d_v <= 0) return fail(FA_ERR_INVALID, "head dims must be positive");
+  if (B >= kI32 || Hq >= kI32) return fail(FA_ERR_LIMIT, "B or Hq exceeds int32");
+  return FA_OK;
+}
+
+// Decode path geometry: keys are split into chunks of split_len.
+struct SplitPlan {
+  int64_t split_len = 0, n_split = 0;
+};
+
+SplitPlan plan_splits(int64_t B, int64_t Hkv, int64_t max_sk) {
+  SplitPlan p;
+  int64_t target = (max_sk * B * Hkv) / 16384;
+  int64_t len = 256;
+  while (len < target && len < 2048) len *= 2;
+  p.split_len = len;
+  p.n_split = max_sk > 0 ? (max_sk + len - 1) / len : 1;
+  return p;
+}
+
+bool uses_decode(int64_t max_sq, int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v, fa_dtype kv, int64_t page_size) {
+  if (kv != FA_FP8_E4M3 || d_v != 128 || (d_qk != 192 && d_qk != 128)) return false;
+  if (page_size < 32) return false;   // the decode kernel looks pages up once per 32-key tile
+  return max_sq >= 1 && max_sq * (Hq / Hkv) <= kDecodeRows;
+}
+
+size_t workspace_bytes(int64_t B, int64_t total_q, int64_t max_sq, int64_t max_sk, int64_t Hq, int64_t Hkv,
+                       int64_t d_qk, int64_t d_v, fa_dtype kv, int64_t page_size) {
+  if (Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0) return 0;
+  if (!uses_decode(max_sq, Hq, Hkv, d_qk, d_v, kv, page_size)) return 0;
+  const SplitPlan p = plan_splits(B, Hkv, max_sk);
+  return (size_t)p.n_split * (size_t)total_q * (size_t)Hq * (size_t)(d_v + 1) * sizeof(float) + 256;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_last_error(void) { return g_err.c_str(); }
+
+int fa_abi_version(void) { return 1; }
+
+int fa_fwd_dense(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int64_t B, int64_t Sq, int64_t Skv, int64_t Hq, int64_t Hkv,
+                 int64_t d_qk, int64_t d_v, const fa_mods* mods, void* stream) {
+  g_err.clear();
+  int rc = check_common(B, Hq, Hkv, d_qk, d_v);
+  if (rc) return rc;
+  if (Sq < 0 || Skv < 0) return fail(FA_ERR_INVALID, "sequence lengths must be >= 0");
+  if (Sq >= kI32 || Skv >= kI32 || B * Sq >= kI32 || B * Skv >= kI32)
+    return fail(FA_ERR_LIMIT, "token counts must stay below 2^31");
+  Mods m;
+  if ((rc = read_mods(mods, d_qk, Sq, Skv, &m))) return rc;
+  if (!prefill_dims_built(d_qk, d_v, false, false))
+    return fail(FA_ERR_UNSUPPORTED, "dense bf16 head dims (%lld, %lld) not built; built: (64,64), (128,128)",
+                (long long)d_qk, (long long)d_v);
+  if (B == 0 || Sq == 0) return FA_OK;
+  if (!q || !o || !lse) return fail(FA_ERR_INVALID, "q, o and lse must be non-NULL");
+  if (Skv > 0 && (!k || !v)) return fail(FA_ERR_INVALID, "k and v must be non-NULL");
+  const size_t nq = (size_t)(B * Sq * Hq * d_qk) * 2, no = (size_t)(B * Sq * Hq * d_v) * 2;
+  const size_t nk = (size_t)(B * Skv * Hkv * d_qk) * 2, nv = (size_t)(B * Skv * Hkv * d_v) * 2;
+  const size_t nl = (size_t)(B * Hq * Sq) * 4;
+  if (overlaps(o, no, lse, nl)) return fail(FA_ERR_INVALID, "lse must not overlap o");
+  if (overlaps(o, no, q, nq) || overlaps(o, no, k, nk) || overlaps(o, no, v, nv) ||
+      overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nk) || overlaps(lse, nl, v, nv))
+    return fail(FA_ERR_INVALID, "outputs must not overlap inputs");
+  fa::PrefillArgs a{};
+  a.q = (const __bf16*)q;
+  a.k = k;
+  a.v = v;
+  a.o = (__bf16*)o;
+  a.lse = lse;
+  a.q_st = Hq * d_qk; a.q_sh = d_qk;
+  a.k_st = Hkv * d_qk; a.k_sh = d_qk;
+  a.v_st = Hkv * d_v; a.v_sh = d_v;
+  a.o_st = Hq * d_v; a.o_sh = d_v;
+  a.Sq = (int)Sq; a.Skv = (int)Skv;
+  a.Hq = (int)Hq; a.group = (int)(Hq / Hkv);
+  fill_mods(a, m);
+  return launch_prefill(a, d_qk, d_v, false, false, mod_bits(m), B, Hq, Sq, (hipStream_t)stream);
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t B,
+                  int64_t total_q, int64_t total_k, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                  int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v,
+                  const fa_mods* mods, void* stream) {
+  g_err.clear();
+  int rc = check_common(B, Hq, Hkv, d_qk, d_v);
+  if (rc) return rc;
+  if (total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(FA_ERR_INVALID, "token counts must be >= 0");
+  if (max_seqlen_q > total_q || max_seqlen_k > total_k)
+    return fail(FA_ERR_INVALID, "max_seqlen exceeds the packed token count");
+  if (total_q >= kI32 || total_k >= kI32) return fail(FA_ERR_LIMIT, "token counts must stay below 2^31");
+  Mods m;
+  if ((rc = read_mods(mods, d_qk, max_seqlen_q, max_seqlen_k, &m))) return rc;
+  if (!prefill_dims_built(d_qk, d_v, false, false))
+    return fail(FA_ERR_UNSUPPORTED, "varlen bf16 head dims (%lld, %lld) not built; built: (64,64), (128,128)",
+                (long long)d_qk, (long long)d_v);
+  if (B == 0 || total_q == 0) return FA_OK;
+  if (!q || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return fail(FA_ERR_INVALID, "q, o, lse and cu_seqlens must be non-NULL");
+  if (total_k > 0 && (!k || !v)) return fail(FA_ERR_INVALID, "k and v must be non-NULL");
+  const size_t nq = (size_t)(total_q * Hq * d_qk) * 2, no = (size_t)(total_q * Hq * d_v) * 2;
+  const size_t nk = (size_t)(total_k * Hkv * d_qk) * 2, nv = (size_t)(total_k * Hkv * d_v) * 2;
+  const size_t nl = (size_t)(Hq * total_q) * 4;
+  if (overlaps(o, no, lse, nl)) return fail(FA_ERR_INVALID, "lse must not overlap o");
+  if (overlaps(o, no, q, nq) || overlaps(o, no, k, nk) || overlaps(o, no, v, nv) ||
+      overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nk) || overlaps(lse, nl, v, nv))
+    return fail(FA_ERR_INVALID, "outputs must not overlap inputs");
+  fa::PrefillArgs a{};
+  a.q = (const __bf16*)q;
+  a.k = k;
+  a.v = v;
+  a.o = (__bf16*)o;
+  a.lse = lse;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.q_st = Hq * d_qk; a.q_sh = d_qk;
+  a.k_st = Hkv * d_qk; a.k_sh = d_qk;
+  a.v_st = Hkv * d_v; a.v_sh = d_v;
+  a.o_st = Hq * d_v; a.o_sh = d_v;
+  a.lse_tq = total_q;
+  a.Hq = (int)Hq; a.group = (int)(Hq / Hkv);
+  fill_mods(a, m);
+  return launch_prefill(a, d_qk, d_v, false, false, mod_bits(m), B, Hq, max_seqlen_q, (hipStream_t)stream);
+}
+
+size_t fa_fwd_paged_workspace_size(int64_t B, int64_t total_q, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                                   int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v, int64_t page_size,
+                                   fa_dtype kv_dtype) {
+  return workspace_bytes(B, total_q, max_seqlen_q, max_seqlen_k, Hq, Hkv, d_qk, d_v, kv_dtype, page_size);
+}
+
+int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                 const int32_t* cu_seqlens_q, const int32_t* seqlen_k, const int32_t* block_table,
+                 int64_t B, int64_t total_q, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                 int64_t num_pages, int64_t page_size, int64_t max_pages_per_seq,
+                 int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v, fa_dtype kv_dtype,
+                 const float* k_descale, const float* v_descale,
+                 void* workspace, size_t workspace_bytes_in,
+                 const fa_mods* mods, void* stream) {
+  g_err.clear();
+  int rc = check_common(B, Hq, Hkv, d_qk, d_v);
+  if (rc) return rc;
+  if (kv_dtype != FA_BF16 && kv_dtype != FA_FP8_E4M3) return fail(FA_ERR_INVALID, "unknown kv_dtype %d", (int)kv_dtype);
+  if (total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_pages < 0 || max_pages_per_seq < 0)
+    return fail(FA_ERR_INVALID, "sizes must be >= 0");
+  if (max_seqlen_q > total_q) return fail(FA_ERR_INVALID, "max_seqlen_q exceeds total_q");
+  if (page_size < 1 || page_size > 1024 || (page_size & (page_size - 1)))
+    return fail(FA_ERR_UNSUPPORTED, "page_size must be a power of two in [1, 1024], got %lld", (long long)page_size);
+  if (total_q >= kI32 || max_seqlen_k >= kI32 || num_pages >= kI32 || max_pages_per_seq >= kI32)
+    return fail(FA_ERR_LIMIT, "token and page counts must stay below 2^31");
+  if (B * max_pages_per_seq >= kI32) return fail(FA_ERR_LIMIT, "block_table extent exceeds 2^31");
+  if (max_pages_per_seq * page_size < max_seqlen_k)
+    return fail(FA_ERR_INVALID, "max_pages_per_seq * page_size (%lld) < max_seqlen_k (%lld)",
+                (long long)(max_pages_per_seq * page_size), (long long)max_seqlen_k);
+  Mods m;
+  if ((rc = read_mods(mods, d_qk, max_seqlen_q, max_seqlen_k, &m))) return rc;
+  if (m.flags & (FA_ALIBI | FA_SOFTCAP | FA_BLOCK_MASK))
+    return fail(FA_ERR_UNSUPPORTED, "paged caches support FA_CAUSAL and FA_WINDOW only");
+  const bool fp8 = kv_dtype == FA_FP8_E4M3;
+  const bool decode = uses_decode(max_seqlen_q, Hq, Hkv, d_qk, d_v, kv_dtype, page_size);
+  if (!decode && !prefill_dims_built(d_qk, d_v, fp8, true))
+    return fail(FA_ERR_UNSUPPORTED, "paged head dims (%lld, %lld) with kv_dtype %d not built", (long long)d_qk,
+                (long long)d_v, (int)kv_dtype);
+  if (B == 0 || total_q == 0) return FA_OK;
+  if (!q || !o || !lse || !cu_seqlens_q || !seqlen_k || !block_table)
+    return fail(FA_ERR_INVALID, "q, o, lse, cu_seqlens_q, seqlen_k and block_table must be non-NULL");
+  if (num_pages > 0 && (!k_cache || !v_cache)) return fail(FA_ERR_INVALID, "caches must be non-NULL");
+  if (max_seqlen_k > 0 && num_pages == 0) return fail(FA_ERR_INVALID, "num_pages is 0 but max_seqlen_k > 0");
+  if (fp8 && (!k_descale || !v_descale)) return fail(FA_ERR_INVALID, "FP8 caches need k_descale and v_descale");
+  const size_t es = fp8 ? 1 : 2;
+  const size_t nq = (size_t)(total_q * Hq * d_qk) * 2, no = (size_t)(total_q * Hq * d_v) * 2;
+  const size_t nk = (size_t)num_pages * Hkv * page_size * d_qk * es, nv = (size_t)num_pages * Hkv * page_size * d_v * es;
+  const size_t nl = (size_t)(Hq * total_q) * 4;
+  if (overlaps(o, no, lse, nl)) return fail(FA_ERR_INVALID, "lse must not overlap o");
+  if (overlaps(o, no, q, nq) || overlaps(o, no, k_cache, nk) || overlaps(o, no, v_cache, nv) ||
+      overlaps(lse, nl, q, nq) || overlaps(lse, nl, k_cache, nk) || overlaps(lse, nl, v_cache, nv))
+    return fail(FA_ERR_INVALID, "outputs must not overlap inputs");
+  int shift = 0;
+  while ((1ll << shift) < page_size) ++shift;
+  const hipStream_t st = (hipStream_t)stream;
+
+  if (decode) {
+    const size_t need = workspace_bytes(B, total_q, max_seqlen_q, max_seqlen_k, Hq, Hkv, d_qk, d_v, kv_dtype, page_size);
+    if (!workspace || workspace_bytes_in < need)
+      return fail(FA_ERR_WORKSPACE, "decode path needs a workspace of %zu bytes (got %zu)", need, workspace_bytes_in);
+    if (overlaps(workspace, need, o, no) || overlaps(workspace, need, lse, nl) || overlaps(workspace, need, q, nq))
+      return fail(FA_ERR_INVALID, "workspace must not overlap q, o or lse");
+    const SplitPlan p = plan_splits(B, Hkv, max_seqlen_k);
+    if (p.n_split * B * Hkv >= kI32) return fail(FA_ERR_LIMIT, "decode work count exceeds 2^31");
+    float* part_o = (float*)workspace;
+    float* part_lse = part_o + (size_t)p.n_split * total_q * Hq * d_v;
+    fa::DecodeArgs d{};
+    d.q = (const __bf16*)q;
+    d.k = k_cache;
+    d.v = v_cache;
+    d.part_o = part_o;
+    d.part_lse = part_lse;
+    d.cu_q = cu_seqlens_q;
+    d.seqlen_k = seqlen_k;
+    d.block_table = block_table;
+    d.k_descale = k_descale;
+    d.v_descale = v_descale;
+    d.q_st = Hq * d_qk; d.q_sh = d_qk;
+    d.k_st = d_qk; d.k_sh = page_size * d_qk; d.k_pg = Hkv * page_size * d_qk;
+    d.v_st = d_v; d.v_sh = page_size * d_v; d.v_pg = Hkv * page_size * d_v;
+    d.total_q = total_q;
+    d.B = (int)B; d.Hq = (int)Hq; d.Hkv = (int)Hkv; d.group = (int)(Hq / Hkv);
+    d.max_pages = (int)max_pages_per_seq;
+    d.page_shift = shift;
+    d.num_pages = (int)num_pages;
+    d.n_split = (int)p.n_split;
+    d.split_len = (int)p.split_len;
+    d.qk_scale = m.scale;
+    d.causal = (m.flags & FA_CAUSAL) ? 1 : 0;
+    d.win_left = (m.flags & FA_WINDOW) ? clamp_i32(m.wl) : -1;
+    d.win_right = (m.flags & FA_WINDOW) ? clamp_i32(m.wr) : -1;
+    bool supported = false;
+    hipError_t e = fa::decode_dispatch(d, (int)d_qk, (int)d_v, fp8, st, &supported);
+    if (!supported) return fail(FA_ERR_UNSUPPORTED, "no decode kernel for (%lld, %lld)", (long long)d_qk, (long long)d_v);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    fa::CombineArgs c{};
+    c.part_o = part_o;
+    c.part_lse = part_lse;
+    c.o = (__bf16*)o;
+    c.lse = lse;
+    c.o_st = Hq * d_v; c.o_sh = d_v;
+    c.total_q = total_q;
+    c.Hq = (int)Hq;
+    c.n_split = (int)p.n_split;
+    e = fa::combine_dispatch(c, (int)d_v, st, &supported);
+    if (!supported) return fail(FA_ERR_UNSUPPORTED, "no combine kernel for d_v=%lld", (long long)d_v);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
+    return FA_OK;
+  }
+
+  fa::PrefillArgs a{};
+  a.q = (const __bf16*)q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.o = (__bf16*)o;
+  a.lse = lse;
+  a.cu_q = cu_seqlens_q;
+  a.seqlen_k = seqlen_k;
+  a.block_table = block_table;
+  a.k_descale = k_descale;
+  a.v_descale = v_descale;
+  a.q_st = Hq * d_qk; a.q_sh = d_qk;
+  a.k_st = d_qk; a.k_sh = page_size * d_qk; a.k_pg = Hkv * page_size * d_qk;
+  a.v_st = d_v; a.v_sh = page_size * d_v; a.v_pg = Hkv * page_size * d_v;
+  a.o_st = Hq * d_v; a.o_sh = d_v;
+  a.lse_tq = total_q;
+  a.Hq = (int)Hq; a.group = (int)(Hq / Hkv);
+  a.max_pages = (int)max_pages_per_seq;
+  a.page_shift = shift;
+  a.num_pages = (int)num_pages;
+  fill_mods(a, m);
+  return launch_prefill(a, d_qk, d_v, fp8, true, 0, B, Hq, max_seqlen_q, st);
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// Device-side building blocks for the gfx950 (CDNA4) attention kernels.
+//
+// Everything here is written for 64-lane wavefronts and the gfx950 matrix
+// cores.  Lane layouts of the builtins used below (verified on the hardware
+// with an in-bounds layout probe):
+//
+//  v_mfma_f32_32x32x16_bf16  A[32 x 16], B[16 x 32], C[32 x 32]
+//    lane l holds A[l%32][(l/32)*8 + e] and B[(l/32)*8 + e][l%32], e = 0..7;
+//    C register i of lane l is C[(i/4)*8 + (l/32)*4 + i%4][l%32], i = 0..15.
+//  ds_read_b64_tr_b16 (8 bytes per lane, transposed inside each group of 16
+//    lanes): if lane j of a group points at four 16-bit values src[j][0..3],
+//    lane i of the group receives out[t] = src[4t + i/4][i%4], t = 0..3.
+//  v_permlane32_swap x, x: returns (x from lane l&31, x from lane (l&31)+32).
+//  v_cvt_scalef32_pk_bf16_fp8: two OCP E4M3 bytes -> two bf16 (exact).
+//  global_load_lds_dwordx4: lane l's 16 bytes land at LDS base + 16*l.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+#define FA_GLOBAL __attribute__((address_space(1)))
+#define FA_CONST __attribute__((address_space(4)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Running-max floor: a large finite value so that rows with no visible key
+// never evaluate (-inf) - (-inf).
+constexpr float kMaxFloor = -3.0e38f;
+
+// s_waitcnt immediate for "vector memory count <= n" (gfx9 encoding), leaving
+// the LDS/scalar and export counters unconstrained.
+__device__ __forceinline__ constexpr int vmcnt_imm(int n) {
+  return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+#define FA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(::fa::vmcnt_imm(n))
+
+// Wave-uniform load of read-only metadata through the scalar cache (s_load):
+// it is tracked by the LDS/scalar counter, so it never waits behind the
+// vector-memory data loads that are in flight.
+__device__ __forceinline__ int load_uniform_i32(const int32_t* base, int64_t idx) {
+  const FA_CONST int32_t* p = (const FA_CONST int32_t*)(base);
+  return p[idx];
+}
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Value of x held by the lane 32 positions away (l ^ 32).
+__device__ __forceinline__ float partner32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  int lane = __lane_id();
+  return __uint_as_float(lane < 32 ? r[1] : r[0]);
+}
+
+// max over the two lanes {l, l^32}
+__device__ __forceinline__ float max_pair32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_pair32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Hyperbolic tangent from the exponential: tanh(x) = 1 - 2 / (1 + e^{2x}).
+// Saturates correctly at +-1 (e^{2x} -> inf gives 1, -> 0 gives -1).
+__device__ __forceinline__ float tanh_fast(float x) {
+  float e = exp2_hw(x * (2.0f * kLog2e));
+  return 1.0f - 2.0f * rcp_hw(1.0f + e);
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const char FA_LDS* p) {
+  return *reinterpret_cast<const bf16x8 FA_LDS*>(p);
+}
+
+__device__ __forceinline__ bf16x4 lds_read_tr16(const char FA_LDS* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<s16x4 FA_LDS*>(const_cast<char FA_LDS*>(p)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// 16 bytes from global memory straight into LDS (base + 16*lane).
+__device__ __forceinline__ void global_to_lds16(const void* gsrc, char FA_LDS* lds_base) {
+  __builtin_amdgcn_global_load_lds((const FA_GLOBAL void*)(gsrc), (FA_LDS void*)(lds_base), 16, 0, 0);
+}
+
+// 16 OCP E4M3 bytes -> 16 bf16 (exact).
+__device__ __forceinline__ void fp8x16_to_bf16(i32x4 w, bf16x8& lo, bf16x8& hi) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[d], 1.0f, false);
+    bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[d], 1.0f, true);
+    if (d < 2) {
+      lo[4 * d + 0] = a[0]; lo[4 * d + 1] = a[1]; lo[4 * d + 2] = b[0]; lo[4 * d + 3] = b[1];
+    } else {
+      hi[4 * (d - 2) + 0] = a[0]; hi[4 * (d - 2) + 1] = a[1];
+      hi[4 * (d - 2) + 2] = b[0]; hi[4 * (d - 2) + 3] = b[1];
+    }
+  }
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace fa

@@ -1,0 +1,85 @@
+// Kernel argument blocks and launch entry points shared by the host library
+// and the kernel translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+constexpr int kModAlibi = 1;
+constexpr int kModSoftcap = 2;
+
+// Strides are in elements.  Contiguous K/V: element (token t, kv-head g, d) at
+// t*k_st + g*k_sh + d.  Paged K/V: element (page p, kv-head g, slot s, d) at
+// p*k_pg + g*k_sh + s*k_st + d.
+struct PrefillArgs {
+  const __bf16* q;
+  const void* k;
+  const void* v;
+  __bf16* o;
+  float* lse;
+  const int32_t* cu_q;         // packed query starts [B+1]; null: dense (b*Sq)
+  const int32_t* cu_k;         // packed key starts [B+1]; null: dense or paged
+  const int32_t* seqlen_k;     // paged: keys per sequence [B]
+  const int32_t* block_table;  // paged: [B, max_pages]
+  const float* k_descale;      // FP8 caches: per-tensor descales (device scalars)
+  const float* v_descale;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh;
+  int64_t k_pg, v_pg;
+  int64_t lse_tq;              // packed layouts: LSE is [Hq, lse_tq]
+  int Sq, Skv;                 // dense lengths
+  int Hq, group;               // group = Hq / Hkv
+  int max_pages;
+  int page_shift;
+  int num_pages;               // paged: page ids are clamped to [0, num_pages)
+  float qk_scale;
+  float alibi_slope;
+  float softcap;
+  int causal;
+  int win_left, win_right;     // < 0: unbounded
+  const uint8_t* bmask;        // [B*Hq, bm_nqb, bm_nkb] or null
+  int bm_bq, bm_bk, bm_nqb, bm_nkb;
+};
+
+// Split-KV decode over a paged cache.  One wavefront handles the key range
+// [split*split_len, (split+1)*split_len) of one (sequence, kv-head) for all
+// rows = (query i, q-head h in the kv-head's group), rows <= 32.
+struct DecodeArgs {
+  const __bf16* q;
+  const void* k;
+  const void* v;
+  float* part_o;               // [n_split, total_q, Hq, Dv] fp32 (normalised by own l)
+  float* part_lse;             // [n_split, total_q, Hq] fp32 natural-log LSE
+  const int32_t* cu_q;
+  const int32_t* seqlen_k;
+  const int32_t* block_table;
+  const float* k_descale;
+  const float* v_descale;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, k_pg, v_pg;
+  int64_t total_q;
+  int B, Hq, Hkv, group;
+  int max_pages, page_shift;
+  int num_pages;
+  int n_split, split_len;
+  float qk_scale;
+  int causal;
+  int win_left, win_right;
+};
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_lse;
+  __bf16* o;
+  float* lse;
+  int64_t o_st, o_sh;
+  int64_t total_q;
+  int Hq, n_split;
+};
+
+hipError_t prefill_dispatch(const PrefillArgs& a, int dqk, int dv, bool fp8, bool paged, int mods,
+                            int n_bh, int n_qtiles, hipStream_t stream, bool* supported);
+hipError_t decode_dispatch(const DecodeArgs& a, int dqk, int dv, bool fp8, hipStream_t stream,
+                           bool* supported);
+hipError_t combine_dispatch(const CombineArgs& a, int dv, hipStream_t stream, bool* supported);
+
+}  // namespace fa

@@ -1,0 +1,157 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) FlashAttention forward library, libfa.so.
+ *
+ * The library computes, in one fused pass per (sequence, q-head) and query
+ * tile, the attention output O = softmax(scale * Q K^T [+ score mods, masks]) V
+ * together with the per-row log-sum-exp LSE = m + ln(l) of the scaled logits
+ * (running max m, denominator l).  Sources: "Add forward LSE output to FlyDSL
+ * flash attention kernels" (FlyDSL PR 844, Summary and Changes: LSE is the
+ * per-row normalisation statistic, fully masked rows get -inf, split-K
+ * partials merge from (m, l)); "SM90 TMA + mma.sync FlashAttention ..."
+ * (RL-Kernel PR 237, description: packed varlen [total_tokens, H, D] with
+ * cu_seqlens, attention-domain LSE, zero-length sequences valid); "Support
+ * paged FP8 Flash attention with asymmetric K/V head dim on gfx950" (FlyDSL
+ * PR 1066, overview and review: paged OCP E4M3 K/V with single-value
+ * descales, Q/K width 192 with V/O width 128, int32 block_table and seqlen_k,
+ * native-width bf16 output, 64-bit cache offsets past 4 GiB, int32 overflow
+ * guards, no host work inside graph capture); "flash_attention: prologue
+ * fusion, mma tensor cores, fp8 KV cache, flex attention + block sparsity"
+ * (fkl_python PR 7, part 4: ALiBi, SoftCap, SlidingWindow score mods whose
+ * values are runtime parameters, and a (bh, nQB, nKB) uint8 tile mask whose
+ * inactive tiles are skipped).
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or keeps them.  Tensors are contiguous in the
+ *    layouts stated per function; bf16 means IEEE bfloat16, FP8 means OCP
+ *    E4M3 (e4m3fn, max 448, 0x7F/0xFF NaN).
+ *  - Sizes are int64_t host values.  Token counts, page counts and every
+ *    flattened tensor extent must stay below 2^31 elements (FA_ERR_LIMIT);
+ *    byte offsets inside the kernels are 64-bit.
+ *  - `stream` is a hipStream_t (NULL: the default stream).  Work is only
+ *    enqueued on it; nothing synchronises with the host and no host-device
+ *    copy happens, so calls can be captured in a HIP graph.
+ *  - Return 0 (FA_OK) on success.  Every argument check runs on the host
+ *    before any HIP call; on failure nothing is enqueued and fa_last_error()
+ *    returns a message (thread-local).  Device-resident metadata
+ *    (cu_seqlens, seqlen_k, block_table, block_mask) cannot be checked
+ *    without a synchronisation; it must be consistent with the host sizes.
+ *  - Rows that see no key (causal with fewer keys than queries, windows,
+ *    inactive block-mask tiles, empty key sequences) produce O = 0 and
+ *    LSE = -inf.  Zero-length query sequences write nothing.
+ *  - Query row i of a sequence with Sq queries and Skv keys is aligned to key
+ *    position i' = i + Skv - Sq (bottom-right); causal means key j <= i'.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_OK 0
+#define FA_ERR_INVALID (-1)     /* null / aliasing pointers, inconsistent sizes */
+#define FA_ERR_UNSUPPORTED (-2) /* head-dim pair, dtype, page size or mod combination not built */
+#define FA_ERR_LIMIT (-3)       /* a count or flattened extent >= 2^31 */
+#define FA_ERR_WORKSPACE (-4)   /* workspace missing or too small */
+#define FA_ERR_HIP (-5)         /* the HIP runtime rejected a launch */
+
+typedef enum fa_dtype { FA_BF16 = 0, FA_FP8_E4M3 = 1 } fa_dtype;
+
+/* fa_mods.flags */
+#define FA_CAUSAL 1u     /* key j visible to row i only if j <= i' */
+#define FA_WINDOW 2u     /* i' - window_left <= j <= i' + window_right (negative: unbounded side) */
+#define FA_ALIBI 4u      /* logit -= alibi_slope * |i' - j| (same slope for every head) */
+#define FA_SOFTCAP 8u    /* logit = softcap * tanh(logit / softcap), applied before ALiBi */
+#define FA_BLOCK_MASK 16u /* tile mask: key j visible to row i only if
+                             block_mask[(b*Hq + h)][i / mask_block_q][j / mask_block_k] != 0 */
+
+/* Score modifications and masks.  A NULL fa_mods* means: no flags, default scale. */
+typedef struct fa_mods {
+  uint32_t flags;
+  float softmax_scale;      /* <= 0: 1/sqrt(d_qk) */
+  float alibi_slope;        /* FA_ALIBI */
+  float softcap;            /* FA_SOFTCAP, > 0 */
+  int64_t window_left;      /* FA_WINDOW */
+  int64_t window_right;
+  const uint8_t* block_mask; /* FA_BLOCK_MASK: device uint8 [B*Hq, mask_nqb, mask_nkb] */
+  int64_t mask_block_q;     /* must be a multiple of 128 */
+  int64_t mask_block_k;     /* must be a multiple of 64 */
+  int64_t mask_nqb;         /* >= ceil(max_seqlen_q / mask_block_q) */
+  int64_t mask_nkb;         /* >= ceil(max_seqlen_k / mask_block_k) */
+} fa_mods;
+
+/*
+ * Dense batch.  Q [B, Sq, Hq, d_qk], K [B, Skv, Hkv, d_qk], V [B, Skv, Hkv, d_v]
+ * and O [B, Sq, Hq, d_v] are bf16; LSE [B, Hq, Sq] is fp32.  Hq % Hkv == 0;
+ * q-head h reads kv-head h / (Hq / Hkv).  Built head dims: (64, 64), (128, 128).
+ * All mods are supported.  O and LSE must not overlap each other or the inputs.
+ */
+int fa_fwd_dense(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int64_t B, int64_t Sq, int64_t Skv, int64_t Hq, int64_t Hkv,
+                 int64_t d_qk, int64_t d_v, const fa_mods* mods, void* stream);
+
+/*
+ * Packed variable-length batch.  Sequence b owns query rows
+ * [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key rows [cu_seqlens_k[b],
+ * cu_seqlens_k[b+1]) (device int32 [B+1], non-decreasing, starting at 0).
+ * Q [total_q, Hq, d_qk], K [total_k, Hkv, d_qk], V [total_k, Hkv, d_v],
+ * O [total_q, Hq, d_v] bf16; LSE [Hq, total_q] fp32.  max_seqlen_q/k bound
+ * every sequence's lengths (host scalars, so no device read-back is needed).
+ * Built head dims and mods as for fa_fwd_dense.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t B,
+                  int64_t total_q, int64_t total_k, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                  int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v,
+                  const fa_mods* mods, void* stream);
+
+/*
+ * Paged KV cache.  Q [total_q, Hq, d_qk] bf16 packed by cu_seqlens_q (device
+ * int32 [B+1]); O [total_q, Hq, d_v] bf16; LSE [Hq, total_q] fp32.
+ * Caches are head-major pages: K [num_pages, Hkv, page_size, d_qk] and
+ * V [num_pages, Hkv, page_size, d_v], elements FP8 E4M3 (kv_dtype =
+ * FA_FP8_E4M3, real value = code * descale with k_descale / v_descale device
+ * fp32 scalars) or bf16 (FA_BF16, descales ignored, may be NULL).
+ * Key j of sequence b is slot j % page_size of page
+ * block_table[b * max_pages_per_seq + j / page_size] (device int32
+ * [B, max_pages_per_seq]); seqlen_k (device int32 [B]) is its key count.
+ * Only the first ceil(seqlen_k[b] / page_size) entries of a block-table row
+ * are read, and bytes past seqlen_k in a page never influence the result.
+ * page_size: a power of two in [16, 1024].
+ * Built: FP8 (d_qk, d_v) in {(192, 128), (128, 128)}; bf16 (64, 64), (128, 128).
+ * Mods: FA_CAUSAL and FA_WINDOW only.
+ * When max_seqlen_q * (Hq / Hkv) <= 32 (decode), kv_dtype is FP8, d_v is 128
+ * and page_size >= 32, the
+ * keys are split and partial results merged; that path needs a device
+ * workspace of fa_fwd_paged_workspace_size(...) bytes (else FA_ERR_WORKSPACE).
+ * The workspace is scratch, overwritten by the call.
+ */
+int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                 const int32_t* cu_seqlens_q, const int32_t* seqlen_k, const int32_t* block_table,
+                 int64_t B, int64_t total_q, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                 int64_t num_pages, int64_t page_size, int64_t max_pages_per_seq,
+                 int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v, fa_dtype kv_dtype,
+                 const float* k_descale, const float* v_descale,
+                 void* workspace, size_t workspace_bytes,
+                 const fa_mods* mods, void* stream);
+
+/* Workspace bytes fa_fwd_paged needs for these sizes (0 when it needs none). */
+size_t fa_fwd_paged_workspace_size(int64_t B, int64_t total_q, int64_t max_seqlen_q,
+                                   int64_t max_seqlen_k, int64_t Hq, int64_t Hkv, int64_t d_qk,
+                                   int64_t d_v, int64_t page_size, fa_dtype kv_dtype);
+
+/* Message describing the last non-zero return on this thread ("" if none). */
+const char* fa_last_error(void);
+
+/* ABI version of this header (increments on any signature change). */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -225,11 +225,14 @@ def paged_rows(q, k_cache, v_cache, cu_q, seqlen_k, block_table, picks, mods=Non
     groups = {}
     for n, (b, h, i) in enumerate(picks):
         groups.setdefault((b, h), []).append((n, i))
+    gathered = {}
     for (b, h), lst in groups.items():
         g = h // grp
         L = int(seqlen_k[b])
-        kh = gather_paged(k_cache, block_table[b], L, g, k_descale)
-        vh = gather_paged(v_cache, block_table[b], L, g, v_descale)
+        if (b, g) not in gathered:
+            gathered = {(b, g): (gather_paged(k_cache, block_table[b], L, g, k_descale),
+                                 gather_paged(v_cache, block_table[b], L, g, v_descale))}
+        kh, vh = gathered[(b, g)]
         q0, q1 = cu_q[b], cu_q[b + 1]
         rows = np.array([i for _, i in lst])
         bm = None if m["block_mask"] is None else np.asarray(m["block_mask"])[b * Hq + h]

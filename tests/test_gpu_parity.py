@@ -1,0 +1,370 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+Small and ragged shapes are compared element by element; the full-size
+workloads are compared on sampled rows that the oracle computes one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.helpers import TOL_LSE, TOL_O_BF16, TOL_O_FP8, compare, f64
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import attention_fa_fwd_03_amd as fa
+
+DEV = "cuda"
+
+
+def _nan_like(shape, dtype):
+    return torch.full(shape, float("nan"), dtype=dtype, device=DEV)
+
+
+def _dense_run(d, mods_kw, Dv):
+    q, k, v = (d[x].to(DEV) for x in ("q", "k", "v"))
+    B, Sq, Hq, _ = q.shape
+    o = _nan_like((B, Sq, Hq, Dv), torch.bfloat16)
+    lse = _nan_like((B, Hq, Sq), torch.float32)
+    fa.fa_fwd_dense(q, k, v, o, lse, fa.Mods(**mods_kw))
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _oracle_mods(mods_kw, block_mask=None):
+    m = dict(mods_kw)
+    if "block_mask" in m:
+        m["block_mask"] = None if m["block_mask"] is None else m["block_mask"].cpu().numpy()
+    if block_mask is not None:
+        m["block_mask"] = block_mask
+    if "mask_block" not in m:
+        m["mask_block"] = (128, 128)
+    return m
+
+
+# ----------------------------------------------------------------------------- dense
+def test_dense_small_config():
+    """B=1, H=2, Sq=Skv=128, D=64, scale 1/sqrt(64), non-causal."""
+    d = synth.make_dense(1, 128, 128, 2, 2, 64, 64, seed=synth.seed_for(1))
+    o, lse = _dense_run(d, dict(scale=1 / 8), 64)
+    o_ref, l_ref = oracle.attention_dense(f64(d["q"]), f64(d["k"]), f64(d["v"]), dict(scale=1 / 8))
+    compare(o, lse, o_ref, l_ref, TOL_O_BF16, what="dense cfg1")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Sq,Skv", [(128, 128), (200, 333), (333, 200), (1, 77), (64, 1), (257, 257), (5, 0)])
+def test_dense_shapes(D, causal, Sq, Skv):
+    d = synth.make_dense(2, Sq, Skv, 4, 2, D, D, seed=11 + Sq + 7 * Skv + D)
+    o, lse = _dense_run(d, dict(causal=causal), D)
+    o_ref, l_ref = oracle.attention_dense(f64(d["q"]), f64(d["k"]), f64(d["v"]), dict(causal=causal))
+    compare(o, lse, o_ref, l_ref, TOL_O_BF16, what=f"dense D{D} c{causal} {Sq}x{Skv}")
+
+
+# ----------------------------------------------------------------------------- varlen
+def _varlen_run(d, mods_kw, Dv):
+    q, k, v = (d[x].to(DEV) for x in ("q", "k", "v"))
+    cu_q, cu_k = d["cu_q"].to(DEV), d["cu_k"].to(DEV)
+    Tq, Hq, _ = q.shape
+    o = _nan_like((Tq, Hq, Dv), torch.bfloat16)
+    lse = _nan_like((Hq, Tq), torch.float32)
+    fa.fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, max(d["lengths_q"]), max(d["lengths_k"]), fa.Mods(**mods_kw))
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 4, 4), (128, 8, 2), (64, 3, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_ragged(D, Hq, Hkv, causal):
+    lq = [5, 0, 130, 64, 1, 300, 0, 77]
+    lk = [5, 0, 130, 64, 1, 300, 0, 77]
+    d = synth.make_varlen(lq, lk, Hq, Hkv, D, D, seed=21 + D + Hq)
+    o, lse = _varlen_run(d, dict(causal=causal), D)
+    o_ref, l_ref = oracle.attention_varlen(f64(d["q"]), f64(d["k"]), f64(d["v"]), d["cu_q"], d["cu_k"],
+                                           dict(causal=causal))
+    compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_BF16, what="varlen ragged")
+
+
+def test_varlen_cross_lengths():
+    """Query and key lengths differ per sequence (bottom-right causal alignment)."""
+    lq = [3, 40, 200, 1, 0, 65]
+    lk = [10, 40, 150, 300, 7, 0]
+    d = synth.make_varlen(lq, lk, 4, 2, 128, 128, seed=31)
+    for causal in (False, True):
+        o, lse = _varlen_run(d, dict(causal=causal), 128)
+        o_ref, l_ref = oracle.attention_varlen(f64(d["q"]), f64(d["k"]), f64(d["v"]), d["cu_q"], d["cu_k"],
+                                               dict(causal=causal))
+        compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_BF16, what=f"cross c{causal}")
+
+
+def test_varlen_packing_is_bitwise_invariant():
+    """A sequence gives bit-identical O/LSE alone and packed at any offset."""
+    lens = [77, 300, 129]
+    d = synth.make_varlen(lens, lens, 4, 4, 128, 128, seed=41)
+    o_all, l_all = _varlen_run(d, dict(causal=True), 128)
+    cu = d["cu_q"].tolist()
+    for b in range(3):
+        sl = slice(cu[b], cu[b + 1])
+        one = dict(q=d["q"][sl], k=d["k"][sl], v=d["v"][sl], cu_q=torch.tensor([0, lens[b]], dtype=torch.int32),
+                   cu_k=torch.tensor([0, lens[b]], dtype=torch.int32), lengths_q=[lens[b]], lengths_k=[lens[b]])
+        o1, l1 = _varlen_run(one, dict(causal=True), 128)
+        assert torch.equal(o1, o_all[sl]) and torch.equal(l1, l_all[:, sl])
+
+
+def test_varlen_full_size_sampled():
+    """H=16, D=128, 8 sequences with lengths uniform in [0,4096] (one zero,
+    several not multiples of 64), causal; sampled rows against the oracle."""
+    lens = synth.varlen_lengths(synth.seed_for(2))
+    d = synth.make_varlen(lens, lens, 16, 16, 128, 128, seed=synth.seed_for(2))
+    o, lse = _varlen_run(d, dict(causal=True), 128)
+    rng = np.random.default_rng(5)
+    picks = []
+    for b, L in enumerate(lens):
+        if L == 0:
+            continue
+        rows = sorted({0, 1, 63, 64, L - 1, L // 2, *rng.integers(0, L, 4).tolist()} & set(range(L)))
+        for h in (0, 7, 15):
+            picks += [(b, h, i) for i in rows]
+    o_ref, l_ref = oracle.varlen_rows(f64(d["q"]), f64(d["k"]), f64(d["v"]), d["cu_q"], d["cu_k"], picks,
+                                      dict(causal=True))
+    cu = d["cu_q"].tolist()
+    og = torch.stack([o[cu[b] + i, h] for b, h, i in picks])
+    lg = torch.stack([lse[h, cu[b] + i] for b, h, i in picks])
+    compare(og, lg, o_ref, l_ref, TOL_O_BF16, what="varlen full")
+    # every row of the packed output was written and is finite
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+# ----------------------------------------------------------------------------- closed forms on the GPU
+def test_q_zero_gives_log_visible_count():
+    lens = [100, 257, 64]
+    d = synth.make_varlen(lens, lens, 2, 2, 128, 128, seed=51)
+    d["q"] = torch.zeros_like(d["q"])
+    for mods in (dict(causal=True), dict(window=(37, 0)), dict()):
+        o, lse = _varlen_run(d, mods, 128)
+        cu = d["cu_q"].tolist()
+        for b, L in enumerate(lens):
+            i = np.arange(L)
+            if mods.get("causal"):
+                n = i + 1
+            elif "window" in mods:
+                n = np.minimum(i, 37) + 1
+            else:
+                n = np.full(L, L)
+            got = lse[:, cu[b]:cu[b + 1]].double().cpu().numpy()
+            assert np.max(np.abs(got - np.log(n)[None, :])) < TOL_LSE
+
+
+def test_diagonal_window_is_exact():
+    """window (0,0): each row sees only its own key, so O equals that V row
+    exactly and LSE equals that single scaled logit."""
+    lens = [70, 129]
+    d = synth.make_varlen(lens, lens, 4, 2, 128, 128, seed=61)
+    d["v"] = torch.randint(-8, 9, d["v"].shape).to(torch.bfloat16)
+    o, lse = _varlen_run(d, dict(window=(0, 0)), 128)
+    qf, kf = d["q"].double(), d["k"].double()
+    for h in range(4):
+        g = h // 2
+        assert torch.equal(o[:, h].cpu(), d["v"][:, g])
+        s = (qf[:, h] * kf[:, g]).sum(-1) / math.sqrt(128)
+        assert torch.max(torch.abs(lse[h].double().cpu() - s)) < TOL_LSE
+
+
+def test_peaked_queries_pair_k_with_v():
+    """Q_i = alpha * K_sigma(i): each row's softmax concentrates on one key, so any
+    K/V row-pairing or permutation mistake shows as a large O error."""
+    L = 256
+    d = synth.make_varlen([L], [L], 2, 2, 128, 128, seed=71)
+    sigma = torch.randperm(L, generator=torch.Generator().manual_seed(7))
+    d["q"] = synth.peaked_queries(d["k"][sigma], 1.5)
+    o, lse = _varlen_run(d, dict(), 128)
+    o_ref, l_ref = oracle.attention_varlen(f64(d["q"]), f64(d["k"]), f64(d["v"]), d["cu_q"], d["cu_k"], dict())
+    compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_BF16, what="peaked")
+    # the peak really dominates: O is close to the selected V row
+    assert torch.max(torch.abs(o[:, 0].float().cpu() - d["v"][sigma, 0].float())) < 0.5
+
+
+# ----------------------------------------------------------------------------- paged
+def _paged_run(d, mods_kw, Dv, workspace=True):
+    q = d["q"].to(DEV)
+    kc, vc = d["k_cache"].to(DEV), d["v_cache"].to(DEV)
+    Tq, Hq, Dqk = q.shape
+    P, Hkv, ps, _ = kc.shape
+    B = len(d["lengths_k"])
+    msq, msk = max(d["lengths_q"]), max(d["lengths_k"])
+    o = _nan_like((Tq, Hq, Dv), torch.bfloat16)
+    lse = _nan_like((Hq, Tq), torch.float32)
+    fp8 = kc.dtype == torch.uint8
+    ws = None
+    if workspace:
+        n = fa.fa_fwd_paged_workspace_size(B, Tq, msq, msk, Hq, Hkv, Dqk, Dv, ps,
+                                           fa.FA_FP8_E4M3 if fp8 else fa.FA_BF16)
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+    fa.fa_fwd_paged(q, kc, vc, o, lse, d["cu_q"].to(DEV), d["seqlen_k"].to(DEV), d["block_table"].to(DEV),
+                    msq, msk, d["k_descale"].to(DEV), d["v_descale"].to(DEV), ws, fa.Mods(**mods_kw))
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _paged_ref(d, mods_kw):
+    return oracle.attention_paged(f64(d["q"]), f64(d["k_cache"]), f64(d["v_cache"]), d["cu_q"], d["seqlen_k"],
+                                  d["block_table"], dict(mods_kw), float(d["k_descale"]), float(d["v_descale"]))
+
+
+@pytest.mark.parametrize("ps", [64, 16, 128])
+def test_paged_fp8_prefill_small(ps):
+    lk = [70, 3, 128, 129, 600]
+    lq = [70, 3, 128, 129, 600]
+    d = synth.make_paged(lq, lk, 4, 4, 192, 128, page_size=ps, seed=81 + ps, extra_pages=3)
+    o, lse = _paged_run(d, dict(causal=True), 128)
+    o_ref, l_ref = _paged_ref(d, dict(causal=True))
+    compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_FP8, what=f"paged ps{ps}")
+
+
+def test_paged_fp8_chunked_prefill_and_gqa():
+    """Fewer queries than keys (bottom-right causal), GQA 2:1, D 128/128."""
+    lk = [300, 64, 1000]
+    lq = [40, 64, 100]
+    d = synth.make_paged(lq, lk, 4, 2, 128, 128, page_size=64, seed=91)
+    o, lse = _paged_run(d, dict(causal=True), 128)
+    o_ref, l_ref = _paged_ref(d, dict(causal=True))
+    compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_FP8, what="chunked")
+
+
+def _reshuffle(d, seed):
+    """Same logical cache, different physical page placement."""
+    P = d["k_cache"].shape[0]
+    perm = torch.randperm(P, generator=torch.Generator().manual_seed(seed))
+    e = dict(d)
+    e["k_cache"] = torch.empty_like(d["k_cache"])
+    e["v_cache"] = torch.empty_like(d["v_cache"])
+    e["k_cache"][perm] = d["k_cache"]
+    e["v_cache"][perm] = d["v_cache"]
+    e["block_table"] = perm.to(torch.int32)[d["block_table"].long()]
+    return e
+
+
+@pytest.mark.parametrize("lq", [[200, 64, 1], [1, 1, 1]])
+def test_paged_placement_is_bitwise_invariant(lq):
+    lk = [300, 64, 700]
+    d = synth.make_paged(lq, lk, 8, 1 if lq[0] == 1 else 8, 192, 128, page_size=64, seed=95, extra_pages=11)
+    o1, l1 = _paged_run(d, dict(causal=True), 128)
+    e = _reshuffle(d, 3)
+    o2, l2 = _paged_run(e, dict(causal=True), 128)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_paged_full_prefill_sampled():
+    """Q [8192,16,192] bf16, FP8 K (192) / V (128) in pages of 64 with a
+    shuffled block table, 4 sequences of 2048, causal; sampled rows."""
+    L = [2048] * 4
+    d = synth.make_paged(L, L, 16, 16, 192, 128, page_size=64, seed=synth.seed_for(3))
+    o, lse = _paged_run(d, dict(causal=True), 128)
+    rng = np.random.default_rng(3)
+    picks = [(b, h, int(i)) for b in range(4) for h in (0, 9, 15) for i in {0, 1, 2047, 1024, *rng.integers(0, 2048, 3).tolist()}]
+    o_ref, l_ref = oracle.paged_rows(f64(d["q"]), f64(d["k_cache"]), f64(d["v_cache"]), d["cu_q"], d["seqlen_k"],
+                                     d["block_table"], picks, dict(causal=True),
+                                     float(d["k_descale"]), float(d["v_descale"]))
+    cu = d["cu_q"].tolist()
+    og = torch.stack([o[cu[b] + i, h] for b, h, i in picks])
+    lg = torch.stack([lse[h, cu[b] + i] for b, h, i in picks])
+    compare(og, lg, o_ref, l_ref, TOL_O_FP8, what="paged full")
+
+
+# ----------------------------------------------------------------------------- decode
+@pytest.mark.parametrize("Hq,Hkv,Dqk,sq", [(16, 2, 192, 1), (8, 8, 128, 1), (16, 2, 192, 4), (64, 8, 192, 1)])
+def test_decode_small(Hq, Hkv, Dqk, sq):
+    lk = [1, 31, 32, 33, 64, 1000, 3000, 257]
+    lq = [min(sq, l) for l in lk]
+    d = synth.make_paged(lq, lk, Hq, Hkv, Dqk, 128, page_size=64, seed=101 + Hq + sq, extra_pages=5)
+    o, lse = _paged_run(d, dict(causal=True), 128)
+    o_ref, l_ref = _paged_ref(d, dict(causal=True))
+    compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_FP8, what="decode")
+
+
+def test_decode_requires_workspace():
+    d = synth.make_paged([1, 1], [100, 50], 16, 2, 192, 128, page_size=64, seed=111)
+    with pytest.raises(fa.FaError) as e:
+        _paged_run(d, dict(), 128, workspace=False)
+    assert e.value.code == -4
+
+
+def test_decode_full_size_sampled():
+    """64 sequences, contexts uniform in [1024, 32768], GQA 64/8, D 192/128,
+    pages of 64 with a shuffled block table; 6 sequences checked in full."""
+    lk = synth.make_decode_lengths(synth.seed_for(4))
+    lq = [1] * 64
+    d = synth.make_paged(lq, lk, 64, 8, 192, 128, page_size=64, seed=synth.seed_for(4), device=DEV)
+    o, lse = _paged_run(d, dict(causal=True), 128)
+    bsel = [0, 5, 17, 33, 50, 63]
+    picks = [(b, h, 0) for b in bsel for h in range(64)]
+    o_ref, l_ref = oracle.paged_rows(f64(d["q"]), f64(d["k_cache"]), f64(d["v_cache"]), d["cu_q"].cpu(),
+                                     d["seqlen_k"].cpu(), d["block_table"].cpu(), picks, dict(causal=True),
+                                     float(d["k_descale"]), float(d["v_descale"]))
+    og = torch.stack([o[b, h] for b, h, _ in picks])
+    lg = torch.stack([lse[h, b] for b, h, _ in picks])
+    compare(og, lg, o_ref, l_ref, TOL_O_FP8, what="decode full")
+
+
+# ----------------------------------------------------------------------------- flex
+FLEX_CASES = {
+    "alibi": dict(alibi_slope=0.0625),
+    "softcap": dict(softcap=20.0),
+    "window": dict(window=(256, 0)),
+    "window_sym": dict(window=(16, 8)),
+    "alibi_softcap_causal": dict(alibi_slope=0.25, softcap=5.0, causal=True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(FLEX_CASES))
+def test_flex_mods_small(case):
+    d = synth.make_dense(2, 300, 300, 2, 2, 128, 128, seed=121)
+    mods = FLEX_CASES[case]
+    o, lse = _dense_run(d, mods, 128)
+    o_ref, l_ref = oracle.attention_dense(f64(d["q"]), f64(d["k"]), f64(d["v"]), dict(mods))
+    compare(o, lse, o_ref, l_ref, TOL_O_BF16, what=case)
+
+
+@pytest.mark.parametrize("kind", ["bernoulli", "block_causal", "bernoulli_causal"])
+def test_flex_block_mask_small(kind):
+    B, H, S = 2, 2, 640
+    nb = math.ceil(S / 128)
+    if kind.startswith("bernoulli"):
+        bm = synth.bernoulli_block_mask(B * H, nb, nb, 0.5, seed=131)
+        bm[0, 1, :] = 0          # a fully masked query block
+    else:
+        bm = synth.block_causal_mask(B * H, nb, nb)
+    d = synth.make_dense(B, S, S, H, H, 128, 128, seed=132)
+    mods = dict(block_mask=bm.to(DEV), mask_block=(128, 128), causal=kind.endswith("causal") and kind != "block_causal")
+    o, lse = _dense_run(d, mods, 128)
+    o_ref, l_ref = oracle.attention_dense(f64(d["q"]), f64(d["k"]), f64(d["v"]), _oracle_mods(mods))
+    compare(o, lse, o_ref, l_ref, TOL_O_BF16, what=kind)
+
+
+@pytest.mark.parametrize("case", ["alibi", "softcap", "window", "bernoulli", "block_causal"])
+def test_flex_full_size_sampled(case):
+    """B=2, H=16, S=8192, D=128 (non-causal unless stated); sampled rows."""
+    B, H, S = 2, 16, 8192
+    d = synth.make_dense(B, S, S, H, H, 128, 128, seed=synth.seed_for(5))
+    if case == "bernoulli":
+        mods = dict(block_mask=synth.bernoulli_block_mask(B * H, 64, 64, 0.5, seed=synth.seed_for(5, 3)).to(DEV))
+    elif case == "block_causal":
+        mods = dict(block_mask=synth.block_causal_mask(B * H, 64, 64).to(DEV))
+    else:
+        mods = dict(FLEX_CASES[case])
+    o, lse = _dense_run(d, mods, 128)
+    rng = np.random.default_rng(9)
+    rows = sorted({0, 1, 127, 128, 4095, 8191, *rng.integers(0, S, 4).tolist()})
+    picks = [(b, h, i) for b in range(B) for h in (0, 11) for i in rows]
+    qv = f64(d["q"]).reshape(B * S, H, 128)
+    kv = f64(d["k"]).reshape(B * S, H, 128)
+    vv = f64(d["v"]).reshape(B * S, H, 128)
+    cu = np.array([0, S, 2 * S])
+    o_ref, l_ref = oracle.varlen_rows(qv, kv, vv, cu, cu, picks, _oracle_mods(mods))
+    og = torch.stack([o[b, i, h] for b, h, i in picks])
+    lg = torch.stack([lse[b, h, i] for b, h, i in picks])
+    compare(og, lg, o_ref, l_ref, TOL_O_BF16, what=f"flex full {case}")
