@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+Default workload: packed varlen causal prefill, H=16, D=128, bf16, 8
+sequences with lengths uniform in [0, 4096] (one zero-length, several not
+multiples of 64).  One step = one fa_fwd_varlen call over that batch (the
+whole hot path: work enumeration, K/V addressing and staging, Q.K^T, masks,
+online softmax, P.V, epilogue with O and LSE).  Inputs are resident in HBM
+before timing starts.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+                  [--flex alibi|softcap|window|bernoulli|block_causal] [--no-cpu-baseline]
+
+--config selects another workload for investigation (1 dense D64, 3 paged
+FP8 prefill, 4 paged FP8 decode, 5 flex); the default line is config 2.
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s + fraction of MFMA peak; paged-decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+KERNEL_SOURCES = {
+    "prefill": ["attention_fa_fwd_03_amd/csrc/fa_prefill.hip", "attention_fa_fwd_03_amd/csrc/fa_device.h",
+                "attention_fa_fwd_03_amd/csrc/fa_kernels.h"],
+    "decode": ["attention_fa_fwd_03_amd/csrc/fa_decode.hip", "attention_fa_fwd_03_amd/csrc/fa_device.h",
+               "attention_fa_fwd_03_amd/csrc/fa_kernels.h"],
+}
+
+
+def kernel_sha(kind: str) -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_key: str, kind: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
+    the kernel source changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tab = json.load(f)
+    e = tab.get(workload_key)
+    if not e or e.get("kernel_sha") != kernel_sha(kind):
+        return None
+    return e["hbm_bytes_per_launch"]
+
+
+def build_workload(cfg: int, flex: str, torch, synth, fa):
+    """Returns (name, run_fn, work dict, oracle sample fn)."""
+    dev = "cuda"
+    if cfg == 1:
+        d = synth.make_dense(1, 128, 128, 2, 2, 64, 64, seed=synth.seed_for(1), device=dev)
+        o = torch.empty(1, 128, 2, 64, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(1, 2, 128, dtype=torch.float32, device=dev)
+        mods = fa.Mods(scale=1 / 8)
+        flops = 1 * 2 * 128 * 128 * (2 * 64 + 2 * 64)
+        run = lambda: fa.fa_fwd_dense(d["q"], d["k"], d["v"], o, lse, mods)
+        name = "dense non-causal B1 H2 S128 D64 bf16"
+        return name, run, dict(flops=flops, kind="prefill", bound="mfma"), {"B": 1, "H": 2, "S": 128, "D": 64}, None
+    if cfg == 2:
+        lens = synth.varlen_lengths(synth.seed_for(2))
+        d = synth.make_varlen(lens, lens, 16, 16, 128, 128, seed=synth.seed_for(2), device=dev)
+        T = sum(lens)
+        o = torch.empty(T, 16, 128, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(16, T, dtype=torch.float32, device=dev)
+        mods = fa.Mods(causal=True)
+        flops = sum(16 * L * (L + 1) // 2 * (2 * 128 + 2 * 128) for L in lens)
+        run = lambda: fa.fa_fwd_varlen(d["q"], d["k"], d["v"], o, lse, d["cu_q"], d["cu_k"], max(lens), max(lens), mods)
+        name = "varlen causal prefill H16 D128 bf16, 8 seqs U[0,4096]"
+
+        def sample():
+            import numpy as np
+            import oracle
+            qh, kh, vh = (d[x][:, :4].float().cpu().double().numpy() for x in ("q", "k", "v"))
+            cu = d["cu_q"].cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.attention_varlen(qh, kh, vh, cu, cu, dict(causal=True), workers=_cores())
+            dt = time.perf_counter() - t0
+            sflops = sum(4 * L * (L + 1) // 2 * 512 for L in lens)
+            return dict(seconds=dt, flops=sflops, sample="heads 0-3 of all 8 sequences (1/4 of the batch)")
+        return name, run, dict(flops=flops, kind="prefill", bound="mfma"), \
+            {"seqlens": lens, "total_tokens": T, "H": 16, "D": 128, "causal": True}, sample
+    if cfg == 3:
+        L = [2048] * 4
+        d = synth.make_paged(L, L, 16, 16, 192, 128, page_size=64, seed=synth.seed_for(3), device=dev)
+        o = torch.empty(8192, 16, 128, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(16, 8192, dtype=torch.float32, device=dev)
+        mods = fa.Mods(causal=True)
+        flops = 64 * 2048 * 2049 // 2 * (2 * 192 + 2 * 128)
+        run = lambda: fa.fa_fwd_paged(d["q"], d["k_cache"], d["v_cache"], o, lse, d["cu_q"], d["seqlen_k"],
+                                      d["block_table"], 2048, 2048, d["k_descale"], d["v_descale"], None, mods)
+        name = "paged FP8 causal prefill 4x2048 H16 Dqk192 Dv128 page64"
+        return name, run, dict(flops=flops, kind="prefill", bound="mfma"), \
+            {"B": 4, "S": 2048, "H": 16, "d_qk": 192, "d_v": 128, "page_size": 64}, None
+    if cfg == 4:
+        lk = synth.make_decode_lengths(synth.seed_for(4))
+        lq = [1] * 64
+        d = synth.make_paged(lq, lk, 64, 8, 192, 128, page_size=64, seed=synth.seed_for(4), device=dev)
+        o = torch.empty(64, 64, 128, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(64, 64, dtype=torch.float32, device=dev)
+        n = fa.fa_fwd_paged_workspace_size(64, 64, 1, max(lk), 64, 8, 192, 128, 64)
+        ws = torch.empty(n, dtype=torch.uint8, device=dev)
+        mods = fa.Mods(causal=True)
+        kv_bytes = sum(lk) * 8 * (192 + 128)
+        io_bytes = 64 * 64 * 192 * 2 + 64 * 64 * 128 * 2 + 64 * 64 * 4 + sum(math.ceil(x / 64) for x in lk) * 4
+        flops = sum(lk) * 64 * (2 * 192 + 2 * 128)
+        run = lambda: fa.fa_fwd_paged(d["q"], d["k_cache"], d["v_cache"], o, lse, d["cu_q"], d["seqlen_k"],
+                                      d["block_table"], 1, max(lk), d["k_descale"], d["v_descale"], ws, mods)
+        name = "paged FP8 decode 64 seqs ctx U[1024,32768] GQA 64/8 Dqk192 Dv128 page64"
+        return name, run, dict(flops=flops, bytes=kv_bytes + io_bytes, kind="decode", bound="hbm"), \
+            {"B": 64, "ctx_total": sum(lk), "Hq": 64, "Hkv": 8, "page_size": 64}, None
+    if cfg == 5:
+        B, H, S, D = 2, 16, 8192, 128
+        d = synth.make_dense(B, S, S, H, H, D, D, seed=synth.seed_for(5), device=dev)
+        o = torch.empty(B, S, H, D, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(B, H, S, dtype=torch.float32, device=dev)
+        bound = "mfma"
+        if flex == "alibi":
+            mods, pairs = fa.Mods(alibi_slope=0.0625), S * S
+        elif flex == "softcap":
+            mods, pairs = fa.Mods(softcap=20.0), S * S
+        elif flex == "window":
+            mods, pairs = fa.Mods(window=(256, 0)), sum(min(i, 256) + 1 for i in range(S))
+            bound = "hbm"
+        elif flex == "bernoulli":
+            bm = synth.bernoulli_block_mask(B * H, 64, 64, 0.5, seed=synth.seed_for(5, 3)).to(dev)
+            mods, pairs = fa.Mods(block_mask=bm), None
+            act = int(bm.sum())
+        else:
+            bm = synth.block_causal_mask(B * H, 64, 64).to(dev)
+            mods, pairs = fa.Mods(block_mask=bm), None
+            act = int(bm.sum())
+        if pairs is None:
+            flops = act * 128 * 128 * (2 * D + 2 * D)
+        else:
+            flops = B * H * pairs * (2 * D + 2 * D)
+        byts = 4 * B * S * H * D * 2 + B * H * S * 4
+        run = lambda: fa.fa_fwd_dense(d["q"], d["k"], d["v"], o, lse, mods)
+        name = f"flex {flex} B2 H16 S8192 D128 bf16"
+        return name, run, dict(flops=flops, bytes=byts, kind="prefill", bound=bound), \
+            {"B": B, "H": H, "S": S, "D": D, "mod": flex}, None
+    raise SystemExit(f"unknown config {cfg}")
+
+
+def _cores() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--flex", default="alibi")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 256 MiB device copy first (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(the path shards by sequence and head; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import attention_fa_fwd_03_amd as fa
+
+    torch.cuda.init()
+    name, run, work, cfg_extra, sample = build_workload(args.config, args.flex, torch, synth, fa)
+    if args.copy_calibration:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall * 1e3 / args.steps
+    per_launch_s = gpu_ms * 1e-3 / args.steps
+
+    tflops = work["flops"] * args.steps / wall / 1e12
+    if work["bound"] == "hbm":
+        value = work["bytes"] * args.steps / wall / 1e9
+        unit = "GB/s"
+        achieved = work["bytes"] / per_launch_s / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 2), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBS, 4))
+    else:
+        value = tflops
+        unit = "TFLOP/s"
+        achieved = work["flops"] / per_launch_s / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 4))
+    key = f"config{args.config}" + (f"_{args.flex}" if args.config == 5 else "")
+    roof["traffic"] = measured_traffic(key, work["kind"])
+    roof["kernel_ms"] = round(per_launch_s * 1e3, 4)
+
+    cpu = None
+    if sample is not None and not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            r = sample()
+        cpu = dict(value=round(r["flops"] / r["seconds"] / 1e12, 6), unit="TFLOP/s", cores=_cores(),
+                   kind="oracle", sample=r["sample"], seconds=round(r["seconds"], 2))
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-kv/bf16" if args.config in (3, 4) else "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, **cfg_extra},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    if work["bound"] == "hbm":
+        line["config"]["tflops"] = round(tflops, 3)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -52,7 +52,7 @@ def test_dense_small_config():
     d = synth.make_dense(1, 128, 128, 2, 2, 64, 64, seed=synth.seed_for(1))
     o, lse = _dense_run(d, dict(scale=1 / 8), 64)
     o_ref, l_ref = oracle.attention_dense(f64(d["q"]), f64(d["k"]), f64(d["v"]), dict(scale=1 / 8))
-    compare(o, lse, o_ref, l_ref, TOL_O_BF16, what="dense cfg1")
+    compare(o.permute(0, 2, 1, 3), lse, o_ref.transpose(0, 2, 1, 3), l_ref, TOL_O_BF16, what="dense cfg1")
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -62,7 +62,8 @@ def test_dense_shapes(D, causal, Sq, Skv):
     d = synth.make_dense(2, Sq, Skv, 4, 2, D, D, seed=11 + Sq + 7 * Skv + D)
     o, lse = _dense_run(d, dict(causal=causal), D)
     o_ref, l_ref = oracle.attention_dense(f64(d["q"]), f64(d["k"]), f64(d["v"]), dict(causal=causal))
-    compare(o, lse, o_ref, l_ref, TOL_O_BF16, what=f"dense D{D} c{causal} {Sq}x{Skv}")
+    compare(o.permute(0, 2, 1, 3), lse, o_ref.transpose(0, 2, 1, 3), l_ref, TOL_O_BF16,
+            what=f"dense D{D} c{causal} {Sq}x{Skv}")
 
 
 # ----------------------------------------------------------------------------- varlen
@@ -326,7 +327,7 @@ def test_flex_mods_small(case):
     mods = FLEX_CASES[case]
     o, lse = _dense_run(d, mods, 128)
     o_ref, l_ref = oracle.attention_dense(f64(d["q"]), f64(d["k"]), f64(d["v"]), dict(mods))
-    compare(o, lse, o_ref, l_ref, TOL_O_BF16, what=case)
+    compare(o.permute(0, 2, 1, 3), lse, o_ref.transpose(0, 2, 1, 3), l_ref, TOL_O_BF16, what=case)
 
 
 @pytest.mark.parametrize("kind", ["bernoulli", "block_causal", "bernoulli_causal"])
@@ -342,7 +343,7 @@ def test_flex_block_mask_small(kind):
     mods = dict(block_mask=bm.to(DEV), mask_block=(128, 128), causal=kind.endswith("causal") and kind != "block_causal")
     o, lse = _dense_run(d, mods, 128)
     o_ref, l_ref = oracle.attention_dense(f64(d["q"]), f64(d["k"]), f64(d["v"]), _oracle_mods(mods))
-    compare(o, lse, o_ref, l_ref, TOL_O_BF16, what=kind)
+    compare(o.permute(0, 2, 1, 3), lse, o_ref.transpose(0, 2, 1, 3), l_ref, TOL_O_BF16, what=kind)
 
 
 @pytest.mark.parametrize("case", ["alibi", "softcap", "window", "bernoulli", "block_causal"])
