@@ -16,7 +16,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libfa.so")
 if not os.path.exists(library_path):
-    raise ImportError(f"{library_path} is missing: build it with `python -m attention_fa_fwd_03_amd.build`")
+    raise ImportError(f"{library_path} is missing: build it with `python attention_fa_fwd_03_amd/build.py`")
 lib = ctypes.CDLL(library_path)
 
 FA_CAUSAL, FA_WINDOW, FA_ALIBI, FA_SOFTCAP, FA_BLOCK_MASK = 1, 2, 4, 8, 16

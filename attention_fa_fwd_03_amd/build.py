@@ -1,6 +1,7 @@
 """Compile libfa.so (HIP kernels + C ABI) for gfx950 with hipcc.
 
-Usage: python -m attention_fa_fwd_03_amd.build   (or build() from Python).
+Usage: python attention_fa_fwd_03_amd/build.py   (or build() from Python; the
+package itself cannot be imported before the library exists).
 Objects go to _build/ at the repository root; the shared library is written
 next to this file so that the Python binding finds it in-tree.
 """

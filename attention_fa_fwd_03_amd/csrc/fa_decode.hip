@@ -30,7 +30,11 @@ constexpr int kDecWaves = 4;
 constexpr int kDecKT = 32;       // keys per tile
 constexpr int kDecStages = 3;    // V tiles in flight per wavefront
 
-__device__ __forceinline__ int dec_vswz(int r) { return ((r & 3) << 1) | ((r >> 3) & 1); }
+// V tile rows are 128 bytes (alternating halves of the 64-bank LDS); the
+// transposed reads take rows {0-3, 8-11} (+4 for lanes 32-63) at 2 chunks per
+// 32 lanes.  Spreading rows {0, 2, 8, 10} over even chunk offsets makes the
+// 32 accesses hit distinct banks.
+__device__ __forceinline__ int dec_vswz(int r) { return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)); }
 
 __device__ __forceinline__ i32x2 lds_read_tr8(const char FA_LDS* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 FA_LDS*)(p));

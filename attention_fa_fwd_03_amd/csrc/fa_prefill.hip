@@ -32,8 +32,10 @@
 // K/V staging: bf16 K/V go global -> LDS with global_load_lds_dwordx4 (no
 // registers); FP8 E4M3 K/V are loaded to registers one tile ahead, converted
 // exactly to bf16 and written to LDS.  LDS rows are 16-byte-chunk XOR
-// swizzled (chunk c of row r stored at c ^ (r & 7)) so that both the K reads
-// and the transposed V reads are bank-conflict free.
+// swizzled so that both the K reads and the transposed V reads are
+// bank-conflict free.  Whole tiles take a fast addressing path (per-lane
+// 32-bit offsets from one scalar tile base); the sequence tail and pages
+// smaller than a tile take a clamped per-row path.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -64,98 +66,158 @@ struct SeqView {
   int64_t qstart, kstart; // first token row (packed Q/O; contiguous K/V)
 };
 
-// Element offset of key row j.  `tile_page` is the wave-uniform page of the
-// tile when pages hold at least one whole tile (page_size >= 64), else -1
-// and each row looks its page up.
+// LDS row swizzle: 16-byte chunk c of tile row r is stored at c ^ swz(r).
+// The LDS behaves as 64 four-byte banks (256 bytes per conflict-free cycle).
+// K reads (ds_read_b128) touch rows r..r+15 at one chunk per 16 lanes; the
+// transposed V reads (ds_read_b64_tr_b16) touch 4 rows x 4 adjacent chunks
+// per 32 lanes.  256-byte rows: a 4-bit map that is a bijection on r mod 16
+// and sends the 4 rows of a V group to distinct quarters of the bank space.
+// 128- and 384-byte rows alternate bank halves by themselves: a 3-bit map on
+// r >> 1 that also keeps rows 2 apart in different 4-chunk groups.  The XOR
+// stays inside aligned groups of 16 (8) chunks, i.e. inside the row.
+template <int kRow>
+__device__ __forceinline__ int swz(int r) {
+  if (kRow == 256) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Element offset of key row j in the slow path (tail tiles, pages smaller
+// than a tile): clamped row, per-row page lookup.
 __device__ __forceinline__ int64_t key_row_offset(const PrefillArgs& a, const SeqView& sv, int j,
-                                                  int64_t tok_stride, int64_t head_stride,
-                                                  int64_t page_stride, bool paged, int tile_page) {
+                                                  int64_t st, int64_t sh, int64_t pg, bool paged) {
+  j = j < sv.skv ? j : sv.skv - 1;                  // tail rows are masked anyway
   if (paged) {
-    int page = tile_page >= 0 ? tile_page : a.block_table[(int64_t)sv.b * a.max_pages + (j >> a.page_shift)];
+    int page = a.block_table[(int64_t)sv.b * a.max_pages + (j >> a.page_shift)];
     page = min(max(page, 0), a.num_pages - 1);      // never read outside the cache
     const int slot = j & ((1 << a.page_shift) - 1);
-    return (int64_t)page * page_stride + (int64_t)sv.g * head_stride + (int64_t)slot * tok_stride;
+    return (int64_t)page * pg + (int64_t)sv.g * sh + (int64_t)slot * st;
   }
-  return (sv.kstart + j) * tok_stride + (int64_t)sv.g * head_stride;
+  return (sv.kstart + j) * st + (int64_t)sv.g * sh;
 }
 
-// Page of tile k0 when a page spans whole tiles (scalar load), else -1.
-__device__ __forceinline__ int tile_page_of(const PrefillArgs& a, const SeqView& sv, int k0, bool paged) {
-  if (!paged || a.page_shift < 6) return -1;
-  return load_uniform_i32(a.block_table, (int64_t)sv.b * a.max_pages + (k0 >> a.page_shift));
+// Element offset of row 0 of tile k0 in the fast path (whole tile inside the
+// sequence and, for paged caches, inside one page: one scalar page lookup).
+__device__ __forceinline__ int64_t tile_base(const PrefillArgs& a, const SeqView& sv, int k0,
+                                             int64_t st, int64_t sh, int64_t pg, bool paged) {
+  if (paged) {
+    int page = load_uniform_i32(a.block_table, (int64_t)sv.b * a.max_pages + (k0 >> a.page_shift));
+    page = min(max(page, 0), a.num_pages - 1);
+    return (int64_t)page * pg + (int64_t)sv.g * sh + (int64_t)(k0 & ((1 << a.page_shift) - 1)) * st;
+  }
+  return (sv.kstart + k0) * st + (int64_t)sv.g * sh;
 }
 
-// Issue the bf16 copy of one K or V tile into LDS (global_load_lds).
+// bf16 tile of D columns: global -> LDS with one 1 KB global_load_lds per
+// wave instruction.  Instruction n covers LDS bytes [n*1024, n*1024+1024);
+// lane l fills 16 bytes at n*1024 + 16*l, i.e. tile row r, stored chunk pos,
+// which holds source chunk pos ^ swz(r).
 template <int D, bool PAGED>
-__device__ __forceinline__ void stage_bf16(const PrefillArgs& a, const SeqView& sv, const bf16* base,
-                                           int64_t tok_stride, int64_t head_stride, int64_t page_stride,
-                                           char FA_LDS* tile, int k0, int tile_page) {
-  constexpr int kRow = D * 2;
-  constexpr int kInstr = BN * kRow / 1024;          // 1 KB per wave instruction
-  constexpr int kPerWave = kInstr / 4;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+struct Bf16Stager {
+  static constexpr int kRow = D * 2;
+  static constexpr int kPerWave = BN * kRow / 1024 / 4;
+  int off[kPerWave];   // element offset of this lane's 16 bytes from tile row 0
+  int row[kPerWave];
+  int chunk[kPerWave];
+  __device__ __forceinline__ void init(int64_t st, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < kPerWave; ++i) {
-    const int n = wave * kPerWave + i;
-    const int byte = n * 1024 + lane * 16;
-    const int r = byte / kRow;
-    const int pos = (byte % kRow) >> 4;
-    const int c = pos ^ (r & 7);
-    int j = k0 + r;
-    j = j < sv.skv ? j : sv.skv - 1;                 // clamp: tail rows are masked anyway
-    const int64_t off = key_row_offset(a, sv, j, tok_stride, head_stride, page_stride, PAGED, tile_page);
-    global_to_lds16(base + off + c * 8, tile + n * 1024);
+    for (int i = 0; i < kPerWave; ++i) {
+      const int byte = (wave * kPerWave + i) * 1024 + lane * 16;
+      row[i] = byte / kRow;
+      chunk[i] = ((byte % kRow) >> 4) ^ swz<kRow>(row[i]);
+      off[i] = row[i] * (int)st + chunk[i] * 8;
+    }
   }
-}
-
-template <int D>
-struct Fp8Regs {
-  static constexpr int kItems = BN * D / 16;
-  static constexpr int kPer = (kItems + NTHREADS - 1) / NTHREADS;
-  i32x4 w[kPer];
+  __device__ __forceinline__ void issue(const PrefillArgs& a, const SeqView& sv, const bf16* base, int64_t st,
+                                        int64_t sh, int64_t pg, char FA_LDS* tile, int k0, bool fast, int wave) {
+    if (fast) {
+      const bf16* tb = base + tile_base(a, sv, k0, st, sh, pg, PAGED);
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i) global_to_lds16(tb + off[i], tile + (wave * kPerWave + i) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i)
+        global_to_lds16(base + key_row_offset(a, sv, k0 + row[i], st, sh, pg, PAGED) + chunk[i] * 8,
+                        tile + (wave * kPerWave + i) * 1024);
+    }
+  }
 };
 
+// FP8 tile of D columns: 16-byte items loaded to registers one tile ahead,
+// converted exactly to bf16 and written to the swizzled LDS rows.
 template <int D, bool PAGED>
-__device__ __forceinline__ void load_fp8(const PrefillArgs& a, const SeqView& sv, const uint8_t* base,
-                                         int64_t tok_stride, int64_t head_stride, int64_t page_stride,
-                                         Fp8Regs<D>& regs, int k0, int tile_page) {
-  constexpr int kPerRow = D / 16;
+struct Fp8Stager {
+  static constexpr int kPerRow = D / 16;
+  static constexpr int kItems = BN * D / 16;
+  static constexpr int kPer = (kItems + NTHREADS - 1) / NTHREADS;
+  static constexpr int kRow = D * 2;
+  i32x4 w[kPer];
+  int off[kPer];
+  __device__ __forceinline__ void init(int64_t st, int tid) {
 #pragma unroll
-  for (int it = 0; it < Fp8Regs<D>::kPer; ++it) {
-    const int idx = it * NTHREADS + threadIdx.x;
-    if (Fp8Regs<D>::kItems % NTHREADS == 0 || idx < Fp8Regs<D>::kItems) {
-      const int r = idx / kPerRow, f = idx % kPerRow;
-      int j = k0 + r;
-      j = j < sv.skv ? j : sv.skv - 1;
-      const int64_t off = key_row_offset(a, sv, j, tok_stride, head_stride, page_stride, PAGED, tile_page);
-      regs.w[it] = *reinterpret_cast<const i32x4*>(base + off + f * 16);
+    for (int it = 0; it < kPer; ++it) {
+      const int idx = min(it * NTHREADS + tid, kItems - 1);
+      off[it] = (idx / kPerRow) * (int)st + (idx % kPerRow) * 16;
     }
   }
-}
-
-template <int D>
-__device__ __forceinline__ void store_fp8(const Fp8Regs<D>& regs, char FA_LDS* tile) {
-  constexpr int kPerRow = D / 16;
-  constexpr int kRow = D * 2;
+  __device__ __forceinline__ void load(const PrefillArgs& a, const SeqView& sv, const uint8_t* base, int64_t st,
+                                       int64_t sh, int64_t pg, int k0, bool fast, int tid) {
+    if (fast) {
+      const uint8_t* tb = base + tile_base(a, sv, k0, st, sh, pg, PAGED);
 #pragma unroll
-  for (int it = 0; it < Fp8Regs<D>::kPer; ++it) {
-    const int idx = it * NTHREADS + threadIdx.x;
-    if (Fp8Regs<D>::kItems % NTHREADS == 0 || idx < Fp8Regs<D>::kItems) {
-      const int r = idx / kPerRow, f = idx % kPerRow;
-      bf16x8 lo, hi;
-      fp8x16_to_bf16(regs.w[it], lo, hi);
-      char FA_LDS* row = tile + r * kRow;
-      *reinterpret_cast<bf16x8 FA_LDS*>(row + (((2 * f) ^ (r & 7)) << 4)) = lo;
-      *reinterpret_cast<bf16x8 FA_LDS*>(row + (((2 * f + 1) ^ (r & 7)) << 4)) = hi;
+      for (int it = 0; it < kPer; ++it) w[it] = *reinterpret_cast<const i32x4*>(tb + off[it]);
+    } else {
+#pragma unroll
+      for (int it = 0; it < kPer; ++it) {
+        const int idx = min(it * NTHREADS + tid, kItems - 1);
+        const int r = idx / kPerRow, f = idx % kPerRow;
+        w[it] = *reinterpret_cast<const i32x4*>(base + key_row_offset(a, sv, k0 + r, st, sh, pg, PAGED) + f * 16);
+      }
     }
   }
-}
+  __device__ __forceinline__ void store(char FA_LDS* tile, int tid) const {
+#pragma unroll
+    for (int it = 0; it < kPer; ++it) {
+      const int idx = it * NTHREADS + tid;
+      if (kItems % NTHREADS == 0 || idx < kItems) {
+        const int r = idx / kPerRow, f = idx % kPerRow;
+        bf16x8 lo, hi;
+        fp8x16_to_bf16(w[it], lo, hi);
+        char FA_LDS* rowp = tile + r * kRow;
+        *reinterpret_cast<bf16x8 FA_LDS*>(rowp + (((2 * f) ^ swz<kRow>(r)) << 4)) = lo;
+        *reinterpret_cast<bf16x8 FA_LDS*>(rowp + (((2 * f + 1) ^ swz<kRow>(r)) << 4)) = hi;
+      }
+    }
+  }
+};
 
-__device__ __forceinline__ bool tile_active(const PrefillArgs& a, const SeqView& sv, int q0, int t) {
-  if (!a.bmask) return true;
-  const int64_t row = ((int64_t)sv.b * a.Hq + sv.h) * a.bm_nqb + q0 / a.bm_bq;
-  return a.bmask[row * a.bm_nkb + (t * BN) / a.bm_bk] != 0;
-}
+// Active-tile bits of a block-mask row, 64 mask key-blocks at a time (one
+// vector load and a ballot per 64 blocks; the per-tile test is scalar).
+struct MaskBits {
+  const uint8_t* row;   // mask bytes of this (sequence, head, query block)
+  int nkb, bk;
+  int chunk;
+  uint64_t bits;
+  __device__ __forceinline__ void init(const PrefillArgs& a, const SeqView& sv, int q0) {
+    row = a.bmask ? a.bmask + (((int64_t)sv.b * a.Hq + sv.h) * a.bm_nqb + q0 / a.bm_bq) * a.bm_nkb : nullptr;
+    nkb = a.bm_nkb;
+    bk = a.bm_bk;
+    chunk = -1;
+    bits = ~0ull;
+  }
+  __device__ __forceinline__ bool active(int t) {
+    if (!row) return true;
+    const int kb = (t * BN) / bk;
+    const int c = kb >> 6;
+    if (c != chunk) {
+      const int lane = __lane_id();
+      const int idx = c * 64 + lane;
+      const bool on = idx < nkb && row[idx] != 0;
+      bits = __builtin_amdgcn_ballot_w64(on);
+      chunk = c;
+    }
+    return (bits >> (kb & 63)) & 1ull;
+  }
+};
 
 template <int DQK, int DV, bool FP8, bool PAGED, int MODS>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2)))
@@ -168,7 +230,8 @@ void fa_prefill_kernel(const PrefillArgs a) {
   constexpr bool SOFTCAP = (MODS & kModSoftcap) != 0;
   constexpr bool ANYMOD = ALIBI || SOFTCAP;
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int bh = blockIdx.x;
   const int qt = (int)gridDim.y - 1 - (int)blockIdx.y;   // longest causal tiles first
   SeqView sv;
@@ -185,7 +248,7 @@ void fa_prefill_kernel(const PrefillArgs a) {
   }
   if (PAGED) {
     sv.kstart = 0;
-    sv.skv = (int)min((int64_t)a.seqlen_k[sv.b], (int64_t)a.max_pages << a.page_shift);   // bounded page-table lookups
+    sv.skv = (int)min((int64_t)a.seqlen_k[sv.b], (int64_t)a.max_pages << a.page_shift);   // bounded lookups
   } else if (a.cu_k) {
     const int s0 = a.cu_k[sv.b], s1 = a.cu_k[sv.b + 1];
     sv.kstart = s0;
@@ -199,7 +262,8 @@ void fa_prefill_kernel(const PrefillArgs a) {
   const int q1 = min(q0 + BM, sv.sq);
   const int delta = sv.skv - sv.sq;
 
-  // Visible key interval of a row i (aligned position i' = i + delta).
+  // Visible key interval [row_lo(i), row_hi(i)] of query row i (aligned
+  // position i' = i + delta); empty when row_hi < row_lo.
   auto row_hi = [&](int i) {
     int hi = sv.skv - 1;
     if (a.causal) hi = min(hi, i + delta);
@@ -230,6 +294,7 @@ void fa_prefill_kernel(const PrefillArgs a) {
     }
   }
   const int my_lo = row_lo(qrow), my_hi = row_hi(qrow);
+  const unsigned my_cnt = (unsigned)max(my_hi - my_lo + 1, 0);
   const int wq0 = q0 + wave * 32;
   const int wave_lo_max = row_lo(wq0 + 31), wave_hi_min = row_hi(wq0);
 
@@ -243,32 +308,52 @@ void fa_prefill_kernel(const PrefillArgs a) {
   const float raw_scale = a.qk_scale * kdesc;      // raw dot -> natural scaled logit
   const float cap = a.softcap, inv_cap = SOFTCAP ? 1.0f / a.softcap : 0.0f;
   const int ip = qrow + delta;
+  const int lane_key = (lane >> 5) * 4;            // key offset of this lane's S^T registers
 
   f32x16 oacc[DV / 32];
 #pragma unroll
   for (int d = 0; d < DV / 32; ++d) oacc[d] = f32x16{};
   float m_run = kMaxFloor, l_run = 0.0f;
 
-  // find first active tile
-  while (t_begin <= t_end && !tile_active(a, sv, q0, t_begin)) ++t_begin;
+  MaskBits mb;
+  mb.init(a, sv, q0);
+  while (t_begin <= t_end && !mb.active(t_begin)) ++t_begin;
 
   char FA_LDS* stage0 = lds;
   char FA_LDS* stage1 = lds + T::kStage;
   const int64_t kpg = a.k_pg, vpg = a.v_pg;
+  const bool small_pages = PAGED && a.page_shift < 6;
+  auto fast_tile = [&](int k0) { return k0 + BN <= sv.skv && !small_pages; };
 
-  Fp8Regs<DQK> kreg;
-  Fp8Regs<DV> vreg;
+  Bf16Stager<DQK, PAGED> kdma;
+  Bf16Stager<DV, PAGED> vdma;
+  Fp8Stager<DQK, PAGED> k8;
+  Fp8Stager<DV, PAGED> v8;
+  if (FP8) {
+    k8.init(a.k_st, tid);
+    v8.init(a.v_st, tid);
+  } else {
+    kdma.init(a.k_st, wave, lane);
+    vdma.init(a.v_st, wave, lane);
+  }
+  auto issue = [&](int t, char FA_LDS* st) {
+    const int k0 = t * BN;
+    const bool fast = fast_tile(k0);
+    if (FP8) {
+      k8.load(a, sv, reinterpret_cast<const uint8_t*>(a.k), a.k_st, a.k_sh, kpg, k0, fast, tid);
+      v8.load(a, sv, reinterpret_cast<const uint8_t*>(a.v), a.v_st, a.v_sh, vpg, k0, fast, tid);
+    } else {
+      kdma.issue(a, sv, reinterpret_cast<const bf16*>(a.k), a.k_st, a.k_sh, kpg, st, k0, fast, wave);
+      vdma.issue(a, sv, reinterpret_cast<const bf16*>(a.v), a.v_st, a.v_sh, vpg, st + T::kTileK, k0, fast, wave);
+    }
+  };
 
   if (t_begin <= t_end) {
-    const int tp = tile_page_of(a, sv, t_begin * BN, PAGED);
+    issue(t_begin, stage0);
     if (FP8) {
-      load_fp8<DQK, PAGED>(a, sv, reinterpret_cast<const uint8_t*>(a.k), a.k_st, a.k_sh, kpg, kreg, t_begin * BN, tp);
-      load_fp8<DV, PAGED>(a, sv, reinterpret_cast<const uint8_t*>(a.v), a.v_st, a.v_sh, vpg, vreg, t_begin * BN, tp);
-      store_fp8<DQK>(kreg, stage0);
-      store_fp8<DV>(vreg, stage0 + T::kTileK);
+      k8.store(stage0, tid);
+      v8.store(stage0 + T::kTileK, tid);
     } else {
-      stage_bf16<DQK, PAGED>(a, sv, reinterpret_cast<const bf16*>(a.k), a.k_st, a.k_sh, kpg, stage0, t_begin * BN, tp);
-      stage_bf16<DV, PAGED>(a, sv, reinterpret_cast<const bf16*>(a.v), a.v_st, a.v_sh, vpg, stage0 + T::kTileK, t_begin * BN, tp);
       FA_WAIT_VMCNT(0);
     }
     __syncthreads();
@@ -277,61 +362,69 @@ void fa_prefill_kernel(const PrefillArgs a) {
   int cur = 0;
   for (int t = t_begin; t <= t_end;) {
     int tn = t + 1;
-    while (tn <= t_end && !tile_active(a, sv, q0, tn)) ++tn;
+    while (tn <= t_end && !mb.active(tn)) ++tn;
     const bool has_next = tn <= t_end;
     char FA_LDS* sc = cur ? stage1 : stage0;
     char FA_LDS* sn = cur ? stage0 : stage1;
-    if (has_next) {
-      const int tp = tile_page_of(a, sv, tn * BN, PAGED);
-      if (FP8) {
-        load_fp8<DQK, PAGED>(a, sv, reinterpret_cast<const uint8_t*>(a.k), a.k_st, a.k_sh, kpg, kreg, tn * BN, tp);
-        load_fp8<DV, PAGED>(a, sv, reinterpret_cast<const uint8_t*>(a.v), a.v_st, a.v_sh, vpg, vreg, tn * BN, tp);
-      } else {
-        stage_bf16<DQK, PAGED>(a, sv, reinterpret_cast<const bf16*>(a.k), a.k_st, a.k_sh, kpg, sn, tn * BN, tp);
-        stage_bf16<DV, PAGED>(a, sv, reinterpret_cast<const bf16*>(a.v), a.v_st, a.v_sh, vpg, sn + T::kTileK, tn * BN, tp);
-      }
-    }
+    if (has_next) issue(tn, sn);
 
     const int k0 = t * BN;
     // ---------------- S^T = K Q^T ----------------
-    f32x16 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
-      const int r = kb * 32 + (lane & 31);
+    // two independent accumulation chains (key blocks 0 and 1) interleaved
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    {
+      const int r = lane & 31;                       // swz(r) == swz(r + 32)
       const char FA_LDS* rowp = sc + r * T::kRowK;
 #pragma unroll
       for (int s = 0; s < DQK / 16; ++s) {
         const int c = s * 2 + (lane >> 5);
-        const bf16x8 kf = lds_read_b128(rowp + ((c ^ (r & 7)) << 4));
-        sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 kf = lds_read_b128(rowp + kb * 32 * T::kRowK + ((c ^ swz<T::kRowK>(r)) << 4));
+          sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
+        }
       }
     }
 
-    // ---------------- scores, masking ----------------
-    const bool need_mask = !(k0 >= wave_lo_max && k0 + BN - 1 <= wave_hi_min);
-    float mx = -INFINITY;
+    // ---------------- score mods (log2 domain) ----------------
+    if (ANYMOD) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = k0 + kb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-        float val = sacc[kb][i];
-        if (ANYMOD) {
-          float s = val * raw_scale;
+        for (int i = 0; i < 16; ++i) {
+          float s = sacc[kb][i] * raw_scale;
           if (SOFTCAP) s = cap * tanh_fast(s * inv_cap);
-          if (ALIBI) s -= a.alibi_slope * fabsf((float)(ip - j));
-          val = s * kLog2e;
+          if (ALIBI) {
+            const int j = k0 + kb * 32 + (i >> 2) * 8 + lane_key + (i & 3);
+            s -= a.alibi_slope * fabsf((float)(ip - j));
+          }
+          sacc[kb][i] = s * kLog2e;
         }
-        if (need_mask) val = (j >= my_lo && j <= my_hi) ? val : -INFINITY;
-        sacc[kb][i] = val;
-        mx = fmaxf(mx, val);
       }
     }
+    // ---------------- masks: only tiles that straddle a row's key interval ----------------
+    const bool need_mask = !(k0 >= wave_lo_max && k0 + BN - 1 <= wave_hi_min);
+    if (need_mask) {
+      // keeps this a real branch: selects would otherwise be speculated onto every tile
+      asm volatile("" ::);
+      const int base = k0 + lane_key - my_lo;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const unsigned rel = (unsigned)(base + kb * 32 + (i >> 2) * 8 + (i & 3));
+          sacc[kb][i] = rel < my_cnt ? sacc[kb][i] : -INFINITY;
+        }
+    }
+    // ---------------- online softmax ----------------
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
     mx = max_pair32(mx);
     const float m_new = fmaxf(m_run, mx * C);
-    const bool grow = m_new > m_run + kLazyTau;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run + kLazyTau) != 0) {
       const float alpha = exp2_hw(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
@@ -364,8 +457,8 @@ void fa_prefill_kernel(const PrefillArgs a) {
         for (int d = 0; d < DV / 32; ++d) {
           const int dcol = d * 32 + (grp & 1) * 16 + 4 * (i16 & 3);
           const int chunk = dcol >> 3, half = (dcol >> 2) & 1;
-          const bf16x4 lo4 = lds_read_tr16(vt + r1 * T::kRowV + ((chunk ^ (r1 & 7)) << 4) + half * 8);
-          const bf16x4 hi4 = lds_read_tr16(vt + r2 * T::kRowV + ((chunk ^ (r2 & 7)) << 4) + half * 8);
+          const bf16x4 lo4 = lds_read_tr16(vt + r1 * T::kRowV + ((chunk ^ swz<T::kRowV>(r1)) << 4) + half * 8);
+          const bf16x4 hi4 = lds_read_tr16(vt + r2 * T::kRowV + ((chunk ^ swz<T::kRowV>(r2)) << 4) + half * 8);
           bf16x8 vf;
           vf[0] = lo4[0]; vf[1] = lo4[1]; vf[2] = lo4[2]; vf[3] = lo4[3];
           vf[4] = hi4[0]; vf[5] = hi4[1]; vf[6] = hi4[2]; vf[7] = hi4[3];
@@ -376,8 +469,8 @@ void fa_prefill_kernel(const PrefillArgs a) {
 
     if (has_next) {
       if (FP8) {
-        store_fp8<DQK>(kreg, sn);
-        store_fp8<DV>(vreg, sn + T::kTileK);
+        k8.store(sn, tid);
+        v8.store(sn + T::kTileK, tid);
       } else {
         FA_WAIT_VMCNT(0);
       }
