@@ -32,7 +32,8 @@ int fail(int code, const char* fmt, ...) {
 }
 
 constexpr int64_t kI32 = (int64_t)1 << 31;
-constexpr int kBM = 128;           // prefill query rows per workgroup
+constexpr int kBM = 256;           // prefill query rows per workgroup
+constexpr int kMaskBQ = 128;       // block-mask query tiles: multiples of half a workgroup
 constexpr int kBN = 64;            // prefill keys per tile
 constexpr int kDecodeRows = 32;    // decode rows (query x q-head-in-group) per wavefront
 
@@ -79,9 +80,9 @@ int read_mods(const fa_mods* m, int64_t d_qk, int64_t max_sq, int64_t max_sk, Mo
       r.nqb = m->mask_nqb;
       r.nkb = m->mask_nkb;
       if (!r.bm) return fail(FA_ERR_INVALID, "FA_BLOCK_MASK set but block_mask is NULL");
-      if (r.bq <= 0 || r.bk <= 0 || r.bq % kBM != 0 || r.bk % kBN != 0)
+      if (r.bq <= 0 || r.bk <= 0 || r.bq % kMaskBQ != 0 || r.bk % kBN != 0)
         return fail(FA_ERR_UNSUPPORTED, "block mask tiles must be multiples of %d (query) and %d (key), got %lld x %lld",
-                    kBM, kBN, (long long)r.bq, (long long)r.bk);
+                    kMaskBQ, kBN, (long long)r.bq, (long long)r.bk);
       if (r.nqb < (max_sq + r.bq - 1) / r.bq || r.nkb < (max_sk + r.bk - 1) / r.bk)
         return fail(FA_ERR_INVALID, "block mask geometry %lld x %lld does not cover %lld x %lld tokens",
                     (long long)r.nqb, (long long)r.nkb, (long long)max_sq, (long long)max_sk);
@@ -123,13 +124,16 @@ int mod_bits(const Mods& m) {
   return ((m.flags & FA_ALIBI) ? fa::kModAlibi : 0) | ((m.flags & FA_SOFTCAP) ? fa::kModSoftcap : 0);
 }
 
-int launch_prefill(const fa::PrefillArgs& a, int64_t dqk, int64_t dv, bool fp8, bool paged, int mods,
+int launch_prefill(const fa::PrefillArgs& a_in, int64_t dqk, int64_t dv, bool fp8, bool paged, int mods,
                    int64_t B, int64_t Hq, int64_t max_sq, hipStream_t stream) {
   const int64_t n_bh = B * Hq;
   const int64_t n_qt = (max_sq + kBM - 1) / kBM;
-  if (n_bh >= kI32) return fail(FA_ERR_LIMIT, "B*Hq = %lld exceeds the grid limit", (long long)n_bh);
+  // grid: x = B*Hq rounded up to 8, y = query tiles
+  if (n_bh + 7 >= kI32) return fail(FA_ERR_LIMIT, "B*Hq = %lld exceeds the grid limit", (long long)n_bh);
   if (n_qt > 65535) return fail(FA_ERR_LIMIT, "max_seqlen_q = %lld exceeds %d", (long long)max_sq, 65535 * kBM);
   if (n_bh == 0 || n_qt == 0) return FA_OK;
+  fa::PrefillArgs a = a_in;
+  a.n_bh = (int)n_bh;
   bool supported = false;
   hipError_t e = fa::prefill_dispatch(a, (int)dqk, (int)dv, fp8, paged, mods, (int)n_bh, (int)n_qt, stream, &supported);
   if (!supported) return fail(FA_ERR_UNSUPPORTED, "no kernel built for d_qk=%lld d_v=%lld fp8=%d paged=%d mods=%d",

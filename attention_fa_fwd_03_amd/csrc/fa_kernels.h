@@ -29,6 +29,7 @@ struct PrefillArgs {
   int64_t lse_tq;              // packed layouts: LSE is [Hq, lse_tq]
   int Sq, Skv;                 // dense lengths
   int Hq, group;               // group = Hq / Hkv
+  int n_bh;                    // B * Hq (the grid's x extent is this rounded up to 8)
   int max_pages;
   int page_shift;
   int num_pages;               // paged: page ids are clamped to [0, num_pages)

@@ -1,8 +1,10 @@
 // Fused attention forward (prefill / dense / varlen / paged) for gfx950.
 //
-// One workgroup = 4 wavefronts = 128 query rows of one (sequence, q-head);
-// each wavefront owns 32 query rows.  The key axis is walked in tiles of 64
-// keys staged in LDS (double buffered).  Per tile and wavefront:
+// One workgroup = 8 wavefronts = 256 query rows of one (sequence, q-head);
+// each wavefront owns 32 query rows, two wavefronts share each SIMD.  The key
+// axis is walked in tiles of 64 keys staged in LDS (bf16: a ring of three
+// stages, so every tile load has two iterations to land).  Per tile and
+// wavefront:
 //
 //   S^T[64 x 32]  = K_tile . Q^T          v_mfma_f32_32x32x16_bf16, A = K from LDS,
 //                                          B = Q fragments kept in registers
@@ -27,10 +29,13 @@
 // Masking is by select to -inf (never by multiply, so NaN bytes in unused
 // cache slots cannot leak), with rows that see no key producing O = 0 and
 // LSE = -inf.  Tiles wholly outside the causal / window range or inactive in
-// the block mask are skipped; tiles wholly inside skip the per-score mask.
+// the block mask are not loaded; a wavefront whose own 32 rows see nothing
+// in a loaded tile skips its math for that tile; tiles wholly inside a
+// wavefront's range skip the per-score mask.
 //
 // K/V staging: bf16 K/V go global -> LDS with global_load_lds_dwordx4 (no
-// registers); FP8 E4M3 K/V are loaded to registers one tile ahead, converted
+// registers), two tiles ahead; FP8 E4M3 K/V are loaded to registers one tile
+// ahead (two LDS stages), converted
 // exactly to bf16 and written to LDS.  LDS rows are 16-byte-chunk XOR
 // swizzled so that both the K reads and the transposed V reads are
 // bank-conflict free.  Whole tiles take a fast addressing path (per-lane
@@ -41,9 +46,12 @@
 
 namespace fa {
 
-constexpr int BM = 128;
+constexpr int NWAVES = 8;
+constexpr int BM = 32 * NWAVES;
 constexpr int BN = 64;
-constexpr int NTHREADS = 256;
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr int kMaskRows = 128;          // block-mask query tiles are multiples of this
+constexpr int kHalves = BM / kMaskRows; // mask rows one workgroup can span
 constexpr float kLazyTau = 8.0f;
 
 template <int DQK, int DV, bool FP8>
@@ -53,7 +61,8 @@ struct PrefillTraits {
   static constexpr int kTileK = BN * kRowK;
   static constexpr int kTileV = BN * kRowV;
   static constexpr int kStage = kTileK + kTileV;
-  static constexpr int kLds = 2 * kStage;
+  static constexpr int kStages = FP8 ? 2 : 3;     // FP8 tiles wait one iteration in registers
+  static constexpr int kLds = kStages * kStage;
   static constexpr int kKItems = BN * DQK / 16;    // 16-byte source items per K tile (fp8)
   static constexpr int kVItems = BN * DV / 16;
   static constexpr int kKPer = (kKItems + NTHREADS - 1) / NTHREADS;
@@ -114,30 +123,37 @@ __device__ __forceinline__ int64_t tile_base(const PrefillArgs& a, const SeqView
 template <int D, bool PAGED>
 struct Bf16Stager {
   static constexpr int kRow = D * 2;
-  static constexpr int kPerWave = BN * kRow / 1024 / 4;
+  static constexpr int kPerWave = BN * kRow / 1024 / NWAVES;
+  static_assert(kPerWave >= 1, "a bf16 tile must give every wavefront a 1 KB piece");
   int off[kPerWave];   // element offset of this lane's 16 bytes from tile row 0
-  int row[kPerWave];
-  int chunk[kPerWave];
+  __device__ __forceinline__ static void place(int i, int wave, int lane, int& row, int& chunk) {
+    const int byte = (wave * kPerWave + i) * 1024 + lane * 16;
+    row = byte / kRow;
+    chunk = ((byte % kRow) >> 4) ^ swz<kRow>(row);
+  }
   __device__ __forceinline__ void init(int64_t st, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
-      const int byte = (wave * kPerWave + i) * 1024 + lane * 16;
-      row[i] = byte / kRow;
-      chunk[i] = ((byte % kRow) >> 4) ^ swz<kRow>(row[i]);
-      off[i] = row[i] * (int)st + chunk[i] * 8;
+      int row, chunk;
+      place(i, wave, lane, row, chunk);
+      off[i] = row * (int)st + chunk * 8;
     }
   }
   __device__ __forceinline__ void issue(const PrefillArgs& a, const SeqView& sv, const bf16* base, int64_t st,
-                                        int64_t sh, int64_t pg, char FA_LDS* tile, int k0, bool fast, int wave) {
+                                        int64_t sh, int64_t pg, char FA_LDS* tile, int k0, bool fast, int wave,
+                                        int lane) {
     if (fast) {
       const bf16* tb = base + tile_base(a, sv, k0, st, sh, pg, PAGED);
 #pragma unroll
       for (int i = 0; i < kPerWave; ++i) global_to_lds16(tb + off[i], tile + (wave * kPerWave + i) * 1024);
     } else {
 #pragma unroll
-      for (int i = 0; i < kPerWave; ++i)
-        global_to_lds16(base + key_row_offset(a, sv, k0 + row[i], st, sh, pg, PAGED) + chunk[i] * 8,
+      for (int i = 0; i < kPerWave; ++i) {
+        int row, chunk;
+        place(i, wave, lane, row, chunk);
+        global_to_lds16(base + key_row_offset(a, sv, k0 + row, st, sh, pg, PAGED) + chunk * 8,
                         tile + (wave * kPerWave + i) * 1024);
+      }
     }
   }
 };
@@ -190,32 +206,40 @@ struct Fp8Stager {
   }
 };
 
-// Active-tile bits of a block-mask row, 64 mask key-blocks at a time (one
-// vector load and a ballot per 64 blocks; the per-tile test is scalar).
+// Active-tile bits of the block-mask rows that a workgroup spans (one per
+// 128-query half), 64 mask key-blocks at a time: one vector load and a ballot
+// per row and 64 blocks; the per-tile tests are scalar.  tile_bits(t) has bit
+// h set when half h has tile t active.
 struct MaskBits {
-  const uint8_t* row;   // mask bytes of this (sequence, head, query block)
+  const uint8_t* row[kHalves];
   int nkb, bk;
   int chunk;
-  uint64_t bits;
+  uint64_t bits[kHalves];
   __device__ __forceinline__ void init(const PrefillArgs& a, const SeqView& sv, int q0) {
-    row = a.bmask ? a.bmask + (((int64_t)sv.b * a.Hq + sv.h) * a.bm_nqb + q0 / a.bm_bq) * a.bm_nkb : nullptr;
     nkb = a.bm_nkb;
     bk = a.bm_bk;
     chunk = -1;
-    bits = ~0ull;
+#pragma unroll
+    for (int h = 0; h < kHalves; ++h) {
+      const int qh = min(q0 + h * kMaskRows, sv.sq - 1);   // halves past the end reuse the last row
+      row[h] = a.bmask ? a.bmask + (((int64_t)sv.b * a.Hq + sv.h) * a.bm_nqb + qh / a.bm_bq) * a.bm_nkb : nullptr;
+      bits[h] = ~0ull;
+    }
   }
-  __device__ __forceinline__ bool active(int t) {
-    if (!row) return true;
+  __device__ __forceinline__ unsigned tile_bits(int t) {
+    if (!row[0]) return (1u << kHalves) - 1;
     const int kb = (t * BN) / bk;
     const int c = kb >> 6;
     if (c != chunk) {
-      const int lane = __lane_id();
-      const int idx = c * 64 + lane;
-      const bool on = idx < nkb && row[idx] != 0;
-      bits = __builtin_amdgcn_ballot_w64(on);
+      const int idx = c * 64 + __lane_id();
+#pragma unroll
+      for (int h = 0; h < kHalves; ++h) bits[h] = __builtin_amdgcn_ballot_w64(idx < nkb && row[h][idx] != 0);
       chunk = c;
     }
-    return (bits >> (kb & 63)) & 1ull;
+    unsigned r = 0;
+#pragma unroll
+    for (int h = 0; h < kHalves; ++h) r |= (unsigned)((bits[h] >> (kb & 63)) & 1ull) << h;
+    return r;
   }
 };
 
@@ -232,8 +256,12 @@ void fa_prefill_kernel(const PrefillArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  // grid.x is B*Hq rounded up to a multiple of 8 and workgroup i runs on XCD
+  // i % 8, so all query tiles of one (sequence, head) share one XCD's L2;
+  // grid.y walks the query tiles longest (causal) first
   const int bh = blockIdx.x;
-  const int qt = (int)gridDim.y - 1 - (int)blockIdx.y;   // longest causal tiles first
+  if (bh >= a.n_bh) return;
+  const int qt = (int)gridDim.y - 1 - (int)blockIdx.y;
   SeqView sv;
   sv.b = bh / a.Hq;
   sv.h = bh % a.Hq;
@@ -295,8 +323,13 @@ void fa_prefill_kernel(const PrefillArgs a) {
   }
   const int my_lo = row_lo(qrow), my_hi = row_hi(qrow);
   const unsigned my_cnt = (unsigned)max(my_hi - my_lo + 1, 0);
+  // this wavefront's rows [wq0, wq1]: union and intersection of their key ranges
   const int wq0 = q0 + wave * 32;
-  const int wave_lo_max = row_lo(wq0 + 31), wave_hi_min = row_hi(wq0);
+  const int wq1 = min(wq0 + 31, q1 - 1);
+  const bool wave_rows = wq0 < q1;
+  const int wave_lo_min = row_lo(wq0), wave_hi_max = row_hi(wq1);
+  const int wave_lo_max = row_lo(wq1), wave_hi_min = row_hi(wq0);
+  const int my_half = wave * 32 / kMaskRows;
 
   float kdesc = 1.0f, vdesc = 1.0f;
   if (FP8) {
@@ -317,10 +350,16 @@ void fa_prefill_kernel(const PrefillArgs a) {
 
   MaskBits mb;
   mb.init(a, sv, q0);
-  while (t_begin <= t_end && !mb.active(t_begin)) ++t_begin;
+  // next active tile at or after t (t_end + 1 when none), with its half bits
+  auto next_tile = [&](int t, unsigned& hb) {
+    for (; t <= t_end; ++t) {
+      hb = mb.tile_bits(t);
+      if (hb) return t;
+    }
+    hb = 0;
+    return t;
+  };
 
-  char FA_LDS* stage0 = lds;
-  char FA_LDS* stage1 = lds + T::kStage;
   const int64_t kpg = a.k_pg, vpg = a.v_pg;
   const bool small_pages = PAGED && a.page_shift < 6;
   auto fast_tile = [&](int k0) { return k0 + BN <= sv.skv && !small_pages; };
@@ -329,6 +368,7 @@ void fa_prefill_kernel(const PrefillArgs a) {
   Bf16Stager<DV, PAGED> vdma;
   Fp8Stager<DQK, PAGED> k8;
   Fp8Stager<DV, PAGED> v8;
+  constexpr int kDmaPerTile = Bf16Stager<DQK, PAGED>::kPerWave + Bf16Stager<DV, PAGED>::kPerWave;
   if (FP8) {
     k8.init(a.k_st, tid);
     v8.init(a.v_st, tid);
@@ -336,6 +376,8 @@ void fa_prefill_kernel(const PrefillArgs a) {
     kdma.init(a.k_st, wave, lane);
     vdma.init(a.v_st, wave, lane);
   }
+  auto stage_ptr = [&](int i) { return lds + i * T::kStage; };
+  // bf16: DMA straight into the stage.  FP8: load into registers only.
   auto issue = [&](int t, char FA_LDS* st) {
     const int k0 = t * BN;
     const bool fast = fast_tile(k0);
@@ -343,141 +385,180 @@ void fa_prefill_kernel(const PrefillArgs a) {
       k8.load(a, sv, reinterpret_cast<const uint8_t*>(a.k), a.k_st, a.k_sh, kpg, k0, fast, tid);
       v8.load(a, sv, reinterpret_cast<const uint8_t*>(a.v), a.v_st, a.v_sh, vpg, k0, fast, tid);
     } else {
-      kdma.issue(a, sv, reinterpret_cast<const bf16*>(a.k), a.k_st, a.k_sh, kpg, st, k0, fast, wave);
-      vdma.issue(a, sv, reinterpret_cast<const bf16*>(a.v), a.v_st, a.v_sh, vpg, st + T::kTileK, k0, fast, wave);
+      kdma.issue(a, sv, reinterpret_cast<const bf16*>(a.k), a.k_st, a.k_sh, kpg, st, k0, fast, wave, lane);
+      vdma.issue(a, sv, reinterpret_cast<const bf16*>(a.v), a.v_st, a.v_sh, vpg, st + T::kTileK, k0, fast, wave,
+                 lane);
     }
   };
+  auto fp8_store = [&](char FA_LDS* st) {
+    k8.store(st, tid);
+    v8.store(st + T::kTileK, tid);
+  };
 
-  if (t_begin <= t_end) {
-    issue(t_begin, stage0);
+  // Tile pipeline: t (computed now, stage sc), t1 and t2 (the next two
+  // active tiles).  bf16 keeps t and t1 (and after the issue below t2) in
+  // flight in the stage ring; FP8 keeps t1 in registers.
+  unsigned hb, hb1, hb2;
+  int t = next_tile(t_begin, hb);
+  int t1 = t <= t_end ? next_tile(t + 1, hb1) : t_end + 1;
+  int t2 = (!FP8 && t1 <= t_end) ? next_tile(t1 + 1, hb2) : t_end + 1;
+  if (FP8) hb2 = 0;
+  int sc = 0;
+  if (t <= t_end) {
+    issue(t, stage_ptr(0));
     if (FP8) {
-      k8.store(stage0, tid);
-      v8.store(stage0 + T::kTileK, tid);
+      fp8_store(stage_ptr(0));
+    } else if (t1 <= t_end) {
+      issue(t1, stage_ptr(1));
+      FA_WAIT_VMCNT(kDmaPerTile);
     } else {
       FA_WAIT_VMCNT(0);
     }
-    __syncthreads();
   }
 
-  int cur = 0;
-  for (int t = t_begin; t <= t_end;) {
-    int tn = t + 1;
-    while (tn <= t_end && !mb.active(tn)) ++tn;
-    const bool has_next = tn <= t_end;
-    char FA_LDS* sc = cur ? stage1 : stage0;
-    char FA_LDS* sn = cur ? stage0 : stage1;
-    if (has_next) issue(tn, sn);
-
+  while (t <= t_end) {
+    __syncthreads();   // tile t visible to all; everyone is done with the stage reused below
+    if (FP8) {
+      if (t1 <= t_end) issue(t1, nullptr);
+    } else if (t2 <= t_end) {
+      const int s2 = sc + 2 < T::kStages ? sc + 2 : sc + 2 - T::kStages;
+      issue(t2, stage_ptr(s2));
+    }
+    const char FA_LDS* cur = stage_ptr(sc);
     const int k0 = t * BN;
-    // ---------------- S^T = K Q^T ----------------
-    // two independent accumulation chains (key blocks 0 and 1) interleaved
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
-    {
-      const int r = lane & 31;                       // swz(r) == swz(r + 32)
-      const char FA_LDS* rowp = sc + r * T::kRowK;
+    const bool wave_active = wave_rows && k0 <= wave_hi_max && k0 + BN - 1 >= wave_lo_min &&
+                             ((hb >> my_half) & 1u);
+    if (wave_active) {
+      // ---------------- S^T = K Q^T ----------------
+      // two independent accumulation chains (key blocks 0 and 1); the K
+      // fragments of step s+1 are read while the products of step s run
+      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+      {
+        const int r = lane & 31;                       // swz(r) == swz(r + 32)
+        const char FA_LDS* rowp = cur + r * T::kRowK;
+        const int sw = swz<T::kRowK>(r);
+        auto kread = [&](int s, int kb) {
+          return lds_read_b128(rowp + kb * 32 * T::kRowK + (((s * 2 + (lane >> 5)) ^ sw) << 4));
+        };
+        bf16x8 kc0 = kread(0, 0), kc1 = kread(0, 1);
 #pragma unroll
-      for (int s = 0; s < DQK / 16; ++s) {
-        const int c = s * 2 + (lane >> 5);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 kf = lds_read_b128(rowp + kb * 32 * T::kRowK + ((c ^ swz<T::kRowK>(r)) << 4));
-          sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
+        for (int s = 0; s < DQK / 16; ++s) {
+          bf16x8 kn0, kn1;
+          if (s + 1 < DQK / 16) {
+            kn0 = kread(s + 1, 0);
+            kn1 = kread(s + 1, 1);
+          }
+          // keep the reads of step s+1 ahead of the products of step s
+          __builtin_amdgcn_sched_barrier(0);
+          sacc[0] = mfma32(kc0, qf[s], sacc[0]);
+          sacc[1] = mfma32(kc1, qf[s], sacc[1]);
+          kc0 = kn0;
+          kc1 = kn1;
         }
       }
-    }
 
-    // ---------------- score mods (log2 domain) ----------------
-    if (ANYMOD) {
+      // ---------------- score mods (log2 domain) ----------------
+      if (ANYMOD) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float x = sacc[kb][i] * raw_scale;
+            if (SOFTCAP) x = cap * tanh_fast(x * inv_cap);
+            if (ALIBI) {
+              const int j = k0 + kb * 32 + (i >> 2) * 8 + lane_key + (i & 3);
+              x -= a.alibi_slope * fabsf((float)(ip - j));
+            }
+            sacc[kb][i] = x * kLog2e;
+          }
+        }
+      }
+      // ---------------- masks: only tiles that straddle a row's key interval ----------------
+      const bool need_mask = !(k0 >= wave_lo_max && k0 + BN - 1 <= wave_hi_min);
+      if (need_mask) {
+        // keeps this a real branch: selects would otherwise be speculated onto every tile
+        asm volatile("" ::);
+        const int base = k0 + lane_key - my_lo;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const unsigned rel = (unsigned)(base + kb * 32 + (i >> 2) * 8 + (i & 3));
+            sacc[kb][i] = rel < my_cnt ? sacc[kb][i] : -INFINITY;
+          }
+      }
+      // ---------------- online softmax ----------------
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      mx = max_pair32(mx);
+      const float m_new = fmaxf(m_run, mx * C);
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run + kLazyTau) != 0) {
+        const float alpha = exp2_hw(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+      }
+      bf16x8 pf[4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float s = sacc[kb][i] * raw_scale;
-          if (SOFTCAP) s = cap * tanh_fast(s * inv_cap);
-          if (ALIBI) {
-            const int j = k0 + kb * 32 + (i >> 2) * 8 + lane_key + (i & 3);
-            s -= a.alibi_slope * fabsf((float)(ip - j));
+          const float p = exp2_hw(fmaf(sacc[kb][i], C, -m_run));
+          l_run += p;
+          pf[kb * 2 + (i >> 3)][i & 7] = (bf16)p;
+        }
+      }
+
+      // ---------------- O^T += V^T P^T ----------------
+      {
+        const char FA_LDS* vt = cur + T::kTileK;
+        const int grp = lane >> 4, i16 = lane & 15;
+        const int hsel = grp >> 1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r1 = u * 16 + hsel * 4 + (i16 >> 2);
+          const int r2 = r1 + 8;
+#pragma unroll
+          for (int d = 0; d < DV / 32; ++d) {
+            const int dcol = d * 32 + (grp & 1) * 16 + 4 * (i16 & 3);
+            const int chunk = dcol >> 3, half = (dcol >> 2) & 1;
+            const bf16x4 lo4 = lds_read_tr16(vt + r1 * T::kRowV + ((chunk ^ swz<T::kRowV>(r1)) << 4) + half * 8);
+            const bf16x4 hi4 = lds_read_tr16(vt + r2 * T::kRowV + ((chunk ^ swz<T::kRowV>(r2)) << 4) + half * 8);
+            bf16x8 vf;
+            vf[0] = lo4[0]; vf[1] = lo4[1]; vf[2] = lo4[2]; vf[3] = lo4[3];
+            vf[4] = hi4[0]; vf[5] = hi4[1]; vf[6] = hi4[2]; vf[7] = hi4[3];
+            oacc[d] = mfma32(vf, pf[u], oacc[d]);
           }
-          sacc[kb][i] = s * kLog2e;
-        }
-      }
-    }
-    // ---------------- masks: only tiles that straddle a row's key interval ----------------
-    const bool need_mask = !(k0 >= wave_lo_max && k0 + BN - 1 <= wave_hi_min);
-    if (need_mask) {
-      // keeps this a real branch: selects would otherwise be speculated onto every tile
-      asm volatile("" ::);
-      const int base = k0 + lane_key - my_lo;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const unsigned rel = (unsigned)(base + kb * 32 + (i >> 2) * 8 + (i & 3));
-          sacc[kb][i] = rel < my_cnt ? sacc[kb][i] : -INFINITY;
-        }
-    }
-    // ---------------- online softmax ----------------
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = max_pair32(mx);
-    const float m_new = fmaxf(m_run, mx * C);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run + kLazyTau) != 0) {
-      const float alpha = exp2_hw(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int d = 0; d < DV / 32; ++d)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
-    }
-    bf16x8 pf[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = exp2_hw(fmaf(sacc[kb][i], C, -m_run));
-        l_run += p;
-        pf[kb * 2 + (i >> 3)][i & 7] = (bf16)p;
-      }
-    }
-
-    // ---------------- O^T += V^T P^T ----------------
-    {
-      const char FA_LDS* vt = sc + T::kTileK;
-      const int grp = lane >> 4, i16 = lane & 15;
-      const int hsel = grp >> 1;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r1 = u * 16 + hsel * 4 + (i16 >> 2);
-        const int r2 = r1 + 8;
-#pragma unroll
-        for (int d = 0; d < DV / 32; ++d) {
-          const int dcol = d * 32 + (grp & 1) * 16 + 4 * (i16 & 3);
-          const int chunk = dcol >> 3, half = (dcol >> 2) & 1;
-          const bf16x4 lo4 = lds_read_tr16(vt + r1 * T::kRowV + ((chunk ^ swz<T::kRowV>(r1)) << 4) + half * 8);
-          const bf16x4 hi4 = lds_read_tr16(vt + r2 * T::kRowV + ((chunk ^ swz<T::kRowV>(r2)) << 4) + half * 8);
-          bf16x8 vf;
-          vf[0] = lo4[0]; vf[1] = lo4[1]; vf[2] = lo4[2]; vf[3] = lo4[3];
-          vf[4] = hi4[0]; vf[5] = hi4[1]; vf[6] = hi4[2]; vf[7] = hi4[3];
-          oacc[d] = mfma32(vf, pf[u], oacc[d]);
         }
       }
     }
 
-    if (has_next) {
-      if (FP8) {
-        k8.store(sn, tid);
-        v8.store(sn + T::kTileK, tid);
-      } else {
-        FA_WAIT_VMCNT(0);
-      }
+    // publish the next tile: FP8 converts its registers into the other
+    // stage; bf16 waits for its own DMA of t1 (t2 may stay in flight)
+    const int s1 = sc + 1 < T::kStages ? sc + 1 : 0;
+    if (FP8) {
+      if (t1 <= t_end) fp8_store(stage_ptr(s1));
+    } else if (t2 <= t_end) {
+      FA_WAIT_VMCNT(kDmaPerTile);
+    } else {
+      FA_WAIT_VMCNT(0);
     }
-    __syncthreads();
-    cur ^= 1;
-    t = tn;
+    sc = s1;
+    t = t1;
+    hb = hb1;
+    if (FP8) {
+      t1 = t1 <= t_end ? next_tile(t1 + 1, hb1) : t_end + 1;
+    } else {
+      t1 = t2;
+      hb1 = hb2;
+      t2 = t2 <= t_end ? next_tile(t2 + 1, hb2) : t_end + 1;
+    }
   }
 
   // ---------------- epilogue ----------------
@@ -510,7 +591,7 @@ void fa_prefill_kernel(const PrefillArgs a) {
 
 template <int DQK, int DV, bool FP8, bool PAGED, int MODS>
 static hipError_t launch_prefill(const PrefillArgs& a, int n_bh, int n_qtiles, hipStream_t stream) {
-  dim3 grid(n_bh, n_qtiles);
+  dim3 grid((n_bh + 7) / 8 * 8, n_qtiles);
   hipLaunchKernelGGL((fa_prefill_kernel<DQK, DV, FP8, PAGED, MODS>), grid, dim3(NTHREADS), 0, stream, a);
   return hipGetLastError();
 }
