@@ -10,6 +10,8 @@ before timing starts.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
                   [--flex alibi|softcap|window|bernoulli|block_causal] [--no-cpu-baseline]
+                  [--copy-calibration]
+  python bench.py --config N --traffic-from FETCH_CSV WRITE_CSV
 
 --config selects another workload for investigation (1 dense D64, 3 paged
 FP8 prefill, 4 paged FP8 decode, 5 flex); the default line is config 2.
@@ -31,6 +33,8 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s + fraction of MFMA peak; paged-decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+COPY_BYTES = 256 << 20        # calibration copy for the HBM byte counters
+DOMINANT = {"prefill": "fa_prefill_kernel", "decode": "fa_decode_kernel"}
 KERNEL_SOURCES = {
     "prefill": ["attention_fa_fwd_03_amd/csrc/fa_prefill.hip", "attention_fa_fwd_03_amd/csrc/fa_device.h",
                 "attention_fa_fwd_03_amd/csrc/fa_kernels.h"],
@@ -61,6 +65,51 @@ def measured_traffic(workload_key: str, kind: str):
     return e["hbm_bytes_per_launch"]
 
 
+def traffic_from_counters(fetch_csv: str, write_csv: str, key: str, kind: str) -> dict:
+    """Turn two rocprofv3 --pmc CSVs (FETCH_SIZE run, WRITE_SIZE run; both
+    with --copy-calibration) into HBM bytes per launch of the dominant kernel
+    and record them in profiles/traffic.json under `key`.
+
+    Each counter is scaled by what it reads for the calibration copy
+    (COPY_BYTES read and COPY_BYTES written by the runtime's copy kernel), so
+    the result does not depend on the counters' unit."""
+    import csv
+
+    def per_dispatch(path, counter):
+        vals, copies = [], []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"])
+                if DOMINANT[kind] in r["Kernel_Name"]:
+                    vals.append(v)
+                elif "rocclr" in r["Kernel_Name"] and "copy" in r["Kernel_Name"].lower():
+                    copies.append(v)
+        if not vals or not copies:
+            raise SystemExit(f"{path}: no {counter} rows for {DOMINANT[kind]} and the calibration copy")
+        return sum(vals) / len(vals), max(copies), len(vals)
+
+    fetch, copy_fetch, n_f = per_dispatch(fetch_csv, "FETCH_SIZE")
+    write, copy_write, n_w = per_dispatch(write_csv, "WRITE_SIZE")
+    sf, sw = COPY_BYTES / copy_fetch, COPY_BYTES / copy_write
+    entry = dict(kernel=DOMINANT[kind], kernel_sha=kernel_sha(kind), dispatches=[n_f, n_w],
+                 fetch_size_per_dispatch=round(fetch, 1), write_size_per_dispatch=round(write, 1),
+                 copy_fetch_size=round(copy_fetch, 1), copy_write_size=round(copy_write, 1),
+                 bytes_per_fetch_unit=round(sf, 3), bytes_per_write_unit=round(sw, 3),
+                 hbm_bytes_per_launch=round(fetch * sf + write * sw))
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    tab = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            tab = json.load(f)
+    tab[key] = entry
+    with open(path, "w") as f:
+        json.dump(tab, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return entry
+
+
 def build_workload(cfg: int, flex: str, torch, synth, fa):
     """Returns (name, run_fn, work dict, oracle sample fn)."""
     dev = "cuda"
@@ -85,15 +134,13 @@ def build_workload(cfg: int, flex: str, torch, synth, fa):
         name = "varlen causal prefill H16 D128 bf16, 8 seqs U[0,4096]"
 
         def sample():
-            import numpy as np
             import oracle
-            qh, kh, vh = (d[x][:, :4].float().cpu().double().numpy() for x in ("q", "k", "v"))
+            qh, kh, vh = (d[x].float().cpu().double().numpy() for x in ("q", "k", "v"))
             cu = d["cu_q"].cpu().numpy()
-            t0 = time.perf_counter()
-            oracle.attention_varlen(qh, kh, vh, cu, cu, dict(causal=True), workers=_cores())
-            dt = time.perf_counter() - t0
-            sflops = sum(4 * L * (L + 1) // 2 * 512 for L in lens)
-            return dict(seconds=dt, flops=sflops, sample="heads 0-3 of all 8 sequences (1/4 of the batch)")
+            dt, reps = _timed_reps(lambda: oracle.attention_varlen(qh, kh, vh, cu, cu, dict(causal=True),
+                                                                   workers=_cores()))
+            return dict(seconds=dt, work=flops * reps,
+                        sample=f"the whole batch (all 8 sequences, all 16 heads), {reps} passes")
         return name, run, dict(flops=flops, kind="prefill", bound="mfma"), \
             {"seqlens": lens, "total_tokens": T, "H": 16, "D": 128, "causal": True}, sample
     if cfg == 3:
@@ -123,8 +170,30 @@ def build_workload(cfg: int, flex: str, torch, synth, fa):
         run = lambda: fa.fa_fwd_paged(d["q"], d["k_cache"], d["v_cache"], o, lse, d["cu_q"], d["seqlen_k"],
                                       d["block_table"], 1, max(lk), d["k_descale"], d["v_descale"], ws, mods)
         name = "paged FP8 decode 64 seqs ctx U[1024,32768] GQA 64/8 Dqk192 Dv128 page64"
+
+        def sample():
+            import oracle
+            n_seq = 8   # the first 8 sequences; only their pages are copied to the host
+            bt = d["block_table"][:n_seq]
+            npg = [math.ceil(x / 64) for x in lk[:n_seq]]
+            ids = torch.cat([bt[b, :npg[b]] for b in range(n_seq)]).long()
+            kc = d["k_cache"].index_select(0, ids).cpu().numpy()
+            vc = d["v_cache"].index_select(0, ids).cpu().numpy()
+            cbt = torch.zeros(n_seq, max(npg), dtype=torch.int64)
+            pos = 0
+            for b in range(n_seq):
+                cbt[b, :npg[b]] = torch.arange(pos, pos + npg[b])
+                pos += npg[b]
+            qh = d["q"][:n_seq].float().cpu().double().numpy()
+            cu = torch.arange(n_seq + 1).numpy()
+            kd, vd = float(d["k_descale"]), float(d["v_descale"])
+            dt, reps = _timed_reps(lambda: oracle.attention_paged(qh, kc, vc, cu, lk[:n_seq], cbt.numpy(),
+                                                                  dict(causal=True), kd, vd, workers=_cores()))
+            sbytes = sum(lk[:n_seq]) * 8 * (192 + 128)
+            return dict(seconds=dt, work=sbytes * reps,
+                        sample=f"sequences 0-{n_seq - 1} ({sum(lk[:n_seq])} cached tokens, all heads), {reps} passes")
         return name, run, dict(flops=flops, bytes=kv_bytes + io_bytes, kind="decode", bound="hbm"), \
-            {"B": 64, "ctx_total": sum(lk), "Hq": 64, "Hkv": 8, "page_size": 64}, None
+            {"B": 64, "ctx_total": sum(lk), "Hq": 64, "Hkv": 8, "page_size": 64}, sample
     if cfg == 5:
         B, H, S, D = 2, 16, 8192, 128
         d = synth.make_dense(B, S, S, H, H, D, D, seed=synth.seed_for(5), device=dev)
@@ -158,6 +227,17 @@ def build_workload(cfg: int, flex: str, torch, synth, fa):
     raise SystemExit(f"unknown config {cfg}")
 
 
+def _timed_reps(fn, min_seconds: float = 10.0, max_reps: int = 30):
+    """Run the oracle sample until it has taken at least min_seconds (a
+    bounded sample of about 10 s of CPU work).  Returns (seconds, passes)."""
+    t0 = time.perf_counter()
+    reps = 0
+    while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
+        fn()
+        reps += 1
+    return time.perf_counter() - t0, reps
+
+
 def _cores() -> int:
     try:
         n = len(os.sched_getaffinity(0))
@@ -176,7 +256,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (reference for HBM byte counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="record HBM bytes per launch from two rocprofv3 --pmc counter CSVs and exit")
     args = ap.parse_args()
+    key = f"config{args.config}" + (f"_{args.flex}" if args.config == 5 else "")
+    if args.traffic_from:
+        kind = "decode" if args.config == 4 else "prefill"
+        print(json.dumps({key: traffic_from_counters(args.traffic_from[0], args.traffic_from[1], key, kind)}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(the path shards by sequence and head; see DESIGN.md)", file=sys.stderr)
@@ -189,10 +276,20 @@ def main():
     torch.cuda.init()
     name, run, work, cfg_extra, sample = build_workload(args.config, args.flex, torch, synth, fa)
     if args.copy_calibration:
-        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        # reference for the HBM byte counters: one device-to-device copy of
+        # COPY_BYTES through the HIP runtime's own copy kernel
+        import ctypes
+        hip = ctypes.CDLL("libamdhip64.so")
+        hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                       ctypes.c_void_p]
+        a = torch.zeros(COPY_BYTES, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
-        b.copy_(a)
         torch.cuda.synchronize()
+        rc = hip.hipMemcpyAsync(b.data_ptr(), a.data_ptr(), COPY_BYTES, 3,
+                                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        if rc != 0:
+            raise SystemExit(f"hipMemcpyAsync failed: {rc}")
         del a, b
 
     for _ in range(args.warmup):
@@ -225,7 +322,6 @@ def main():
         achieved = work["flops"] / per_launch_s / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / PEAK_BF16_TFLOPS, 4))
-    key = f"config{args.config}" + (f"_{args.flex}" if args.config == 5 else "")
     roof["traffic"] = measured_traffic(key, work["kind"])
     roof["kernel_ms"] = round(per_launch_s * 1e3, 4)
 
@@ -234,8 +330,12 @@ def main():
         from threadpoolctl import threadpool_limits
         with threadpool_limits(limits=1):
             r = sample()
-        cpu = dict(value=round(r["flops"] / r["seconds"] / 1e12, 6), unit="TFLOP/s", cores=_cores(),
-                   kind="oracle", sample=r["sample"], seconds=round(r["seconds"], 2))
+        if work["bound"] == "hbm":
+            cval, cunit = r["work"] / r["seconds"] / 1e9, "GB/s"
+        else:
+            cval, cunit = r["work"] / r["seconds"] / 1e12, "TFLOP/s"
+        cpu = dict(value=round(cval, 6), unit=cunit, cores=_cores(), kind="oracle", sample=r["sample"],
+                   seconds=round(r["seconds"], 2))
 
     line = {
         "metric": METRIC,

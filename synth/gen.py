@@ -147,15 +147,14 @@ def make_paged(lengths_q, lengths_k, Hq, Hkv, Dqk, Dv, page_size, seed, device="
     del kf, vf
     k_cache = torch.full((num_pages, Hkv, page_size, Dqk), fill if poison else 0, dtype=cdtype, device=device)
     v_cache = torch.full((num_pages, Hkv, page_size, Dv), fill if poison else 0, dtype=cdtype, device=device)
-    t0 = 0
-    for b in range(B):
-        L = int(lengths_k[b])
-        for p in range(pages_per[b]):
-            a, e = p * page_size, min(L, (p + 1) * page_size)
-            pg = int(block_table[b, p])
-            k_cache[pg, :, : e - a, :] = kq[t0 + a: t0 + e].transpose(0, 1)
-            v_cache[pg, :, : e - a, :] = vq[t0 + a: t0 + e].transpose(0, 1)
-        t0 += L
+    # token t of sequence b, position j: physical page block_table[b, j // ps], slot j % ps
+    if tk:
+        tok_b = torch.repeat_interleave(torch.arange(B), torch.tensor([int(l) for l in lengths_k]))
+        tok_j = torch.cat([torch.arange(int(l)) for l in lengths_k])
+        tok_page = block_table[tok_b, tok_j // page_size].long().to(device)
+        tok_slot = (tok_j % page_size).to(device)
+        k_cache[tok_page, :, tok_slot, :] = kq
+        v_cache[tok_page, :, tok_slot, :] = vq
     small = tk * Hkv * (Dqk + Dv) <= (1 << 26)
     return dict(
         q=q, k_cache=k_cache, v_cache=v_cache,
