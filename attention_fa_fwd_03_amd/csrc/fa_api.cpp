@@ -158,7 +158,7 @@ struct SplitPlan {
 
 SplitPlan plan_splits(int64_t B, int64_t Hkv, int64_t max_sk) {
   SplitPlan p;
-  int64_t target = (max_sk * B * Hkv) / 16384;
+  int64_t target = (max_sk * B * Hkv) / 8192;
   int64_t len = 256;
   while (len < target && len < 2048) len *= 2;
   p.split_len = len;

@@ -9,14 +9,18 @@
 // workspace; the combine kernel merges the partials of a row by their LSE
 // weights (LSE PR: split-K partials are finalised from per-split (m, l)).
 //
-// Per tile:  S^T[32 keys x 32 rows] = K . Q^T with bf16 MFMA; K rows are
-// loaded straight from the cache into registers (two lanes per key row, 16
-// bytes each) and converted exactly from E4M3 to bf16; the contraction runs
-// over head-dim positions in the order d = 32p + 16h + 8u + e (h = lane/32),
-// and the Q fragments are loaded in that same order.  V tiles go to LDS with
-// global_load_lds (no registers, three tiles in flight per wavefront) and are
-// read transposed with ds_read_b64_tr_b8, converted to bf16, and used as the
-// A operand of O^T += V^T P^T.
+// Per tile:  S^T[32 keys x 32 rows] = K . Q^T with bf16 MFMA, then
+// O^T += V^T P^T.  Decode is a streaming read, so the kernel is built to keep
+// many cache bytes in flight: K and V of a tile are loaded straight into
+// registers with 16-byte loads, one tile ahead in two register
+// sets, so every wait is an exact count of ordinary loads.  K rows feed the
+// Q.K^T product from registers (two lanes per key row, converted exactly from
+// E4M3 to bf16); the contraction runs over head-dim positions in the order
+// d = 32p + 16h + 8u + e (h = lane/32).  The V tile is written by the wave
+// into its own LDS tile and read back transposed with ds_read_b64_tr_b8 as
+// the A operand of O^T += V^T P^T.  The Q fragments (same d order) are kept
+// in LDS, each lane reading back its own bytes, which leaves the registers
+// to the loads in flight.
 //
 // Page lookups are bounded to the sequence's own pages and every byte offset
 // is 64-bit, so caches beyond 4 GiB are addressed correctly; keys past
@@ -28,7 +32,6 @@ namespace fa {
 
 constexpr int kDecWaves = 4;
 constexpr int kDecKT = 32;       // keys per tile
-constexpr int kDecStages = 3;    // V tiles in flight per wavefront
 
 // V tile rows are 128 bytes (alternating halves of the 64-bank LDS); the
 // transposed reads take rows {0-3, 8-11} (+4 for lanes 32-63) at 2 chunks per
@@ -56,9 +59,11 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
 void fa_decode_kernel(const DecodeArgs a) {
   static_assert(DQK % 32 == 0 && DV % 128 == 0, "decode tile shapes");
   constexpr int kVTile = kDecKT * DV;            // fp8 bytes per V tile
-  constexpr int kVInstr = kVTile / 1024;
+  constexpr int kVLoads = kVTile / 1024;         // 16-byte V loads per lane per tile
   constexpr int kKLoads = DQK / 32;              // 16-byte K loads per lane per tile
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kDecWaves * kDecStages * kVTile];
+  constexpr int kQBytes = DQK / 16 * 1024;       // Q fragments of one wave, lane-major
+  constexpr int kWaveLds = kQBytes + kVTile;
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kDecWaves * kWaveLds];
 
   // the wavefront index is uniform within a wavefront; readfirstlane lets the
   // compiler keep everything derived from it in scalar registers
@@ -69,7 +74,8 @@ void fa_decode_kernel(const DecodeArgs a) {
   const int g = wi % a.Hkv;
   const int b = (wi / a.Hkv) % a.B;
   const int split = wi / (a.Hkv * a.B);
-  char FA_LDS* vbuf = (char FA_LDS*)(lds_raw) + wave * kDecStages * kVTile;
+  char FA_LDS* qlds = (char FA_LDS*)(lds_raw) + wave * kWaveLds;
+  char FA_LDS* vlds = qlds + kQBytes;
 
   const int skv = (int)min((int64_t)a.seqlen_k[b], (int64_t)a.max_pages << a.page_shift);   // bounded page-table lookups
   const int qs = a.cu_q[b];
@@ -95,19 +101,6 @@ void fa_decode_kernel(const DecodeArgs a) {
   if (a.win_right >= 0) my_hi = min(my_hi, ip + a.win_right);
   if (a.win_left >= 0) my_lo = max(my_lo, ip - a.win_left);
 
-  // Q fragments: step s = 2p + u holds d = 32p + 16*(lane/32) + 8u + e.
-  bf16x8 qf[DQK / 16];
-  {
-    const bf16* qp = a.q + tok * a.q_st + (int64_t)h * a.q_sh + (lane >> 5) * 16;
-#pragma unroll
-    for (int p = 0; p < DQK / 32; ++p) {
-      bf16x8 x0 = *reinterpret_cast<const bf16x8*>(qp + 32 * p);
-      bf16x8 x1 = *reinterpret_cast<const bf16x8*>(qp + 32 * p + 8);
-      if (!rvalid) { x0 = bf16x8{}; x1 = bf16x8{}; }
-      qf[2 * p] = x0;
-      qf[2 * p + 1] = x1;
-    }
-  }
   const float kdesc = *a.k_descale, vdesc = *a.v_descale;
   const float C = a.qk_scale * kLog2e * kdesc;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k);
@@ -115,61 +108,67 @@ void fa_decode_kernel(const DecodeArgs a) {
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
   const int pmask = (1 << a.page_shift) - 1;
 
-  // Pages hold whole 32-key tiles (page_size >= 32, checked by the host):
-  // one wave-uniform scalar lookup per tile.
-  auto page_of = [&](int k0, int) -> int64_t {
-    return min(max(load_uniform_i32(bt, k0 >> a.page_shift), 0), a.num_pages - 1);   // never outside the cache
-  };
-  auto issue_v = [&](int t, int stage) {
-    const int k0 = k_lo + t * kDecKT;
+  // This lane's V pieces: piece n is tile row v_row[n], source chunk
+  // v_chunk[n] (16 bytes), stored at LDS byte n*1024 + 16*lane of the V tile.
+  int v_row[kVLoads], v_chunk[kVLoads];
 #pragma unroll
-    for (int n = 0; n < kVInstr; ++n) {
-      const int byte = n * 1024 + lane * 16;
-      const int rr = byte / DV;
-      const int pos = (byte % DV) >> 4;
-      const int c = pos ^ dec_vswz(rr);
-      int j = k0 + rr;
-      j = j < k_hi ? j : k_hi - 1;
-      const int64_t page = page_of(k0, j);
-      const uint8_t* src = vbase + page * a.v_pg + (int64_t)g * a.v_sh + (int64_t)(j & pmask) * a.v_st + c * 16;
-      global_to_lds16(src, vbuf + stage * kVTile + n * 1024);
+  for (int n = 0; n < kVLoads; ++n) {
+    const int byte = n * 1024 + lane * 16;
+    v_row[n] = byte / DV;
+    v_chunk[n] = ((byte % DV) >> 4) ^ dec_vswz(v_row[n]);
+  }
+
+  // Load tile t's K rows and V pieces into registers.  Pages hold whole
+  // 32-key tiles (page_size >= 32, checked by the host): one wave-uniform
+  // scalar page lookup per tile, clamped to the cache; rows past k_hi re-read
+  // the last key (masked before the softmax).
+  auto load_tile = [&](int t, i32x4 (&kr)[kKLoads], i32x4 (&vr)[kVLoads]) {
+    const int k0 = k_lo + t * kDecKT;
+    const int64_t page = min(max(load_uniform_i32(bt, k0 >> a.page_shift), 0), a.num_pages - 1);
+    const uint8_t* kpage = kbase + page * a.k_pg + (int64_t)g * a.k_sh;
+    const uint8_t* vpage = vbase + page * a.v_pg + (int64_t)g * a.v_sh;
+    const int jk = min(k0 + (lane & 31), k_hi - 1);
+    const uint8_t* krow = kpage + (int64_t)(jk & pmask) * a.k_st + (lane >> 5) * 16;
+#pragma unroll
+    for (int p = 0; p < kKLoads; ++p)
+      kr[p] = *reinterpret_cast<const i32x4*>(krow + 32 * p);
+#pragma unroll
+    for (int n = 0; n < kVLoads; ++n) {
+      const int jv = min(k0 + v_row[n], k_hi - 1);
+      vr[n] = *(
+          reinterpret_cast<const i32x4*>(vpage + (int64_t)(jv & pmask) * a.v_st + v_chunk[n] * 16));
     }
-  };
-  auto load_k = [&](int t, i32x4* kr) {
-    const int k0 = k_lo + t * kDecKT;
-    int j = k0 + (lane & 31);
-    j = j < k_hi ? j : k_hi - 1;
-    const int64_t page = page_of(k0, j);
-    const uint8_t* row = kbase + page * a.k_pg + (int64_t)g * a.k_sh + (int64_t)(j & pmask) * a.k_st + (lane >> 5) * 16;
-#pragma unroll
-    for (int p = 0; p < kKLoads; ++p) kr[p] = *reinterpret_cast<const i32x4*>(row + 32 * p);
   };
 
   const int ntiles = (k_hi - k_lo + kDecKT - 1) / kDecKT;
+  const int last = ntiles - 1;
   f32x16 oacc[DV / 32];
 #pragma unroll
   for (int d = 0; d < DV / 32; ++d) oacc[d] = f32x16{};
   float m_run = kMaxFloor, l_run = 0.0f;
 
-  // Issue order: prologue V0, V1, K0; tile t issues K(t+1) then V(t+2).
-  // Prefetches past the last tile re-read the last tile (clamped index, an
-  // L2 hit) so that every tile issues the same loads and every wait count
-  // is static.  Vector-memory loads complete in issue order; when tile t
-  // needs V(t), only K(t), V(t+1), K(t+1), V(t+2) may still be in flight.
-  static_assert(kDecStages == 3, "the wait counts below assume three V stages");
-  const int last = ntiles - 1;
-  auto body = [&](int t, const i32x4* kc, i32x4* kn) {
-    load_k(min(t + 1, last), kn);
-    issue_v(min(t + 2, last), (t + 2) % kDecStages);
-    // ---- S^T = K Q^T ----
-    f32x16 sacc = f32x16{};
+  // body(t): tile t is in (kc, vc); tile t+1 is in flight in the other set.
+  // After the products have consumed kc and the V pieces are in LDS, tile t+2
+  // is loaded into (kc, vc).  Loads past the last tile re-read the last one.
+  auto body = [&](int t, i32x4 (&kc)[kKLoads], i32x4 (&vc)[kVLoads]) {
+    // ---- S^T = K Q^T ----  (two accumulation chains, summed at the end)
+    f32x16 sacc2[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int p = 0; p < kKLoads; ++p) {
       bf16x8 lo, hi;
       fp8x16_to_bf16(kc[p], lo, hi);
-      sacc = mfma32(lo, qf[2 * p], sacc);
-      sacc = mfma32(hi, qf[2 * p + 1], sacc);
+      const bf16x8 q0 = *reinterpret_cast<const bf16x8 FA_LDS*>(qlds + ((2 * p) * 64 + lane) * 16);
+      const bf16x8 q1 = *reinterpret_cast<const bf16x8 FA_LDS*>(qlds + ((2 * p + 1) * 64 + lane) * 16);
+      sacc2[0] = mfma32(lo, q0, sacc2[0]);
+      sacc2[1] = mfma32(hi, q1, sacc2[1]);
     }
+    f32x16 sacc = sacc2[0] + sacc2[1];
+    // V pieces of tile t into this wave's LDS tile (the transposed reads of
+    // tile t-1 were consumed, hence complete, before this point)
+#pragma unroll
+    for (int n = 0; n < kVLoads; ++n) *reinterpret_cast<i32x4 FA_LDS*>(vlds + n * 1024 + lane * 16) = vc[n];
+    load_tile(min(t + 2, last), kc, vc);
+
     const int k0 = k_lo + t * kDecKT;
     float mx = -INFINITY;
 #pragma unroll
@@ -197,9 +196,7 @@ void fa_decode_kernel(const DecodeArgs a) {
       l_run += p;
       pf[i >> 3][i & 7] = (bf16)p;
     }
-    FA_WAIT_VMCNT(2 * kVInstr + 2 * kKLoads);
     // ---- O^T += V^T P^T ----
-    const char FA_LDS* vt = vbuf + (t % kDecStages) * kVTile;
     const int grp = lane >> 4, i16 = lane & 15;
     const int hsel = grp >> 1;
     const int tt = i16 >> 1, qq = i16 & 1;
@@ -210,23 +207,35 @@ void fa_decode_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int d = 0; d < DV / 32; ++d) {
         const int c = d * 2 + (grp & 1);
-        const i32x2 raw = lds_read_tr8(vt + rr * DV + ((c ^ dec_vswz(rr)) << 4) + qq * 8);
+        const i32x2 raw = lds_read_tr8(vlds + rr * DV + ((c ^ dec_vswz(rr)) << 4) + qq * 8);
         oacc[d] = mfma32(fp8x8_to_bf16(raw), pf[u], oacc[d]);
       }
     }
   };
 
-  i32x4 kA[kKLoads], kB[kKLoads];
-  issue_v(0, 0);
-  issue_v(min(1, last), 1);
-  load_k(0, kA);
+  i32x4 kA[kKLoads], vA[kVLoads], kB[kKLoads], vB[kVLoads];
+  load_tile(0, kA, vA);
+  load_tile(min(1, last), kB, vB);
+  // Q is staged while the first two tiles are in flight
+  // Q fragments: step s = 2p + u holds d = 32p + 16*(lane/32) + 8u + e; lane
+  // l's fragment of step s lives at LDS byte (s*64 + l)*16 of this wave.
+  {
+    const bf16* qp = a.q + tok * a.q_st + (int64_t)h * a.q_sh + (lane >> 5) * 16;
+#pragma unroll
+    for (int p = 0; p < DQK / 32; ++p) {
+      bf16x8 x0 = *reinterpret_cast<const bf16x8*>(qp + 32 * p);
+      bf16x8 x1 = *reinterpret_cast<const bf16x8*>(qp + 32 * p + 8);
+      if (!rvalid) { x0 = bf16x8{}; x1 = bf16x8{}; }
+      *reinterpret_cast<bf16x8 FA_LDS*>(qlds + ((2 * p) * 64 + lane) * 16) = x0;
+      *reinterpret_cast<bf16x8 FA_LDS*>(qlds + ((2 * p + 1) * 64 + lane) * 16) = x1;
+    }
+  }
   int t = 0;
   for (; t + 1 < ntiles; t += 2) {
-    body(t, kA, kB);
-    body(t + 1, kB, kA);
+    body(t, kA, vA);
+    body(t + 1, kB, vB);
   }
-  if (t < ntiles) body(t, kA, kB);
-  FA_WAIT_VMCNT(0);
+  if (t < ntiles) body(t, kA, vA);
 
   // ---- partial epilogue ----
   const float l_tot = sum_pair32(l_run);
