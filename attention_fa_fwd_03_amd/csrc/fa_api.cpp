@@ -32,8 +32,8 @@ int fail(int code, const char* fmt, ...) {
 }
 
 constexpr int64_t kI32 = (int64_t)1 << 31;
-constexpr int kBM = 256;           // prefill query rows per workgroup
-constexpr int kMaskBQ = 128;       // block-mask query tiles: multiples of half a workgroup
+constexpr int kBM = 128;           // prefill query rows per workgroup
+constexpr int kMaskBQ = 128;       // block-mask query tiles: multiples of a workgroup's rows
 constexpr int kBN = 64;            // prefill keys per tile
 constexpr int kDecodeRows = 32;    // decode rows (query x q-head-in-group) per wavefront
 

@@ -88,7 +88,7 @@ __device__ __forceinline__ bf16x8 lds_read_b128(const char FA_LDS* p) {
   return *reinterpret_cast<const bf16x8 FA_LDS*>(p);
 }
 
-__device__ __forceinline__ bf16x4 lds_read_tr16(const char FA_LDS* p) {
+__device__ __forceinline__ bf16x4 lds_read_tr16(const char FA_LDS* __restrict__ p) {
   s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       reinterpret_cast<s16x4 FA_LDS*>(const_cast<char FA_LDS*>(p)));
   return __builtin_bit_cast(bf16x4, v);

@@ -1,10 +1,13 @@
 // Fused attention forward (prefill / dense / varlen / paged) for gfx950.
 //
-// One workgroup = 8 wavefronts = 256 query rows of one (sequence, q-head);
-// each wavefront owns 32 query rows, two wavefronts share each SIMD.  The key
-// axis is walked in tiles of 64 keys staged in LDS (bf16: a ring of three
-// stages, so every tile load has two iterations to land).  Per tile and
-// wavefront:
+// One workgroup = 4 wavefronts = 128 query rows of one (sequence, q-head);
+// each wavefront owns 32 query rows.  A workgroup keeps its LDS ring within
+// 80 KB, so two workgroups share each CU and each SIMD runs one wavefront of
+// each: their barriers are independent, so one workgroup's vector and scalar
+// stretches overlap the other's matrix work.  The key axis is walked in tiles
+// of 64 keys staged in LDS (bf16 at D <= 64: a ring of three stages, two
+// tiles in flight; at D = 128: two stages, the next tile loads while the
+// current one is computed).  Per tile and wavefront:
 //
 //   S^T[64 x 32]  = K_tile . Q^T          v_mfma_f32_32x32x16_bf16, A = K from LDS,
 //                                          B = Q fragments kept in registers
@@ -34,8 +37,8 @@
 // wavefront's range skip the per-score mask.
 //
 // K/V staging: bf16 K/V go global -> LDS with global_load_lds_dwordx4 (no
-// registers), two tiles ahead; FP8 E4M3 K/V are loaded to registers one tile
-// ahead (two LDS stages), converted
+// registers), one or two tiles ahead; FP8 E4M3 K/V are loaded to registers one
+// tile ahead (two LDS stages), converted
 // exactly to bf16 and written to LDS.  LDS rows are 16-byte-chunk XOR
 // swizzled so that both the K reads and the transposed V reads are
 // bank-conflict free.  Whole tiles take a fast addressing path (per-lane
@@ -46,7 +49,7 @@
 
 namespace fa {
 
-constexpr int NWAVES = 8;
+constexpr int NWAVES = 4;
 constexpr int BM = 32 * NWAVES;
 constexpr int BN = 64;
 constexpr int NTHREADS = 64 * NWAVES;
@@ -61,7 +64,8 @@ struct PrefillTraits {
   static constexpr int kTileK = BN * kRowK;
   static constexpr int kTileV = BN * kRowV;
   static constexpr int kStage = kTileK + kTileV;
-  static constexpr int kStages = FP8 ? 2 : 3;     // FP8 tiles wait one iteration in registers
+  // two workgroups per CU: at most 80 KB of LDS each
+  static constexpr int kStages = FP8 ? 2 : ((3 * (BN * DQK * 2 + BN * DV * 2) <= 81920) ? 3 : 2);
   static constexpr int kLds = kStages * kStage;
   static constexpr int kKItems = BN * DQK / 16;    // 16-byte source items per K tile (fp8)
   static constexpr int kVItems = BN * DV / 16;
@@ -408,7 +412,7 @@ void fa_prefill_kernel(const PrefillArgs a) {
     issue(t, stage_ptr(0));
     if (FP8) {
       fp8_store(stage_ptr(0));
-    } else if (t1 <= t_end) {
+    } else if (T::kStages == 3 && t1 <= t_end) {
       issue(t1, stage_ptr(1));
       FA_WAIT_VMCNT(kDmaPerTile);
     } else {
@@ -420,6 +424,8 @@ void fa_prefill_kernel(const PrefillArgs a) {
     __syncthreads();   // tile t visible to all; everyone is done with the stage reused below
     if (FP8) {
       if (t1 <= t_end) issue(t1, nullptr);
+    } else if (T::kStages == 2) {
+      if (t1 <= t_end) issue(t1, stage_ptr(sc ^ 1));
     } else if (t2 <= t_end) {
       const int s2 = sc + 2 < T::kStages ? sc + 2 : sc + 2 - T::kStages;
       issue(t2, stage_ptr(s2));
@@ -544,7 +550,7 @@ void fa_prefill_kernel(const PrefillArgs a) {
     const int s1 = sc + 1 < T::kStages ? sc + 1 : 0;
     if (FP8) {
       if (t1 <= t_end) fp8_store(stage_ptr(s1));
-    } else if (t2 <= t_end) {
+    } else if (T::kStages == 3 && t2 <= t_end) {
       FA_WAIT_VMCNT(kDmaPerTile);
     } else {
       FA_WAIT_VMCNT(0);

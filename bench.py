@@ -9,7 +9,7 @@ online softmax, P.V, epilogue with O and LSE).  Inputs are resident in HBM
 before timing starts.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
-                  [--flex alibi|softcap|window|bernoulli|block_causal] [--no-cpu-baseline]
+                  [--flex alibi|softcap|window|bernoulli|block_causal|none|causal] [--no-cpu-baseline]
                   [--copy-calibration]
   python bench.py --config N --traffic-from FETCH_CSV WRITE_CSV
 
@@ -207,6 +207,10 @@ def build_workload(cfg: int, flex: str, torch, synth, fa):
         elif flex == "window":
             mods, pairs = fa.Mods(window=(256, 0)), sum(min(i, 256) + 1 for i in range(S))
             bound = "hbm"
+        elif flex == "none":
+            mods, pairs = fa.Mods(), S * S
+        elif flex == "causal":
+            mods, pairs = fa.Mods(causal=True), S * (S + 1) // 2
         elif flex == "bernoulli":
             bm = synth.bernoulli_block_mask(B * H, 64, 64, 0.5, seed=synth.seed_for(5, 3)).to(dev)
             mods, pairs = fa.Mods(block_mask=bm), None
