@@ -7,6 +7,7 @@
 // passed by the caller.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
@@ -151,19 +152,13 @@ int check_common(int64_t B, int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v) 
   return FA_OK;
 }
 
-// Decode path geometry: keys are split into chunks of split_len.
-struct SplitPlan {
-  int64_t split_len = 0, n_split = 0;
-};
-
-SplitPlan plan_splits(int64_t B, int64_t Hkv, int64_t max_sk) {
-  SplitPlan p;
-  int64_t target = (max_sk * B * Hkv) / 8192;
-  int64_t len = 256;
-  while (len < target && len < 2048) len *= 2;
-  p.split_len = len;
-  p.n_split = max_sk > 0 ? (max_sk + len - 1) / len : 1;
-  return p;
+// Decode workers: one wavefront each, as many as the chip keeps resident
+// (256 CUs x 4 SIMDs x 3 wavefronts for one 16-row block per wavefront, x 2
+// for two), capped by the tile count so small calls keep small workspaces.
+int64_t decode_workers(int64_t B, int64_t Hkv, int64_t slot_rows, int64_t kv_cap) {
+  const int64_t wmax = slot_rows > 16 ? 2048 : 3072;
+  const int64_t tiles = B * Hkv * ((kv_cap + 31) / 32);
+  return std::max<int64_t>(1, std::min(wmax, tiles));
 }
 
 bool uses_decode(int64_t max_sq, int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v, fa_dtype kv, int64_t page_size) {
@@ -172,12 +167,33 @@ bool uses_decode(int64_t max_sq, int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t 
   return max_sq >= 1 && max_sq * (Hq / Hkv) <= kDecodeRows;
 }
 
+// Workspace of the decode path: the tile prefix ([B+1] int32, padded to 256
+// bytes), then the partial O [slots, slot_rows, d_v] and LSE [slots,
+// slot_rows] in fp32, slots = workers + B * Hkv.
+struct DecodeLayout {
+  int64_t workers = 0, slots = 0, slot_rows = 0, kv_cap = 0;
+  size_t tiles_bytes = 0, o_bytes = 0, total = 0;
+};
+
+DecodeLayout decode_layout(int64_t B, int64_t max_sq, int64_t max_sk, int64_t Hq, int64_t Hkv, int64_t d_v,
+                           int64_t kv_cap) {
+  DecodeLayout L;
+  L.slot_rows = max_sq * (Hq / Hkv);
+  L.kv_cap = std::min(kv_cap, max_sk);
+  L.workers = decode_workers(B, Hkv, L.slot_rows, L.kv_cap);
+  L.slots = L.workers + B * Hkv;
+  L.tiles_bytes = (size_t)((B + 1) * 4 + 255) / 256 * 256;
+  L.o_bytes = (size_t)(L.slots * L.slot_rows * d_v) * sizeof(float);
+  L.total = L.tiles_bytes + L.o_bytes + (size_t)(L.slots * L.slot_rows) * sizeof(float);
+  return L;
+}
+
 size_t workspace_bytes(int64_t B, int64_t total_q, int64_t max_sq, int64_t max_sk, int64_t Hq, int64_t Hkv,
                        int64_t d_qk, int64_t d_v, fa_dtype kv, int64_t page_size) {
-  if (Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0) return 0;
+  (void)total_q;
+  if (B < 0 || max_sq < 0 || max_sk < 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0) return 0;
   if (!uses_decode(max_sq, Hq, Hkv, d_qk, d_v, kv, page_size)) return 0;
-  const SplitPlan p = plan_splits(B, Hkv, max_sk);
-  return (size_t)p.n_split * (size_t)total_q * (size_t)Hq * (size_t)(d_v + 1) * sizeof(float) + 256;
+  return decode_layout(B, max_sq, max_sk, Hq, Hkv, d_v, max_sk).total;
 }
 
 }  // namespace
@@ -336,10 +352,18 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* 
       return fail(FA_ERR_WORKSPACE, "decode path needs a workspace of %zu bytes (got %zu)", need, workspace_bytes_in);
     if (overlaps(workspace, need, o, no) || overlaps(workspace, need, lse, nl) || overlaps(workspace, need, q, nq))
       return fail(FA_ERR_INVALID, "workspace must not overlap q, o or lse");
-    const SplitPlan p = plan_splits(B, Hkv, max_seqlen_k);
-    if (p.n_split * B * Hkv >= kI32) return fail(FA_ERR_LIMIT, "decode work count exceeds 2^31");
-    float* part_o = (float*)workspace;
-    float* part_lse = part_o + (size_t)p.n_split * total_q * Hq * d_v;
+    if (B * Hkv * ((max_seqlen_k + 31) / 32) >= kI32) return fail(FA_ERR_LIMIT, "decode tile count exceeds 2^31");
+    const DecodeLayout L = decode_layout(B, max_seqlen_q, max_seqlen_k, Hq, Hkv, d_v,
+                                         std::min<int64_t>(max_pages_per_seq * page_size, kI32 - 1));
+    int32_t* tiles = (int32_t*)workspace;
+    float* part_o = (float*)((char*)workspace + L.tiles_bytes);
+    float* part_lse = (float*)((char*)part_o + L.o_bytes);
+    fa::DecodePlanArgs pl{};
+    pl.cu_q = cu_seqlens_q;
+    pl.seqlen_k = seqlen_k;
+    pl.tiles = tiles;
+    pl.B = (int)B;
+    pl.kv_cap = (int)L.kv_cap;
     fa::DecodeArgs d{};
     d.q = (const __bf16*)q;
     d.k = k_cache;
@@ -351,22 +375,23 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* 
     d.block_table = block_table;
     d.k_descale = k_descale;
     d.v_descale = v_descale;
+    d.tiles = tiles;
     d.q_st = Hq * d_qk; d.q_sh = d_qk;
     d.k_st = d_qk; d.k_sh = page_size * d_qk; d.k_pg = Hkv * page_size * d_qk;
     d.v_st = d_v; d.v_sh = page_size * d_v; d.v_pg = Hkv * page_size * d_v;
-    d.total_q = total_q;
     d.B = (int)B; d.Hq = (int)Hq; d.Hkv = (int)Hkv; d.group = (int)(Hq / Hkv);
     d.max_pages = (int)max_pages_per_seq;
     d.page_shift = shift;
+    d.kv_cap = (int)L.kv_cap;
     d.num_pages = (int)num_pages;
-    d.n_split = (int)p.n_split;
-    d.split_len = (int)p.split_len;
+    d.n_workers = (int)L.workers;
+    d.slot_rows = (int)L.slot_rows;
     d.qk_scale = m.scale;
     d.causal = (m.flags & FA_CAUSAL) ? 1 : 0;
     d.win_left = (m.flags & FA_WINDOW) ? clamp_i32(m.wl) : -1;
     d.win_right = (m.flags & FA_WINDOW) ? clamp_i32(m.wr) : -1;
     bool supported = false;
-    hipError_t e = fa::decode_dispatch(d, (int)d_qk, (int)d_v, fp8, st, &supported);
+    hipError_t e = fa::decode_dispatch(pl, d, (int)d_qk, (int)d_v, fp8, st, &supported);
     if (!supported) return fail(FA_ERR_UNSUPPORTED, "no decode kernel for (%lld, %lld)", (long long)d_qk, (long long)d_v);
     if (e != hipSuccess) return fail(FA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
     fa::CombineArgs c{};
@@ -374,10 +399,13 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* 
     c.part_lse = part_lse;
     c.o = (__bf16*)o;
     c.lse = lse;
+    c.cu_q = cu_seqlens_q;
+    c.tiles = tiles;
     c.o_st = Hq * d_v; c.o_sh = d_v;
     c.total_q = total_q;
-    c.Hq = (int)Hq;
-    c.n_split = (int)p.n_split;
+    c.B = (int)B; c.Hq = (int)Hq; c.Hkv = (int)Hkv; c.group = (int)(Hq / Hkv);
+    c.n_workers = (int)L.workers;
+    c.slot_rows = (int)L.slot_rows;
     e = fa::combine_dispatch(c, (int)d_v, st, &supported);
     if (!supported) return fail(FA_ERR_UNSUPPORTED, "no combine kernel for d_v=%lld", (long long)d_v);
     if (e != hipSuccess) return fail(FA_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));

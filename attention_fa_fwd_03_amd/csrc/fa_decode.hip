@@ -2,25 +2,48 @@
 //
 // Decode is bound by HBM bandwidth: every cache byte is read once, and the
 // q-heads that share a kv-head (GQA) are packed into the rows of one matrix
-// product so that they share that read.  Each wavefront is an independent
-// worker for one (split, sequence, kv-head): it walks keys [split*L,
-// (split+1)*L) in tiles of 32 keys and writes a partial result
-// (O normalised by its own denominator, and its natural-log LSE) to the
-// workspace; the combine kernel merges the partials of a row by their LSE
-// weights (LSE PR: split-K partials are finalised from per-split (m, l)).
+// product so that they share that read.
 //
-// Per tile:  S^T[32 keys x 32 rows] = K . Q^T with bf16 MFMA, then
-// O^T += V^T P^T.  Decode is a streaming read, so the kernel is built to keep
-// many cache bytes in flight: K and V of a tile are loaded straight into
-// registers with 16-byte loads, one tile ahead in two register
-// sets, so every wait is an exact count of ordinary loads.  K rows feed the
-// Q.K^T product from registers (two lanes per key row, converted exactly from
-// E4M3 to bf16); the contraction runs over head-dim positions in the order
-// d = 32p + 16h + 8u + e (h = lane/32).  The V tile is written by the wave
-// into its own LDS tile and read back transposed with ds_read_b64_tr_b8 as
-// the A operand of O^T += V^T P^T.  The Q fragments (same d order) are kept
-// in LDS, each lane reading back its own bytes, which leaves the registers
-// to the loads in flight.
+// Work split (stream-K style): the 32-key tiles of all units (sequence,
+// kv-head) are laid end to end, and wavefront w of W takes tiles
+// [w T / W, (w+1) T / W) of the T in total, so every wavefront streams the
+// same number of cache bytes whatever the mix of context lengths.  A share
+// may start or end inside a unit and may cover several short units; for each
+// unit segment the wavefront writes a partial result (O normalised by its own
+// denominator, and its natural-log LSE) to slot w + unit of the workspace.
+// A unit's segments come from consecutive workers, so the combine kernel finds
+// them from the unit's first and last tile and merges them by their LSE
+// weights (LSE PR: split-K partials are finalised from per-split (m, l)).
+// A one-workgroup plan kernel turns the per-sequence key counts into the
+// tile prefix both kernels read, so the split needs no host round trip.
+//
+// Rows (query x q-head of the group, up to 16 per row block) are the N side
+// of v_mfma_f32_16x16x32_bf16 products; one or two row blocks per wavefront:
+//
+//   S^T[32 keys x 16 rows] = K . Q^T     v_mfma_f32_16x16x32_fp8_fp8: A = the
+//                                          E4M3 K bytes from LDS, B = Q as two
+//                                          E4M3 parts (below), two products
+//   O^T[Dv x 16 rows]    += V^T . P^T    bf16 MFMA: A = V read transposed from
+//                                          LDS (ds_read_b64_tr_b8) and converted
+//                                          exactly, B = P in bf16
+//
+// The K bytes enter the FP8 product as they are (no conversion instructions,
+// the dominant vector cost of the loop otherwise).  Q (bf16) is scaled by 16
+// (exact) and written as hi + lo with hi = E4M3(16 q), lo = E4M3(16 q - hi):
+// the two 3-bit mantissas carry q to about 2^-8 relative, and the scaled
+// values stay clear of the E4M3 subnormal range; the 1/16 is folded into the
+// logit constant.  Each product is exact (3-bit x 3-bit mantissas) and
+// accumulated in fp32, so the logits differ from the bf16-Q logits only by
+// the split's rounding (about 1e-3 in natural-log units at the largest
+// logits of N(0,1) data).
+//
+// The cache streams through registers with coalesced 16-byte loads (lane l
+// of load i takes bytes [1024 i + 16 l, +16) of the tile, so every load
+// instruction covers whole cache lines), one tile ahead; the wavefront then
+// writes the tile into its own LDS buffer (16-byte chunks of K and V rows
+// XOR-swizzled) and reads the matrix fragments back.  The wavefronts are
+// independent (no barrier), and small register and LDS footprints let twelve
+// of them share a CU, so plenty of cache lines are in flight.
 //
 // Page lookups are bounded to the sequence's own pages and every byte offset
 // is 64-bit, so caches beyond 4 GiB are addressed correctly; keys past
@@ -33,13 +56,20 @@ namespace fa {
 constexpr int kDecWaves = 4;
 constexpr int kDecKT = 32;       // keys per tile
 
-// V tile rows are 128 bytes (alternating halves of the 64-bank LDS); the
-// transposed reads take rows {0-3, 8-11} (+4 for lanes 32-63) at 2 chunks per
-// 32 lanes.  Spreading rows {0, 2, 8, 10} over even chunk offsets makes the
-// 32 accesses hit distinct banks.
-__device__ __forceinline__ int dec_vswz(int r) { return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)); }
+// V tile rows are 128 bytes = 8 chunks of 16; chunk c of row r is stored at
+// c ^ dec_vswz(r).  A transposed read instruction takes, per group of 16
+// lanes g, rows {4g..4g+3, 16+4g..16+4g+3} at one chunk (two 8-byte halves):
+// with this map the even rows of lanes 0-31 (and of lanes 32-63), and the odd
+// rows, each cover all eight chunks, i.e. the 64 banks exactly once.
+__device__ __forceinline__ int dec_vswz(int r) { return ((r >> 1) & 3) | (((r >> 4) & 1) << 2); }
 
-__device__ __forceinline__ i32x2 lds_read_tr8(const char FA_LDS* p) {
+// K tile rows are D_qk bytes (48 banks at 192); chunk c of row r is stored at
+// c ^ dec_kswz(r), which stays inside the aligned group of four chunks.  A
+// K fragment read takes 8 bytes of rows r..r+15 at one chunk: rows four apart
+// start on the same bank and the map moves them to different chunks.
+__device__ __forceinline__ int dec_kswz(int r) { return (r >> 2) & 3; }
+
+__device__ __forceinline__ i32x2 lds_read_tr8(const char FA_LDS* __restrict__ p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 FA_LDS*)(p));
 }
 
@@ -54,240 +84,438 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(i32x2 w) {
   return r;
 }
 
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16_fp8(i32x2 a, i32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(__builtin_bit_cast(long, a), __builtin_bit_cast(long, b), c, 0, 0,
+                                                    0);
+}
+
+// Eight bf16 values x -> E4M3 parts (hi, lo) of 16 x, with 16 x ~= hi + lo.
+__device__ __forceinline__ void split_e4m3(bf16x8 x, i32x2& hi, i32x2& lo) {
+  float f[8], r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = 16.0f * (float)x[e];
+  int h0 = 0, h1 = 0, l0 = 0, l1 = 0;
+  h0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], h0, false);
+  h0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], h0, true);
+  h1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], h1, false);
+  h1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], h1, true);
+  r[0] = f[0] - __builtin_amdgcn_cvt_f32_fp8(h0, 0);
+  r[1] = f[1] - __builtin_amdgcn_cvt_f32_fp8(h0, 1);
+  r[2] = f[2] - __builtin_amdgcn_cvt_f32_fp8(h0, 2);
+  r[3] = f[3] - __builtin_amdgcn_cvt_f32_fp8(h0, 3);
+  r[4] = f[4] - __builtin_amdgcn_cvt_f32_fp8(h1, 0);
+  r[5] = f[5] - __builtin_amdgcn_cvt_f32_fp8(h1, 1);
+  r[6] = f[6] - __builtin_amdgcn_cvt_f32_fp8(h1, 2);
+  r[7] = f[7] - __builtin_amdgcn_cvt_f32_fp8(h1, 3);
+  l0 = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], l0, false);
+  l0 = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], l0, true);
+  l1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[4], r[5], l1, false);
+  l1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[6], r[7], l1, true);
+  hi = i32x2{h0, h1};
+  lo = i32x2{l0, l1};
+}
+
+// max / sum over the four lanes {l, l^16, l^32, l^48} (the four key groups
+// that hold one row's scores)
+__device__ __forceinline__ float max_quad16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_pair32(x);
+}
+__device__ __forceinline__ float sum_quad16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  return sum_pair32(x);
+}
+
 template <int DQK, int DV>
-__global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+struct DecTraits {
+  static constexpr int kKTile = kDecKT * DQK;
+  static constexpr int kVTile = kDecKT * DV;
+  static constexpr int kWaveLds = kKTile + kVTile;
+  static constexpr int kKLoads = kDecKT * DQK / 1024;   // 16-byte loads per lane per tile
+  static constexpr int kVLoads = kDecKT * DV / 1024;
+};
+
+// Tiles per sequence, as an exclusive prefix: tiles[b] = sum over b' < b of
+// ceil(keys_b' / 32) (0 for sequences with no query; keys capped at kv_cap), tiles[B] the total.
+// One workgroup of 256 threads: each thread sums a contiguous run of
+// sequences, thread 0 scans the 256 partial sums, each thread writes its run.
+__global__ __launch_bounds__(256) void fa_decode_plan_kernel(const DecodePlanArgs a) {
+  __shared__ int part[257];
+  const int tid = threadIdx.x;
+  const int per = (a.B + 255) / 256;
+  const int b0 = min(a.B, tid * per), b1 = min(a.B, b0 + per);
+  auto nt = [&](int b) {
+    if (a.cu_q[b + 1] - a.cu_q[b] <= 0) return 0;
+    const int kv = min(a.seqlen_k[b], a.kv_cap);
+    return kv > 0 ? (kv + kDecKT - 1) / kDecKT : 0;
+  };
+  int sum = 0;
+  for (int b = b0; b < b1; ++b) sum += nt(b);
+  part[tid] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int x = part[i];
+      part[i] = run;
+      run += x;
+    }
+    part[256] = run;
+  }
+  __syncthreads();
+  int run = part[tid];
+  for (int b = b0; b < b1; ++b) {
+    a.tiles[b] = run;
+    run += nt(b);
+  }
+  if (tid == 0) a.tiles[a.B] = part[256];
+}
+
+// worker that owns tile i of T in a split over W workers
+__device__ __forceinline__ int worker_of(int64_t i, int64_t T, int W) { return (int)(((i + 1) * W - 1) / T); }
+
+template <int DQK, int DV, int NRB>
+__global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(NRB == 1 ? 3 : 2)))
 void fa_decode_kernel(const DecodeArgs a) {
-  static_assert(DQK % 32 == 0 && DV % 128 == 0, "decode tile shapes");
-  constexpr int kVTile = kDecKT * DV;            // fp8 bytes per V tile
-  constexpr int kVLoads = kVTile / 1024;         // 16-byte V loads per lane per tile
-  constexpr int kKLoads = DQK / 32;              // 16-byte K loads per lane per tile
-  constexpr int kQBytes = DQK / 16 * 1024;       // Q fragments of one wave, lane-major
-  constexpr int kWaveLds = kQBytes + kVTile;
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kDecWaves * kWaveLds];
+  static_assert(DQK % 32 == 0 && DV == 128 && (kDecKT * DQK) % 1024 == 0, "decode tile shapes");
+  using T = DecTraits<DQK, DV>;
+  constexpr int kSteps = DQK / 32;                      // K.Q^T MFMA steps per 16-key half
+  constexpr int kDB = DV / 16;                          // 16-wide blocks of the output
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kDecWaves * T::kWaveLds];
 
   // the wavefront index is uniform within a wavefront; readfirstlane lets the
   // compiler keep everything derived from it in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int wi = blockIdx.x * kDecWaves + wave;
-  const int units = a.n_split * a.B * a.Hkv;
-  if (wi >= units) return;
-  const int g = wi % a.Hkv;
-  const int b = (wi / a.Hkv) % a.B;
-  const int split = wi / (a.Hkv * a.B);
-  char FA_LDS* qlds = (char FA_LDS*)(lds_raw) + wave * kWaveLds;
-  char FA_LDS* vlds = qlds + kQBytes;
+  const int w = blockIdx.x * kDecWaves + wave;
+  if (w >= a.n_workers) return;
+  // this worker's share [s0, s1) of the T tiles of all units
+  const int64_t ntot = (int64_t)a.Hkv * load_uniform_i32(a.tiles, a.B);
+  const int64_t s0 = (int64_t)w * ntot / a.n_workers, s1 = (int64_t)(w + 1) * ntot / a.n_workers;
+  if (s0 >= s1) return;
+  char FA_LDS* klds = (char FA_LDS*)(lds_raw) + wave * T::kWaveLds;
+  char FA_LDS* vlds = klds + T::kKTile;
+  const int kgrp = lane >> 4;                           // key group of this lane's scores
 
-  const int skv = (int)min((int64_t)a.seqlen_k[b], (int64_t)a.max_pages << a.page_shift);   // bounded page-table lookups
-  const int qs = a.cu_q[b];
-  const int sq = a.cu_q[b + 1] - qs;
-  const int R = sq * a.group;
-  if (R <= 0) return;
-  const int r = lane & 31;
-  const bool rvalid = r < R;
-  const int qi = rvalid ? r / a.group : 0;
-  const int h = g * a.group + (rvalid ? r % a.group : 0);
-  const int64_t tok = qs + qi;
-  const int k_lo = split * a.split_len;
-  const int k_hi = min(skv, k_lo + a.split_len);
-  if (k_lo >= k_hi) {
-    if (lane < 32 && rvalid) a.part_lse[((int64_t)split * a.total_q + tok) * a.Hq + h] = -INFINITY;
-    return;
+  // LDS byte of this lane's piece of each tile load (swizzled chunk)
+  int kst[T::kKLoads], vst[T::kVLoads];
+#pragma unroll
+  for (int i = 0; i < T::kKLoads; ++i) {
+    const int off = i * 1024 + lane * 16, row = off / DQK;
+    kst[i] = row * DQK + ((((off % DQK) >> 4) ^ dec_kswz(row)) << 4);
   }
-
-  const int delta = skv - sq;
-  const int ip = qi + delta;
-  int my_hi = k_hi - 1, my_lo = k_lo;
-  if (a.causal) my_hi = min(my_hi, ip);
-  if (a.win_right >= 0) my_hi = min(my_hi, ip + a.win_right);
-  if (a.win_left >= 0) my_lo = max(my_lo, ip - a.win_left);
-
+#pragma unroll
+  for (int n = 0; n < T::kVLoads; ++n) {
+    const int off = n * 1024 + lane * 16, row = off / DV;
+    vst[n] = row * DV + ((((off % DV) >> 4) ^ dec_vswz(row)) << 4);
+  }
+  // transposed V reads: lanes 2t+q of key group kgrp take row vrow(t), half q
+  const int t8 = (lane & 15) >> 1, vq = lane & 1;
+  const int vrow = t8 < 4 ? 4 * kgrp + t8 : 16 + 4 * kgrp + (t8 - 4);
+  const char FA_LDS* vrd = vlds + vrow * DV + vq * 8;
+  const int vsw = dec_vswz(vrow);
+  // K fragment reads: row kh*16 + lane%16 (the swizzle of r and r+16 agree),
+  // chunk 2 st + kgrp/2, half kgrp%2
+  const int krow = lane & 15, kx = dec_kswz(krow);
+  const char FA_LDS* krd = klds + krow * DQK + (kgrp & 1) * 8;
   const float kdesc = *a.k_descale, vdesc = *a.v_descale;
-  const float C = a.qk_scale * kLog2e * kdesc;
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k);
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v);
-  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+  const float C = a.qk_scale * kLog2e * kdesc * (1.0f / 16.0f);   // Q enters scaled by 16
   const int pmask = (1 << a.page_shift) - 1;
 
-  // This lane's V pieces: piece n is tile row v_row[n], source chunk
-  // v_chunk[n] (16 bytes), stored at LDS byte n*1024 + 16*lane of the V tile.
-  int v_row[kVLoads], v_chunk[kVLoads];
-#pragma unroll
-  for (int n = 0; n < kVLoads; ++n) {
-    const int byte = n * 1024 + lane * 16;
-    v_row[n] = byte / DV;
-    v_chunk[n] = ((byte % DV) >> 4) ^ dec_vswz(v_row[n]);
-  }
+  // One unit segment: sequence b, kv-head g, tiles [t0, t1) -> partial slot.
+  auto segment = [&](int b, int g, int t0, int t1, int64_t slot) {
+    const int skv = min(a.seqlen_k[b], a.kv_cap);       // bounds the page-table lookups
+    const int qs = a.cu_q[b];
+    const int sq = a.cu_q[b + 1] - qs;
+    const int R = sq * a.group;
+    const int k_lo = t0 * kDecKT;
+    const int k_hi = min(skv, t1 * kDecKT);
+    const int delta = skv - sq;
 
-  // Load tile t's K rows and V pieces into registers.  Pages hold whole
-  // 32-key tiles (page_size >= 32, checked by the host): one wave-uniform
-  // scalar page lookup per tile, clamped to the cache; rows past k_hi re-read
-  // the last key (masked before the softmax).
-  auto load_tile = [&](int t, i32x4 (&kr)[kKLoads], i32x4 (&vr)[kVLoads]) {
-    const int k0 = k_lo + t * kDecKT;
-    const int64_t page = min(max(load_uniform_i32(bt, k0 >> a.page_shift), 0), a.num_pages - 1);
-    const uint8_t* kpage = kbase + page * a.k_pg + (int64_t)g * a.k_sh;
-    const uint8_t* vpage = vbase + page * a.v_pg + (int64_t)g * a.v_sh;
-    const int jk = min(k0 + (lane & 31), k_hi - 1);
-    const uint8_t* krow = kpage + (int64_t)(jk & pmask) * a.k_st + (lane >> 5) * 16;
+    // rows of this lane: row block rb holds rows rb*16 + lane%16
+    bool rvalid[NRB];
+    int hq[NRB], my_lo[NRB], my_hi[NRB];
+    int64_t tok[NRB];
 #pragma unroll
-    for (int p = 0; p < kKLoads; ++p)
-      kr[p] = *reinterpret_cast<const i32x4*>(krow + 32 * p);
-#pragma unroll
-    for (int n = 0; n < kVLoads; ++n) {
-      const int jv = min(k0 + v_row[n], k_hi - 1);
-      vr[n] = *(
-          reinterpret_cast<const i32x4*>(vpage + (int64_t)(jv & pmask) * a.v_st + v_chunk[n] * 16));
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int r = rb * 16 + (lane & 15);
+      rvalid[rb] = r < R;
+      const int qi = rvalid[rb] ? r / a.group : 0;
+      hq[rb] = g * a.group + (rvalid[rb] ? r % a.group : 0);
+      tok[rb] = qs + qi;
+      const int ip = qi + delta;
+      int hi = k_hi - 1, lo = k_lo;
+      if (a.causal) hi = min(hi, ip);
+      if (a.win_right >= 0) hi = min(hi, ip + a.win_right);
+      if (a.win_left >= 0) lo = max(lo, ip - a.win_left);
+      my_lo[rb] = lo;
+      my_hi[rb] = hi;
     }
-  };
+    // keys every row of this unit sees: tiles inside [all_lo, all_hi] skip
+    // the per-score mask
+    int all_hi = k_hi - 1, all_lo = k_lo;
+    if (a.causal) all_hi = min(all_hi, delta);
+    if (a.win_right >= 0) all_hi = min(all_hi, delta + a.win_right);
+    if (a.win_left >= 0) all_lo = max(all_lo, (sq - 1) + delta - a.win_left);
 
-  const int ntiles = (k_hi - k_lo + kDecKT - 1) / kDecKT;
-  const int last = ntiles - 1;
-  f32x16 oacc[DV / 32];
-#pragma unroll
-  for (int d = 0; d < DV / 32; ++d) oacc[d] = f32x16{};
-  float m_run = kMaxFloor, l_run = 0.0f;
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + (int64_t)g * a.k_sh;
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v) + (int64_t)g * a.v_sh;
+    const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+    const int last = t1 - t0 - 1;
 
-  // body(t): tile t is in (kc, vc); tile t+1 is in flight in the other set.
-  // After the products have consumed kc and the V pieces are in LDS, tile t+2
-  // is loaded into (kc, vc).  Loads past the last tile re-read the last one.
-  auto body = [&](int t, i32x4 (&kc)[kKLoads], i32x4 (&vc)[kVLoads]) {
-    // ---- S^T = K Q^T ----  (two accumulation chains, summed at the end)
-    f32x16 sacc2[2] = {f32x16{}, f32x16{}};
+    // Coalesced tile loads: load i of this lane covers bytes [1024 i + 16
+    // lane, +16) of the tile.  Page rows are contiguous (row stride = head
+    // dim), so a whole tile is one block of the page; pages hold whole
+    // 32-key tiles (page_size >= 32, checked by the host): one wave-uniform
+    // scalar page lookup per tile, clamped to the cache.  In the sequence's
+    // last, partial tile the rows past the end re-read the last key (masked
+    // before the softmax), so no stale bytes reach the products.
+    i32x4 kbuf[T::kKLoads], vbuf[T::kVLoads];
+    auto load_tile = [&](int t) {
+      const int k0 = k_lo + t * kDecKT;
+      const int64_t page = min(max(load_uniform_i32(bt, k0 >> a.page_shift), 0), a.num_pages - 1);
+      const int nv = skv - k0;                          // rows of the tile inside the sequence
+      const uint8_t* kt = kbase + page * a.k_pg + (int64_t)(k0 & pmask) * DQK;
+      const uint8_t* vt = vbase + page * a.v_pg + (int64_t)(k0 & pmask) * DV;
+      if (nv >= kDecKT) {
 #pragma unroll
-    for (int p = 0; p < kKLoads; ++p) {
-      bf16x8 lo, hi;
-      fp8x16_to_bf16(kc[p], lo, hi);
-      const bf16x8 q0 = *reinterpret_cast<const bf16x8 FA_LDS*>(qlds + ((2 * p) * 64 + lane) * 16);
-      const bf16x8 q1 = *reinterpret_cast<const bf16x8 FA_LDS*>(qlds + ((2 * p + 1) * 64 + lane) * 16);
-      sacc2[0] = mfma32(lo, q0, sacc2[0]);
-      sacc2[1] = mfma32(hi, q1, sacc2[1]);
-    }
-    f32x16 sacc = sacc2[0] + sacc2[1];
-    // V pieces of tile t into this wave's LDS tile (the transposed reads of
-    // tile t-1 were consumed, hence complete, before this point)
+        for (int i = 0; i < T::kKLoads; ++i) kbuf[i] = *reinterpret_cast<const i32x4*>(kt + i * 1024 + lane * 16);
 #pragma unroll
-    for (int n = 0; n < kVLoads; ++n) *reinterpret_cast<i32x4 FA_LDS*>(vlds + n * 1024 + lane * 16) = vc[n];
-    load_tile(min(t + 2, last), kc, vc);
+        for (int n = 0; n < T::kVLoads; ++n) vbuf[n] = *reinterpret_cast<const i32x4*>(vt + n * 1024 + lane * 16);
+      } else {
+#pragma unroll
+        for (int i = 0; i < T::kKLoads; ++i) {
+          const int off = i * 1024 + lane * 16, row = off / DQK;
+          kbuf[i] = *reinterpret_cast<const i32x4*>(kt + min(row, nv - 1) * DQK + off % DQK);
+        }
+#pragma unroll
+        for (int n = 0; n < T::kVLoads; ++n) {
+          const int off = n * 1024 + lane * 16, row = off / DV;
+          vbuf[n] = *reinterpret_cast<const i32x4*>(vt + min(row, nv - 1) * DV + off % DV);
+        }
+      }
+    };
 
-    const int k0 = k_lo + t * kDecKT;
-    float mx = -INFINITY;
+    // Q fragments (B operand): step s of row block rb holds the E4M3 parts
+    // of 16 Q[row rb*16 + lane%16][d = 32 s + 8 (lane/16) + e]; read before
+    // the first tile is requested, so waiting for them never waits for the
+    // cache loads
+    i32x2 qhi[NRB][kSteps], qlo[NRB][kSteps];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int j = k0 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-      const float val = (j >= my_lo && j <= my_hi) ? sacc[i] : -INFINITY;
-      sacc[i] = val;
-      mx = fmaxf(mx, val);
+    for (int rb = 0; rb < NRB; ++rb) {
+      const bf16* qp = a.q + tok[rb] * a.q_st + (int64_t)hq[rb] * a.q_sh + kgrp * 8;
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st) {
+        bf16x8 x = *reinterpret_cast<const bf16x8*>(qp + 32 * st);
+        if (!rvalid[rb]) x = bf16x8{};
+        split_e4m3(x, qhi[rb][st], qlo[rb][st]);
+      }
     }
-    mx = max_pair32(mx);
-    const float m_new = fmaxf(m_run, mx * C);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run + 8.0f) != 0) {
-      const float alpha = exp2_hw(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+    load_tile(0);
+
+    f32x4 oacc[NRB][kDB];
 #pragma unroll
-      for (int d = 0; d < DV / 32; ++d)
+    for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+      for (int d = 0; d < kDB; ++d) oacc[rb][d] = f32x4{};
+    float m_run[NRB], l_run[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      m_run[rb] = kMaxFloor;
+      l_run[rb] = 0.0f;
     }
-    bf16x8 pf[2];
+
+    for (int t = 0; t <= last; ++t) {
+      // tile t: registers -> this wavefront's LDS buffer (the fragment reads
+      // of tile t-1 were consumed, hence complete, before this point)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = exp2_hw(fmaf(sacc[i], C, -m_run));
-      l_run += p;
-      pf[i >> 3][i & 7] = (bf16)p;
+      for (int i = 0; i < T::kKLoads; ++i) *reinterpret_cast<i32x4 FA_LDS*>(klds + kst[i]) = kbuf[i];
+#pragma unroll
+      for (int n = 0; n < T::kVLoads; ++n) *reinterpret_cast<i32x4 FA_LDS*>(vlds + vst[n]) = vbuf[n];
+      if (t < last) load_tile(t + 1);
+
+      // ---- S^T = K Q^T ----  (fragment n = (kh, st); each read runs two
+      // fragments ahead of its products, one chunk per fragment)
+      constexpr int kNK = 2 * kSteps;
+      auto kread = [&](int n) {
+        const int kh = n / kSteps, st = n % kSteps;
+        const int c = (2 * st + (kgrp >> 1)) ^ kx;
+        return *reinterpret_cast<const i32x2 FA_LDS*>(krd + kh * 16 * DQK + c * 16);
+      };
+      f32x4 sacc[NRB][2];
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) sacc[rb][0] = sacc[rb][1] = f32x4{};
+      i32x2 kraw[kNK];
+      kraw[0] = kread(0);
+      kraw[1] = kread(1);
+#pragma unroll
+      for (int n = 0; n < kNK; ++n) {
+        if (n + 2 < kNK) kraw[n + 2] = kread(n + 2);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          sacc[rb][n / kSteps] = mfma16_fp8(kraw[n], qhi[rb][n % kSteps], sacc[rb][n / kSteps]);
+          sacc[rb][n / kSteps] = mfma16_fp8(kraw[n], qlo[rb][n % kSteps], sacc[rb][n / kSteps]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // ---- masks and online softmax, per row block ----
+      const int k0 = k_lo + t * kDecKT;
+      bf16x8 pf[NRB];
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        if (k0 < all_lo || k0 + kDecKT - 1 > all_hi) {
+          // keeps this a real branch: selects would otherwise be speculated onto every tile
+          asm volatile("" ::);
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int j = k0 + kh * 16 + 4 * kgrp + i;
+              sacc[rb][kh][i] = (j >= my_lo[rb] && j <= my_hi[rb]) ? sacc[rb][kh][i] : -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[rb][kh][i]);
+        mx = max_quad16(mx);
+        const float m_new = fmaxf(m_run[rb], mx * C);
+        if (__builtin_amdgcn_ballot_w64(m_new > m_run[rb] + 8.0f) != 0) {
+          const float alpha = exp2_hw(m_run[rb] - m_new);
+          m_run[rb] = m_new;
+          l_run[rb] *= alpha;
+#pragma unroll
+          for (int d = 0; d < kDB; ++d) oacc[rb][d] *= alpha;
+        }
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = exp2_hw(fmaf(sacc[rb][kh][i], C, -m_run[rb]));
+            l_run[rb] += p;
+            pf[rb][kh * 4 + i] = (bf16)p;
+          }
+      }
+
+      // ---- O^T += V^T P^T ----  (same two-ahead chunking)
+      i32x2 vraw[kDB];
+      vraw[0] = lds_read_tr8(vrd + ((0 ^ vsw) << 4));
+      vraw[1] = lds_read_tr8(vrd + ((1 ^ vsw) << 4));
+#pragma unroll
+      for (int d = 0; d < kDB; ++d) {
+        if (d + 2 < kDB) vraw[d + 2] = lds_read_tr8(vrd + (((d + 2) ^ vsw) << 4));
+        const bf16x8 vf = fp8x8_to_bf16(vraw[d]);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) oacc[rb][d] = mfma16(vf, pf[rb], oacc[rb][d]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    // ---- O^T += V^T P^T ----
-    const int grp = lane >> 4, i16 = lane & 15;
-    const int hsel = grp >> 1;
-    const int tt = i16 >> 1, qq = i16 & 1;
-    const int key_in = tt < 4 ? hsel * 4 + tt : 8 + hsel * 4 + (tt - 4);
+
+    // ---- partial result: lane l holds O^T[16 d + 4 (l/16) + i][row l%16] ----
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int rr = u * 16 + key_in;
+    for (int rb = 0; rb < NRB; ++rb) {
+      const float l_tot = sum_quad16(l_run[rb]);
+      const int r = rb * 16 + (lane & 15);
+      if (rvalid[rb]) {
+        const float inv = l_tot > 0.0f ? vdesc / l_tot : 0.0f;
+        float* po = a.part_o + (slot * a.slot_rows + r) * DV + kgrp * 4;
 #pragma unroll
-      for (int d = 0; d < DV / 32; ++d) {
-        const int c = d * 2 + (grp & 1);
-        const i32x2 raw = lds_read_tr8(vlds + rr * DV + ((c ^ dec_vswz(rr)) << 4) + qq * 8);
-        oacc[d] = mfma32(fp8x8_to_bf16(raw), pf[u], oacc[d]);
+        for (int d = 0; d < kDB; ++d) {
+          f32x4 w4;
+          w4[0] = oacc[rb][d][0] * inv;
+          w4[1] = oacc[rb][d][1] * inv;
+          w4[2] = oacc[rb][d][2] * inv;
+          w4[3] = oacc[rb][d][3] * inv;
+          *reinterpret_cast<f32x4*>(po + d * 16) = w4;
+        }
+        if (lane < 16)
+          a.part_lse[slot * a.slot_rows + r] = l_tot > 0.0f ? (m_run[rb] + log2_hw(l_tot)) * kLn2 : -INFINITY;
       }
     }
   };
 
-  i32x4 kA[kKLoads], vA[kVLoads], kB[kKLoads], vB[kVLoads];
-  load_tile(0, kA, vA);
-  load_tile(min(1, last), kB, vB);
-  // Q is staged while the first two tiles are in flight
-  // Q fragments: step s = 2p + u holds d = 32p + 16*(lane/32) + 8u + e; lane
-  // l's fragment of step s lives at LDS byte (s*64 + l)*16 of this wave.
-  {
-    const bf16* qp = a.q + tok * a.q_st + (int64_t)h * a.q_sh + (lane >> 5) * 16;
-#pragma unroll
-    for (int p = 0; p < DQK / 32; ++p) {
-      bf16x8 x0 = *reinterpret_cast<const bf16x8*>(qp + 32 * p);
-      bf16x8 x1 = *reinterpret_cast<const bf16x8*>(qp + 32 * p + 8);
-      if (!rvalid) { x0 = bf16x8{}; x1 = bf16x8{}; }
-      *reinterpret_cast<bf16x8 FA_LDS*>(qlds + ((2 * p) * 64 + lane) * 16) = x0;
-      *reinterpret_cast<bf16x8 FA_LDS*>(qlds + ((2 * p + 1) * 64 + lane) * 16) = x1;
+  // first sequence of the share: the largest b with Hkv*tiles[b] <= s0
+  int lo = 0, hi = a.B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)a.Hkv * load_uniform_i32(a.tiles, mid) <= s0) lo = mid;
+    else hi = mid;
+  }
+  int b = lo;
+  int64_t pos = s0;
+  for (;;) {
+    const int tb = load_uniform_i32(a.tiles, b);
+    const int nt = load_uniform_i32(a.tiles, b + 1) - tb;
+    const int64_t base = (int64_t)a.Hkv * tb;
+    const int g = (int)((pos - base) / nt);
+    const int t0 = (int)(pos - base - (int64_t)g * nt);
+    const int t1 = (int)min((int64_t)nt, t0 + (s1 - pos));
+    segment(b, g, t0, t1, (int64_t)w + (int64_t)b * a.Hkv + g);
+    pos += t1 - t0;
+    if (pos >= s1) break;
+    if (pos >= base + (int64_t)a.Hkv * nt) {
+      // next sequence with tiles
+      do {
+        ++b;
+      } while (load_uniform_i32(a.tiles, b + 1) == load_uniform_i32(a.tiles, b));
     }
-  }
-  int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
-    body(t, kA, vA);
-    body(t + 1, kB, vB);
-  }
-  if (t < ntiles) body(t, kA, vA);
-
-  // ---- partial epilogue ----
-  const float l_tot = sum_pair32(l_run);
-  if (rvalid) {
-    const float inv = l_tot > 0.0f ? vdesc / l_tot : 0.0f;
-    float* po = a.part_o + (((int64_t)split * a.total_q + tok) * a.Hq + h) * DV + (lane >> 5) * 4;
-#pragma unroll
-    for (int d = 0; d < DV / 32; ++d)
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        f32x4 w;
-        w[0] = oacc[d][gi * 4 + 0] * inv;
-        w[1] = oacc[d][gi * 4 + 1] * inv;
-        w[2] = oacc[d][gi * 4 + 2] * inv;
-        w[3] = oacc[d][gi * 4 + 3] * inv;
-        *reinterpret_cast<f32x4*>(po + d * 32 + gi * 8) = w;
-      }
-    if (lane < 32)
-      a.part_lse[((int64_t)split * a.total_q + tok) * a.Hq + h] =
-          l_tot > 0.0f ? (m_run + log2_hw(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
-// Merge split partials: one wavefront per (token, q-head).
+// Merge the partials of a unit's rows: one wavefront per (sequence, kv-head,
+// row), lanes over the head dimension.  The workers that touched unit u are
+// those with a non-empty share from the owner of its first tile through the
+// owner of its last; their partials sit in slots w + u.  A unit with no tile
+// (no keys) gives O = 0 and LSE = -inf.
 template <int DV>
 __global__ __launch_bounds__(256) void fa_combine_kernel(const CombineArgs a) {
   constexpr int kPer = DV / 64;
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.total_q * a.Hq) return;
-  const int64_t tok = row / a.Hq;
-  const int h = (int)(row % a.Hq);
-  float m = -INFINITY;
-  for (int s = 0; s < a.n_split; ++s) m = fmaxf(m, a.part_lse[((int64_t)s * a.total_q + tok) * a.Hq + h]);
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= (int64_t)a.B * a.Hkv * a.slot_rows) return;
+  const int r = (int)(item % a.slot_rows);
+  const int u = (int)(item / a.slot_rows);
+  const int g = u % a.Hkv, b = u / a.Hkv;
+  const int qs = a.cu_q[b];
+  if (r >= (a.cu_q[b + 1] - qs) * a.group) return;
+  const int64_t tok = qs + r / a.group;
+  const int h = g * a.group + r % a.group;
+  const int tb = a.tiles[b], nt = a.tiles[b + 1] - tb;
   float acc[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) acc[e] = 0.0f;
   float lse = -INFINITY, inv = 0.0f;
-  if (m > -INFINITY) {
-    float sum = 0.0f;
-    for (int s = 0; s < a.n_split; ++s) {
-      const float ls = a.part_lse[((int64_t)s * a.total_q + tok) * a.Hq + h];
-      if (ls > -INFINITY) {
-        const float w = exp2_hw((ls - m) * kLog2e);
-        sum += w;
-        const float* po = a.part_o + (((int64_t)s * a.total_q + tok) * a.Hq + h) * DV + lane * kPer;
+  if (nt > 0) {
+    const int64_t ntot = (int64_t)a.Hkv * a.tiles[a.B];
+    const int64_t first = (int64_t)a.Hkv * tb + (int64_t)g * nt;
+    const int w0 = worker_of(first, ntot, a.n_workers), w1 = worker_of(first + nt - 1, ntot, a.n_workers);
+    // workers with an empty share (more workers than tiles) wrote nothing
+    auto busy = [&](int w) { return (int64_t)w * ntot / a.n_workers < (int64_t)(w + 1) * ntot / a.n_workers; };
+    float m = -INFINITY;
+    for (int w = w0; w <= w1; ++w)
+      if (busy(w)) m = fmaxf(m, a.part_lse[((int64_t)w + u) * a.slot_rows + r]);
+    if (m > -INFINITY) {
+      float sum = 0.0f;
+      for (int w = w0; w <= w1; ++w) {
+        const int64_t slot = (int64_t)w + u;
+        const float ls = busy(w) ? a.part_lse[slot * a.slot_rows + r] : -INFINITY;
+        if (ls > -INFINITY) {
+          const float wt = exp2_hw((ls - m) * kLog2e);
+          sum += wt;
+          const float* po = a.part_o + (slot * a.slot_rows + r) * DV + lane * kPer;
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) acc[e] += w * po[e];
+          for (int e = 0; e < kPer; ++e) acc[e] += wt * po[e];
+        }
       }
+      inv = 1.0f / sum;
+      lse = m + log2_hw(sum) * kLn2;
     }
-    inv = 1.0f / sum;
-    lse = m + log2_hw(sum) * kLn2;
   }
   bf16* op = a.o + tok * a.o_st + (int64_t)h * a.o_sh + lane * kPer;
 #pragma unroll
@@ -295,26 +523,32 @@ __global__ __launch_bounds__(256) void fa_combine_kernel(const CombineArgs a) {
   if (lane == 0) a.lse[(int64_t)h * a.total_q + tok] = lse;
 }
 
-hipError_t decode_dispatch(const DecodeArgs& a, int dqk, int dv, bool fp8, hipStream_t stream, bool* supported) {
-  *supported = true;
-  const int units = a.n_split * a.B * a.Hkv;
-  const dim3 grid((units + kDecWaves - 1) / kDecWaves);
-  if (fp8 && dqk == 192 && dv == 128) {
-    hipLaunchKernelGGL((fa_decode_kernel<192, 128>), grid, dim3(kDecWaves * 64), 0, stream, a);
-    return hipGetLastError();
+hipError_t decode_dispatch(const DecodePlanArgs& plan, const DecodeArgs& a, int dqk, int dv, bool fp8,
+                           hipStream_t stream, bool* supported) {
+  *supported = fp8 && dv == 128 && (dqk == 192 || dqk == 128);
+  if (!*supported) return hipSuccess;
+  hipLaunchKernelGGL(fa_decode_plan_kernel, dim3(1), dim3(256), 0, stream, plan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((a.n_workers + kDecWaves - 1) / kDecWaves);
+  const bool two = a.slot_rows > 16;
+#define FA_DEC(DQ)                                                                                       \
+  if (dqk == DQ) {                                                                                       \
+    if (two) hipLaunchKernelGGL((fa_decode_kernel<DQ, 128, 2>), grid, dim3(kDecWaves * 64), 0, stream, a); \
+    else hipLaunchKernelGGL((fa_decode_kernel<DQ, 128, 1>), grid, dim3(kDecWaves * 64), 0, stream, a);     \
+    return hipGetLastError();                                                                            \
   }
-  if (fp8 && dqk == 128 && dv == 128) {
-    hipLaunchKernelGGL((fa_decode_kernel<128, 128>), grid, dim3(kDecWaves * 64), 0, stream, a);
-    return hipGetLastError();
-  }
+  FA_DEC(192)
+  FA_DEC(128)
+#undef FA_DEC
   *supported = false;
   return hipSuccess;
 }
 
 hipError_t combine_dispatch(const CombineArgs& a, int dv, hipStream_t stream, bool* supported) {
   *supported = true;
-  const int64_t rows = a.total_q * a.Hq;
-  const dim3 grid((unsigned)((rows + 3) / 4));
+  const int64_t items = (int64_t)a.B * a.Hkv * a.slot_rows;
+  const dim3 grid((unsigned)((items + 3) / 4));
   if (dv == 128) {
     hipLaunchKernelGGL((fa_combine_kernel<128>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();

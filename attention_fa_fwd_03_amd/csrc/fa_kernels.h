@@ -42,29 +42,42 @@ struct PrefillArgs {
   int bm_bq, bm_bk, bm_nqb, bm_nkb;
 };
 
-// Split-KV decode over a paged cache.  One wavefront handles the key range
-// [split*split_len, (split+1)*split_len) of one (sequence, kv-head) for all
-// rows = (query i, q-head h in the kv-head's group), rows <= 32.
+// Decode over a paged cache, balanced over a fixed number of workers.  The
+// key tiles (32 keys) of all (sequence, kv-head) units form one list, unit
+// u = b*Hkv + g holding tiles[b+1] - tiles[b] tiles; worker w (one wavefront)
+// takes the tiles [w*T/W, (w+1)*T/W) of that list and writes one partial
+// result per unit it touches, into slot w + u.  A unit's rows are
+// (query i, q-head h in the kv-head's group), rows <= 32.
 struct DecodeArgs {
   const __bf16* q;
   const void* k;
   const void* v;
-  float* part_o;               // [n_split, total_q, Hq, Dv] fp32 (normalised by own l)
-  float* part_lse;             // [n_split, total_q, Hq] fp32 natural-log LSE
+  float* part_o;               // [n_slots, slot_rows, Dv] fp32 (normalised by own l)
+  float* part_lse;             // [n_slots, slot_rows] fp32 natural-log LSE
   const int32_t* cu_q;
   const int32_t* seqlen_k;
   const int32_t* block_table;
   const float* k_descale;
   const float* v_descale;
+  const int32_t* tiles;        // [B+1] exclusive prefix of per-sequence tile counts
   int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, k_pg, v_pg;
-  int64_t total_q;
   int B, Hq, Hkv, group;
   int max_pages, page_shift;
+  int kv_cap;                  // keys read per sequence at most: min(seqlen_k, kv_cap)
   int num_pages;
-  int n_split, split_len;
+  int n_workers;               // W
+  int slot_rows;               // max_seqlen_q * group
   float qk_scale;
   int causal;
   int win_left, win_right;
+};
+
+struct DecodePlanArgs {
+  const int32_t* cu_q;
+  const int32_t* seqlen_k;
+  int32_t* tiles;
+  int B;
+  int kv_cap;
 };
 
 struct CombineArgs {
@@ -72,15 +85,18 @@ struct CombineArgs {
   const float* part_lse;
   __bf16* o;
   float* lse;
+  const int32_t* cu_q;
+  const int32_t* tiles;
   int64_t o_st, o_sh;
   int64_t total_q;
-  int Hq, n_split;
+  int B, Hq, Hkv, group;
+  int n_workers, slot_rows;
 };
 
 hipError_t prefill_dispatch(const PrefillArgs& a, int dqk, int dv, bool fp8, bool paged, int mods,
                             int n_bh, int n_qtiles, hipStream_t stream, bool* supported);
-hipError_t decode_dispatch(const DecodeArgs& a, int dqk, int dv, bool fp8, hipStream_t stream,
-                           bool* supported);
+hipError_t decode_dispatch(const DecodePlanArgs& plan, const DecodeArgs& a, int dqk, int dv, bool fp8,
+                           hipStream_t stream, bool* supported);
 hipError_t combine_dispatch(const CombineArgs& a, int dv, hipStream_t stream, bool* supported);
 
 }  // namespace fa

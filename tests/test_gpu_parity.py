@@ -287,6 +287,34 @@ def test_decode_small(Hq, Hkv, Dqk, sq):
     compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_FP8, what="decode")
 
 
+def test_decode_many_short_units():
+    """Many short sequences (1..120 keys, two without keys, two without a
+    query), GQA 16/8: about 7800 tiles over 3072 wavefronts, so a wavefront
+    takes tiles from several (sequence, kv-head) units and units are cut
+    across wavefronts."""
+    g = np.random.default_rng(7)
+    lk = g.integers(1, 121, 400).tolist()
+    lk[3] = lk[10] = 0
+    lq = [1] * 400
+    lq[5] = lq[20] = 0
+    d = synth.make_paged(lq, lk, 16, 8, 128, 128, page_size=32, seed=131, extra_pages=7)
+    o, lse = _paged_run(d, dict(causal=True), 128)
+    o_ref, l_ref = _paged_ref(d, dict(causal=True))
+    compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_FP8, what="decode short units")
+
+
+@pytest.mark.parametrize("mods_kw", [dict(causal=True), dict(causal=True, window=(100, 0)), dict(window=(50, 3))])
+def test_decode_two_row_blocks(mods_kw):
+    """Two queries x 16 q-heads per kv-head = 32 rows per unit (two row
+    blocks per wavefront), with empty and key-starved sequences."""
+    lk = [0, 1, 2, 33, 500, 2100, 64, 5000]
+    lq = [2, 1, 2, 2, 2, 2, 0, 2]
+    d = synth.make_paged(lq, lk, 32, 2, 192, 128, page_size=64, seed=137, extra_pages=3)
+    o, lse = _paged_run(d, mods_kw, 128)
+    o_ref, l_ref = _paged_ref(d, mods_kw)
+    compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_FP8, what=f"decode 2rb {mods_kw}")
+
+
 def test_decode_requires_workspace():
     d = synth.make_paged([1, 1], [100, 50], 16, 2, 192, 128, page_size=64, seed=111)
     with pytest.raises(fa.FaError) as e:
