@@ -152,11 +152,13 @@ int check_common(int64_t B, int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v) 
   return FA_OK;
 }
 
-// Decode workers: one wavefront each, as many as the chip keeps resident
-// (256 CUs x 4 SIMDs x 3 wavefronts for one 16-row block per wavefront, x 2
-// for two), capped by the tile count so small calls keep small workspaces.
+// Decode workers: one wavefront each.  With one 16-row block per wavefront
+// the kernel keeps two tiles in flight per wavefront and runs one wavefront
+// per SIMD (256 CUs x 4), which measured faster than two; with two row
+// blocks it keeps one tile in flight and runs two per SIMD.  Capped by the
+// tile count so small calls keep small workspaces.
 int64_t decode_workers(int64_t B, int64_t Hkv, int64_t slot_rows, int64_t kv_cap) {
-  const int64_t wmax = slot_rows > 16 ? 2048 : 3072;
+  const int64_t wmax = slot_rows > 16 ? 2048 : 1024;
   const int64_t tiles = B * Hkv * ((kv_cap + 31) / 32);
   return std::max<int64_t>(1, std::min(wmax, tiles));
 }

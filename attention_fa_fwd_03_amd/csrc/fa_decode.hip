@@ -179,8 +179,8 @@ __global__ __launch_bounds__(256) void fa_decode_plan_kernel(const DecodePlanArg
 // worker that owns tile i of T in a split over W workers
 __device__ __forceinline__ int worker_of(int64_t i, int64_t T, int W) { return (int)(((i + 1) * W - 1) / T); }
 
-template <int DQK, int DV, int NRB>
-__global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(NRB == 1 ? 3 : 2)))
+template <int DQK, int DV, int NRB, int NBUF>
+__global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(NBUF >= 3 ? 1 : (NRB == 1 && NBUF == 1 ? 3 : 2))))
 void fa_decode_kernel(const DecodeArgs a) {
   static_assert(DQK % 32 == 0 && DV == 128 && (kDecKT * DQK) % 1024 == 0, "decode tile shapes");
   using T = DecTraits<DQK, DV>;
@@ -274,8 +274,11 @@ void fa_decode_kernel(const DecodeArgs a) {
     // scalar page lookup per tile, clamped to the cache.  In the sequence's
     // last, partial tile the rows past the end re-read the last key (masked
     // before the softmax), so no stale bytes reach the products.
-    i32x4 kbuf[T::kKLoads], vbuf[T::kVLoads];
-    auto load_tile = [&](int t) {
+    using KBuf = i32x4[T::kKLoads];
+    using VBuf = i32x4[T::kVLoads];
+    KBuf kbuf[NBUF];
+    VBuf vbuf[NBUF];
+    auto load_tile = [&](int t, KBuf& kb, VBuf& vb) {
       const int k0 = k_lo + t * kDecKT;
       const int64_t page = min(max(load_uniform_i32(bt, k0 >> a.page_shift), 0), a.num_pages - 1);
       const int nv = skv - k0;                          // rows of the tile inside the sequence
@@ -283,19 +286,19 @@ void fa_decode_kernel(const DecodeArgs a) {
       const uint8_t* vt = vbase + page * a.v_pg + (int64_t)(k0 & pmask) * DV;
       if (nv >= kDecKT) {
 #pragma unroll
-        for (int i = 0; i < T::kKLoads; ++i) kbuf[i] = *reinterpret_cast<const i32x4*>(kt + i * 1024 + lane * 16);
+        for (int i = 0; i < T::kKLoads; ++i) kb[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(kt + i * 1024 + lane * 16));
 #pragma unroll
-        for (int n = 0; n < T::kVLoads; ++n) vbuf[n] = *reinterpret_cast<const i32x4*>(vt + n * 1024 + lane * 16);
+        for (int n = 0; n < T::kVLoads; ++n) vb[n] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(vt + n * 1024 + lane * 16));
       } else {
 #pragma unroll
         for (int i = 0; i < T::kKLoads; ++i) {
           const int off = i * 1024 + lane * 16, row = off / DQK;
-          kbuf[i] = *reinterpret_cast<const i32x4*>(kt + min(row, nv - 1) * DQK + off % DQK);
+          kb[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(kt + min(row, nv - 1) * DQK + off % DQK));
         }
 #pragma unroll
         for (int n = 0; n < T::kVLoads; ++n) {
           const int off = n * 1024 + lane * 16, row = off / DV;
-          vbuf[n] = *reinterpret_cast<const i32x4*>(vt + min(row, nv - 1) * DV + off % DV);
+          vb[n] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(vt + min(row, nv - 1) * DV + off % DV));
         }
       }
     };
@@ -315,7 +318,8 @@ void fa_decode_kernel(const DecodeArgs a) {
         split_e4m3(x, qhi[rb][st], qlo[rb][st]);
       }
     }
-    load_tile(0);
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) load_tile(min(j, last), kbuf[j], vbuf[j]);
 
     f32x4 oacc[NRB][kDB];
 #pragma unroll
@@ -329,14 +333,16 @@ void fa_decode_kernel(const DecodeArgs a) {
       l_run[rb] = 0.0f;
     }
 
-    for (int t = 0; t <= last; ++t) {
-      // tile t: registers -> this wavefront's LDS buffer (the fragment reads
-      // of tile t-1 were consumed, hence complete, before this point)
+    // One tile: registers -> this wavefront's LDS buffer (the fragment reads
+    // of the previous tile were consumed, hence complete, before this
+    // point), refill the registers with the tile NBUF ahead, then the
+    // products from LDS.
+    auto step = [&](int t, KBuf& kb, VBuf& vb, bool refill) {
 #pragma unroll
-      for (int i = 0; i < T::kKLoads; ++i) *reinterpret_cast<i32x4 FA_LDS*>(klds + kst[i]) = kbuf[i];
+      for (int i = 0; i < T::kKLoads; ++i) *reinterpret_cast<i32x4 FA_LDS*>(klds + kst[i]) = kb[i];
 #pragma unroll
-      for (int n = 0; n < T::kVLoads; ++n) *reinterpret_cast<i32x4 FA_LDS*>(vlds + vst[n]) = vbuf[n];
-      if (t < last) load_tile(t + 1);
+      for (int n = 0; n < T::kVLoads; ++n) *reinterpret_cast<i32x4 FA_LDS*>(vlds + vst[n]) = vb[n];
+      if (refill) load_tile(min(t + NBUF, last), kb, vb);
 
       // ---- S^T = K Q^T ----  (fragment n = (kh, st); each read runs two
       // fragments ahead of its products, one chunk per fragment)
@@ -415,7 +421,20 @@ void fa_decode_kernel(const DecodeArgs a) {
         for (int rb = 0; rb < NRB; ++rb) oacc[rb][d] = mfma16(vf, pf[rb], oacc[rb][d]);
         __builtin_amdgcn_sched_barrier(0);
       }
+    };
+    // Unrolled by NBUF so that each register buffer has a fixed name and the
+    // wait for a tile leaves the later tiles' loads in flight.  The refills
+    // are unconditional (clamped to the last tile, so the final round
+    // re-reads it): conditional ones make the compiler merge the buffers
+    // through copies that wait for every load.
+    int t = 0;
+    for (; t + NBUF - 1 <= last; t += NBUF) {
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j) step(t + j, kbuf[j], vbuf[j], true);
     }
+#pragma unroll
+    for (int j = 0; j < NBUF - 1; ++j)
+      if (t + j <= last) step(t + j, kbuf[j], vbuf[j], false);
 
     // ---- partial result: lane l holds O^T[16 d + 4 (l/16) + i][row l%16] ----
 #pragma unroll
@@ -534,8 +553,8 @@ hipError_t decode_dispatch(const DecodePlanArgs& plan, const DecodeArgs& a, int 
   const bool two = a.slot_rows > 16;
 #define FA_DEC(DQ)                                                                                       \
   if (dqk == DQ) {                                                                                       \
-    if (two) hipLaunchKernelGGL((fa_decode_kernel<DQ, 128, 2>), grid, dim3(kDecWaves * 64), 0, stream, a); \
-    else hipLaunchKernelGGL((fa_decode_kernel<DQ, 128, 1>), grid, dim3(kDecWaves * 64), 0, stream, a);     \
+    if (two) hipLaunchKernelGGL((fa_decode_kernel<DQ, 128, 2, 1>), grid, dim3(kDecWaves * 64), 0, stream, a); \
+    else hipLaunchKernelGGL((fa_decode_kernel<DQ, 128, 1, 2>), grid, dim3(kDecWaves * 64), 0, stream, a);  \
     return hipGetLastError();                                                                            \
   }
   FA_DEC(192)
