@@ -46,6 +46,7 @@
 // smaller than a tile take a clamped per-row path.
 #include "fa_device.h"
 #include "fa_kernels.h"
+#include "fa_prefill_common.h"
 
 namespace fa {
 
@@ -72,53 +73,6 @@ struct PrefillTraits {
   static constexpr int kKPer = (kKItems + NTHREADS - 1) / NTHREADS;
   static constexpr int kVPer = (kVItems + NTHREADS - 1) / NTHREADS;
 };
-
-struct SeqView {
-  int b, h, g;
-  int sq, skv;            // lengths of this sequence
-  int64_t qstart, kstart; // first token row (packed Q/O; contiguous K/V)
-};
-
-// LDS row swizzle: 16-byte chunk c of tile row r is stored at c ^ swz(r).
-// The LDS behaves as 64 four-byte banks (256 bytes per conflict-free cycle).
-// K reads (ds_read_b128) touch rows r..r+15 at one chunk per 16 lanes; the
-// transposed V reads (ds_read_b64_tr_b16) touch 4 rows x 4 adjacent chunks
-// per 32 lanes.  256-byte rows: a 4-bit map that is a bijection on r mod 16
-// and sends the 4 rows of a V group to distinct quarters of the bank space.
-// 128- and 384-byte rows alternate bank halves by themselves: a 3-bit map on
-// r >> 1 that also keeps rows 2 apart in different 4-chunk groups.  The XOR
-// stays inside aligned groups of 16 (8) chunks, i.e. inside the row.
-template <int kRow>
-__device__ __forceinline__ int swz(int r) {
-  if (kRow == 256) return ((r & 3) << 2) | ((r >> 2) & 3);
-  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
-
-// Element offset of key row j in the slow path (tail tiles, pages smaller
-// than a tile): clamped row, per-row page lookup.
-__device__ __forceinline__ int64_t key_row_offset(const PrefillArgs& a, const SeqView& sv, int j,
-                                                  int64_t st, int64_t sh, int64_t pg, bool paged) {
-  j = j < sv.skv ? j : sv.skv - 1;                  // tail rows are masked anyway
-  if (paged) {
-    int page = a.block_table[(int64_t)sv.b * a.max_pages + (j >> a.page_shift)];
-    page = min(max(page, 0), a.num_pages - 1);      // never read outside the cache
-    const int slot = j & ((1 << a.page_shift) - 1);
-    return (int64_t)page * pg + (int64_t)sv.g * sh + (int64_t)slot * st;
-  }
-  return (sv.kstart + j) * st + (int64_t)sv.g * sh;
-}
-
-// Element offset of row 0 of tile k0 in the fast path (whole tile inside the
-// sequence and, for paged caches, inside one page: one scalar page lookup).
-__device__ __forceinline__ int64_t tile_base(const PrefillArgs& a, const SeqView& sv, int k0,
-                                             int64_t st, int64_t sh, int64_t pg, bool paged) {
-  if (paged) {
-    int page = load_uniform_i32(a.block_table, (int64_t)sv.b * a.max_pages + (k0 >> a.page_shift));
-    page = min(max(page, 0), a.num_pages - 1);
-    return (int64_t)page * pg + (int64_t)sv.g * sh + (int64_t)(k0 & ((1 << a.page_shift) - 1)) * st;
-  }
-  return (sv.kstart + k0) * st + (int64_t)sv.g * sh;
-}
 
 // bf16 tile of D columns: global -> LDS with one 1 KB global_load_lds per
 // wave instruction.  Instruction n covers LDS bytes [n*1024, n*1024+1024);
@@ -260,12 +214,9 @@ void fa_prefill_kernel(const PrefillArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  // grid.x is B*Hq rounded up to a multiple of 8 and workgroup i runs on XCD
-  // i % 8, so all query tiles of one (sequence, head) share one XCD's L2;
-  // grid.y walks the query tiles longest (causal) first
-  const int bh = blockIdx.x;
+  int bh, qt;
+  wg_tile(a.causal != 0, bh, qt);
   if (bh >= a.n_bh) return;
-  const int qt = (int)gridDim.y - 1 - (int)blockIdx.y;
   SeqView sv;
   sv.b = bh / a.Hq;
   sv.h = bh % a.Hq;

@@ -36,7 +36,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 COPY_BYTES = 256 << 20        # calibration copy for the HBM byte counters
 DOMINANT = {"prefill": "fa_prefill_kernel", "decode": "fa_decode_kernel"}
 KERNEL_SOURCES = {
-    "prefill": ["attention_fa_fwd_03_amd/csrc/fa_prefill.hip", "attention_fa_fwd_03_amd/csrc/fa_device.h",
+    "prefill": ["attention_fa_fwd_03_amd/csrc/fa_prefill.hip", "attention_fa_fwd_03_amd/csrc/fa_prefill_common.h",
+                "attention_fa_fwd_03_amd/csrc/fa_device.h",
                 "attention_fa_fwd_03_amd/csrc/fa_kernels.h"],
     "decode": ["attention_fa_fwd_03_amd/csrc/fa_decode.hip", "attention_fa_fwd_03_amd/csrc/fa_device.h",
                "attention_fa_fwd_03_amd/csrc/fa_kernels.h"],
