@@ -315,6 +315,32 @@ def test_decode_two_row_blocks(mods_kw):
     compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_FP8, what=f"decode 2rb {mods_kw}")
 
 
+@pytest.mark.parametrize("lq", [[1, 1, 1, 1], [40, 64, 100, 33]])
+def test_paged_pages_beyond_4gib(lq):
+    """Page ids up to 2^19 (K cache 51.5 GB, V 34.4 GB: byte offsets above
+    2^35) with the highest ids in use: decode (one query) and chunked
+    prefill give bitwise the results of the same logical sequences in a
+    compact cache, and those match the oracle."""
+    num_pages = 524289
+    need = num_pages * 8 * 64 * (192 + 128) + (4 << 30)
+    if torch.cuda.mem_get_info()[0] < need:
+        pytest.skip("needs %.1f GB of free device memory" % (need / 1e9))
+    lk = [700, 64, 1000, 33]
+    seed = synth.seed_for(4) + 7
+    big = synth.make_paged(lq, lk, 64, 8, 192, 128, page_size=64, seed=seed, device=DEV,
+                           min_pages=num_pages, place_high=6)
+    assert int(big["block_table"].max()) == num_pages - 1
+    o1, l1 = _paged_run(big, dict(causal=True), 128)
+    del big
+    torch.cuda.empty_cache()
+    # same generator device as above, so the logical K/V and Q are the same values
+    small = synth.make_paged(lq, lk, 64, 8, 192, 128, page_size=64, seed=seed, device=DEV, extra_pages=2)
+    o2, l2 = _paged_run(small, dict(causal=True), 128)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o_ref, l_ref = _paged_ref({k: (v.cpu() if torch.is_tensor(v) else v) for k, v in small.items()}, dict(causal=True))
+    compare(o2.permute(1, 0, 2), l2, o_ref.transpose(1, 0, 2), l_ref, TOL_O_FP8, what="pages beyond 4 GiB")
+
+
 def test_decode_requires_workspace():
     d = synth.make_paged([1, 1], [100, 50], 16, 2, 192, 128, page_size=64, seed=111)
     with pytest.raises(fa.FaError) as e:
