@@ -59,13 +59,19 @@ __device__ __forceinline__ int64_t tile_base(const PrefillArgs& a, const SeqView
 // heads congruent to x mod 8 either way.
 //  - causal (query tiles of unequal cost): query-tile major, longest first,
 //    so the costliest tiles of every head start first (the tail is short);
-//    the few tiles of a head that run together read its K/V in step.
+//    the few tiles of a head that run together read its K/V in step.  Within
+//    an XCD, workgroups are dealt to SEs and CUs round-robin in dispatch
+//    order whatever their cost, so the head of each slot rotates per level.
 //  - otherwise (equal cost): head major, all query tiles of one head in a
 //    row, so the workgroups that read the same K/V share one XCD's L2.
 __device__ __forceinline__ void wg_tile(bool causal, int& bh, int& qt) {
   const int gx = (int)gridDim.x, gy = (int)gridDim.y;
   if (causal) {
-    bh = (int)blockIdx.x;
+    // the head rotates by one XCD slot per query-tile level: workgroups go to
+    // CUs round-robin in dispatch order, so without the rotation a CU would
+    // meet the same (sequence, head) at every level it serves and inherit
+    // that sequence's length as its load
+    bh = ((int)blockIdx.x + 8 * (int)blockIdx.y) % gx;
     qt = gy - 1 - (int)blockIdx.y;
     return;
   }
