@@ -165,7 +165,6 @@ int64_t decode_workers(int64_t B, int64_t Hkv, int64_t slot_rows, int64_t kv_cap
 
 bool uses_decode(int64_t max_sq, int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v, fa_dtype kv, int64_t page_size) {
   if (kv != FA_FP8_E4M3 || d_v != 128 || (d_qk != 192 && d_qk != 128)) return false;
-  if (page_size < 32) return false;   // the decode kernel looks pages up once per 32-key tile
   return max_sq >= 1 && max_sq * (Hq / Hkv) <= kDecodeRows;
 }
 

@@ -269,9 +269,9 @@ void fa_decode_kernel(const DecodeArgs a) {
 
     // Coalesced tile loads: load i of this lane covers bytes [1024 i + 16
     // lane, +16) of the tile.  Page rows are contiguous (row stride = head
-    // dim), so a whole tile is one block of the page; pages hold whole
-    // 32-key tiles (page_size >= 32, checked by the host): one wave-uniform
-    // scalar page lookup per tile, clamped to the cache.  In the sequence's
+    // dim), so with pages of 32 keys or more a whole tile is one block of a
+    // page: one wave-uniform scalar page lookup per tile, clamped to the
+    // cache.  Smaller pages take a per-lane lookup of each row's page.  In the sequence's
     // last, partial tile the rows past the end re-read the last key (masked
     // before the softmax), so no stale bytes reach the products.
     using KBuf = i32x4[T::kKLoads];
@@ -280,8 +280,27 @@ void fa_decode_kernel(const DecodeArgs a) {
     VBuf vbuf[NBUF];
     auto load_tile = [&](int t, KBuf& kb, VBuf& vb) {
       const int k0 = k_lo + t * kDecKT;
-      const int64_t page = min(max(load_uniform_i32(bt, k0 >> a.page_shift), 0), a.num_pages - 1);
       const int nv = skv - k0;                          // rows of the tile inside the sequence
+      if (a.page_shift < 5) {
+        // pages smaller than a tile: each lane looks up the page of the key
+        // row its 16 bytes belong to (a chunk never straddles a row)
+#pragma unroll
+        for (int i = 0; i < T::kKLoads; ++i) {
+          const int off = i * 1024 + lane * 16, key = k0 + min(off / DQK, nv - 1);
+          const int64_t pg = min(max(bt[key >> a.page_shift], 0), a.num_pages - 1);
+          kb[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(
+              kbase + pg * a.k_pg + (int64_t)(key & pmask) * DQK + off % DQK));
+        }
+#pragma unroll
+        for (int n = 0; n < T::kVLoads; ++n) {
+          const int off = n * 1024 + lane * 16, key = k0 + min(off / DV, nv - 1);
+          const int64_t pg = min(max(bt[key >> a.page_shift], 0), a.num_pages - 1);
+          vb[n] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(
+              vbase + pg * a.v_pg + (int64_t)(key & pmask) * DV + off % DV));
+        }
+        return;
+      }
+      const int64_t page = min(max(load_uniform_i32(bt, k0 >> a.page_shift), 0), a.num_pages - 1);
       const uint8_t* kt = kbase + page * a.k_pg + (int64_t)(k0 & pmask) * DQK;
       const uint8_t* vt = vbase + page * a.v_pg + (int64_t)(k0 & pmask) * DV;
       if (nv >= kDecKT) {

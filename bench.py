@@ -9,7 +9,8 @@ online softmax, P.V, epilogue with O and LSE).  Inputs are resident in HBM
 before timing starts.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
-                  [--flex alibi|softcap|window|bernoulli|block_causal|none|causal] [--no-cpu-baseline]
+                  [--flex alibi|softcap|window|bernoulli|block_causal|none|causal] [--page-size P]
+                  [--no-cpu-baseline]
                   [--copy-calibration]
   python bench.py --config N --traffic-from FETCH_CSV WRITE_CSV
 
@@ -111,7 +112,7 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, key: str, kind: str) -
     return entry
 
 
-def build_workload(cfg: int, flex: str, torch, synth, fa):
+def build_workload(cfg: int, flex: str, torch, synth, fa, page_size: int = 64):
     """Returns (name, run_fn, work dict, oracle sample fn)."""
     dev = "cuda"
     if cfg == 1:
@@ -159,24 +160,25 @@ def build_workload(cfg: int, flex: str, torch, synth, fa):
     if cfg == 4:
         lk = synth.make_decode_lengths(synth.seed_for(4))
         lq = [1] * 64
-        d = synth.make_paged(lq, lk, 64, 8, 192, 128, page_size=64, seed=synth.seed_for(4), device=dev)
+        ps = page_size
+        d = synth.make_paged(lq, lk, 64, 8, 192, 128, page_size=ps, seed=synth.seed_for(4), device=dev)
         o = torch.empty(64, 64, 128, dtype=torch.bfloat16, device=dev)
         lse = torch.empty(64, 64, dtype=torch.float32, device=dev)
-        n = fa.fa_fwd_paged_workspace_size(64, 64, 1, max(lk), 64, 8, 192, 128, 64)
+        n = fa.fa_fwd_paged_workspace_size(64, 64, 1, max(lk), 64, 8, 192, 128, ps)
         ws = torch.empty(n, dtype=torch.uint8, device=dev)
         mods = fa.Mods(causal=True)
         kv_bytes = sum(lk) * 8 * (192 + 128)
-        io_bytes = 64 * 64 * 192 * 2 + 64 * 64 * 128 * 2 + 64 * 64 * 4 + sum(math.ceil(x / 64) for x in lk) * 4
+        io_bytes = 64 * 64 * 192 * 2 + 64 * 64 * 128 * 2 + 64 * 64 * 4 + sum(math.ceil(x / ps) for x in lk) * 4
         flops = sum(lk) * 64 * (2 * 192 + 2 * 128)
         run = lambda: fa.fa_fwd_paged(d["q"], d["k_cache"], d["v_cache"], o, lse, d["cu_q"], d["seqlen_k"],
                                       d["block_table"], 1, max(lk), d["k_descale"], d["v_descale"], ws, mods)
-        name = "paged FP8 decode 64 seqs ctx U[1024,32768] GQA 64/8 Dqk192 Dv128 page64"
+        name = f"paged FP8 decode 64 seqs ctx U[1024,32768] GQA 64/8 Dqk192 Dv128 page{ps}"
 
         def sample():
             import oracle
             n_seq = 8   # the first 8 sequences; only their pages are copied to the host
             bt = d["block_table"][:n_seq]
-            npg = [math.ceil(x / 64) for x in lk[:n_seq]]
+            npg = [math.ceil(x / ps) for x in lk[:n_seq]]
             ids = torch.cat([bt[b, :npg[b]] for b in range(n_seq)]).long()
             kc = d["k_cache"].index_select(0, ids).cpu().numpy()
             vc = d["v_cache"].index_select(0, ids).cpu().numpy()
@@ -194,7 +196,7 @@ def build_workload(cfg: int, flex: str, torch, synth, fa):
             return dict(seconds=dt, work=sbytes * reps,
                         sample=f"sequences 0-{n_seq - 1} ({sum(lk[:n_seq])} cached tokens, all heads), {reps} passes")
         return name, run, dict(flops=flops, bytes=kv_bytes + io_bytes, kind="decode", bound="hbm"), \
-            {"B": 64, "ctx_total": sum(lk), "Hq": 64, "Hkv": 8, "page_size": 64}, sample
+            {"B": 64, "ctx_total": sum(lk), "Hq": 64, "Hkv": 8, "page_size": ps}, sample
     if cfg == 5:
         B, H, S, D = 2, 16, 8192, 128
         d = synth.make_dense(B, S, S, H, H, D, D, seed=synth.seed_for(5), device=dev)
@@ -258,6 +260,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--flex", default="alibi")
+    ap.add_argument("--page-size", type=int, default=64, help="decode config: cache page size (power of two)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (reference for HBM byte counters)")
@@ -265,6 +268,8 @@ def main():
                     help="record HBM bytes per launch from two rocprofv3 --pmc counter CSVs and exit")
     args = ap.parse_args()
     key = f"config{args.config}" + (f"_{args.flex}" if args.config == 5 else "")
+    if args.config == 4 and args.page_size != 64:
+        key += f"_ps{args.page_size}"
     if args.traffic_from:
         kind = "decode" if args.config == 4 else "prefill"
         print(json.dumps({key: traffic_from_counters(args.traffic_from[0], args.traffic_from[1], key, kind)}))
@@ -279,7 +284,7 @@ def main():
     import attention_fa_fwd_03_amd as fa
 
     torch.cuda.init()
-    name, run, work, cfg_extra, sample = build_workload(args.config, args.flex, torch, synth, fa)
+    name, run, work, cfg_extra, sample = build_workload(args.config, args.flex, torch, synth, fa, args.page_size)
     if args.copy_calibration:
         # reference for the HBM byte counters: one device-to-device copy of
         # COPY_BYTES through the HIP runtime's own copy kernel

@@ -121,13 +121,13 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  * [B, max_pages_per_seq]); seqlen_k (device int32 [B]) is its key count.
  * Only the first ceil(seqlen_k[b] / page_size) entries of a block-table row
  * are read, and bytes past seqlen_k in a page never influence the result.
- * page_size: a power of two in [16, 1024].
+ * page_size: a power of two in [1, 1024].
  * Built: FP8 (d_qk, d_v) in {(192, 128), (128, 128)}; bf16 (64, 64), (128, 128).
  * Mods: FA_CAUSAL and FA_WINDOW only.
- * When max_seqlen_q * (Hq / Hkv) <= 32 (decode), kv_dtype is FP8, d_v is 128
- * and page_size >= 32, the
- * keys are split and partial results merged; that path needs a device
- * workspace of fa_fwd_paged_workspace_size(...) bytes (else FA_ERR_WORKSPACE).
+ * When max_seqlen_q * (Hq / Hkv) <= 32 (decode), kv_dtype is FP8 and d_v is
+ * 128, the keys are split and partial results merged; that path needs a
+ * device workspace of fa_fwd_paged_workspace_size(...) bytes (else
+ * FA_ERR_WORKSPACE).
  * The workspace is scratch, overwritten by the call.
  */
 int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,

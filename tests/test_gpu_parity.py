@@ -216,7 +216,7 @@ def _paged_ref(d, mods_kw):
                                   d["block_table"], dict(mods_kw), float(d["k_descale"]), float(d["v_descale"]))
 
 
-@pytest.mark.parametrize("ps", [64, 16, 128])
+@pytest.mark.parametrize("ps", [64, 16, 128, 8, 1])
 def test_paged_fp8_prefill_small(ps):
     lk = [70, 3, 128, 129, 600]
     lq = [70, 3, 128, 129, 600]
@@ -249,10 +249,11 @@ def _reshuffle(d, seed):
     return e
 
 
+@pytest.mark.parametrize("ps", [64, 1])
 @pytest.mark.parametrize("lq", [[200, 64, 1], [1, 1, 1]])
-def test_paged_placement_is_bitwise_invariant(lq):
+def test_paged_placement_is_bitwise_invariant(lq, ps):
     lk = [300, 64, 700]
-    d = synth.make_paged(lq, lk, 8, 1 if lq[0] == 1 else 8, 192, 128, page_size=64, seed=95, extra_pages=11)
+    d = synth.make_paged(lq, lk, 8, 1 if lq[0] == 1 else 8, 192, 128, page_size=ps, seed=95, extra_pages=11)
     o1, l1 = _paged_run(d, dict(causal=True), 128)
     e = _reshuffle(d, 3)
     o2, l2 = _paged_run(e, dict(causal=True), 128)
@@ -285,6 +286,18 @@ def test_decode_small(Hq, Hkv, Dqk, sq):
     o, lse = _paged_run(d, dict(causal=True), 128)
     o_ref, l_ref = _paged_ref(d, dict(causal=True))
     compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_FP8, what="decode")
+
+
+@pytest.mark.parametrize("ps,Hq,Hkv,sq", [(16, 16, 2, 1), (8, 16, 2, 1), (1, 16, 2, 1), (8, 32, 2, 2)])
+def test_decode_small_pages(ps, Hq, Hkv, sq):
+    """Pages smaller than the 32-key decode tile: each lane looks up the page
+    of its key row (bytes past seqlen_k and unused pages hold NaN)."""
+    lk = [1, 31, 32, 33, 64, 300, 1000, 77]
+    lq = [min(sq, l) for l in lk]
+    d = synth.make_paged(lq, lk, Hq, Hkv, 192, 128, page_size=ps, seed=151 + ps + sq, extra_pages=9)
+    o, lse = _paged_run(d, dict(causal=True), 128)
+    o_ref, l_ref = _paged_ref(d, dict(causal=True))
+    compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_FP8, what=f"decode ps{ps}")
 
 
 def test_decode_many_short_units():
