@@ -10,9 +10,10 @@ Layouts (readings of the pages, see the package docstring):
             cu_seqlens_q / cu_seqlens_k (int32 [B+1]); O [Tq,Hq,Dv], LSE [Hq,Tq];
   * paged   Q and O as varlen (cu_seqlens_q); key j of sequence b is slot
             j % page_size of physical page block_table[b, j // page_size] in
-            head-major caches K [P,Hkv,page_size,Dqk], V [P,Hkv,page_size,Dv];
-            seqlen_k[b] keys; FP8 caches hold OCP E4M3 codes scaled by a
-            per-tensor descale.
+            head-major caches K [P,Hkv,page_size,Dqk], V [P,Hkv,page_size,Dv],
+            or in the vectorized 5-D caches K [P,Hkv,Dqk/x,page_size,x],
+            V [P,Hkv,page_size/x,Dv,x] (see gather_paged); seqlen_k[b] keys;
+            FP8 caches hold OCP E4M3 codes scaled by a per-tensor descale.
   * GQA     q-head h reads kv-head h // (Hq / Hkv) (consecutive q-heads share
             a kv-head; the pages are silent, Hkv = 1 there).
   * scale   default 1/sqrt(Dqk) (RL-Kernel PR: default softmax scale).
@@ -153,17 +154,40 @@ def varlen_rows(q, k, v, cu_q, cu_k, picks, mods=None):
     return o, lse
 
 
-def gather_paged(cache, block_row, length, g, descale=None):
+def gather_paged(cache, block_row, length, g, descale=None, layout="head_major", kind="k"):
     """Token-major [length, D] float64 rows of kv-head g for one sequence.
 
-    Key j is slot j % ps of page block_row[j // ps]; FP8 caches (uint8) are
-    decoded as OCP E4M3 and multiplied by `descale` in float64.
+    Key j is slot s = j % ps of page p = block_row[j // ps].  Layouts:
+      * head_major  cache [P, Hkv, ps, D]: element (j, d) at [p, g, s, d];
+      * vectorized  (the 5-D page layout of "Support paged FP8 Flash attention
+        with asymmetric K/V head dim on gfx950", review of the interface:
+        a K page is [Hkv, D/16, ps, 16] and a V page [Hkv, ps/16, Dv, 16],
+        16 one-byte codes per vector; x = the last extent):
+          kind "k": cache [P, Hkv, D/x, ps, x], element (j, d) at [p, g, d // x, s, d % x]
+          kind "v": cache [P, Hkv, ps/x, Dv, x], element (j, d) at [p, g, s // x, d, s % x]
+    FP8 caches (uint8) are decoded as OCP E4M3 and multiplied by `descale`
+    in float64.
     """
     cache = np.asarray(cache)
-    ps = cache.shape[2]
     j = np.arange(length)
-    pages = np.asarray(block_row, dtype=np.int64)[j // ps]
-    raw = cache[pages, g, j % ps]
+    if layout == "head_major":
+        ps = cache.shape[2]
+        pages = np.asarray(block_row, dtype=np.int64)[j // ps]
+        raw = cache[pages, g, j % ps]
+    elif layout == "vectorized" and kind == "k":
+        x, ps = cache.shape[4], cache.shape[3]
+        d = np.arange(cache.shape[2] * x)
+        pages = np.asarray(block_row, dtype=np.int64)[j // ps]
+        raw = cache[pages[:, None], g, (d // x)[None, :], (j % ps)[:, None], (d % x)[None, :]]
+    elif layout == "vectorized" and kind == "v":
+        x = cache.shape[4]
+        ps = cache.shape[2] * x
+        d = np.arange(cache.shape[3])
+        pages = np.asarray(block_row, dtype=np.int64)[j // ps]
+        s = j % ps
+        raw = cache[pages[:, None], g, (s // x)[:, None], d[None, :], (s % x)[:, None]]
+    else:
+        raise ValueError(f"unknown paged layout {layout!r} / kind {kind!r}")
     if raw.dtype == np.uint8:
         out = decode_e4m3(raw)
         if descale is not None:
@@ -173,8 +197,9 @@ def gather_paged(cache, block_row, length, g, descale=None):
 
 
 def attention_paged(q, k_cache, v_cache, cu_q, seqlen_k, block_table, mods=None,
-                    k_descale=None, v_descale=None, workers=1):
-    """Paged-KV attention.  Returns (O [Tq,Hq,Dv], LSE [Hq,Tq]) in float64."""
+                    k_descale=None, v_descale=None, workers=1, layout="head_major"):
+    """Paged-KV attention over either page layout (see gather_paged).
+    Returns (O [Tq,Hq,Dv], LSE [Hq,Tq]) in float64."""
     q = _f64(q)
     cu_q = np.asarray(cu_q, dtype=np.int64)
     seqlen_k = np.asarray(seqlen_k, dtype=np.int64)
@@ -191,8 +216,8 @@ def attention_paged(q, k_cache, v_cache, cu_q, seqlen_k, block_table, mods=None,
     def unit(bg):
         b, g = bg
         L = int(seqlen_k[b])
-        kh = gather_paged(k_cache, block_table[b], L, g, k_descale)
-        vh = gather_paged(v_cache, block_table[b], L, g, v_descale)
+        kh = gather_paged(k_cache, block_table[b], L, g, k_descale, layout, "k")
+        vh = gather_paged(v_cache, block_table[b], L, g, v_descale, layout, "v")
         q0, q1 = cu_q[b], cu_q[b + 1]
         res = []
         for h in range(g * grp, (g + 1) * grp):
@@ -209,8 +234,9 @@ def attention_paged(q, k_cache, v_cache, cu_q, seqlen_k, block_table, mods=None,
 
 
 def paged_rows(q, k_cache, v_cache, cu_q, seqlen_k, block_table, picks, mods=None,
-               k_descale=None, v_descale=None):
-    """Selected rows (b, h, i) of paged attention; returns (O [n, Dv], LSE [n])."""
+               k_descale=None, v_descale=None, layout="head_major"):
+    """Selected rows (b, h, i) of paged attention over either page layout;
+    returns (O [n, Dv], LSE [n])."""
     cu_q = np.asarray(cu_q, dtype=np.int64)
     seqlen_k = np.asarray(seqlen_k, dtype=np.int64)
     block_table = np.asarray(block_table, dtype=np.int64)
@@ -230,8 +256,8 @@ def paged_rows(q, k_cache, v_cache, cu_q, seqlen_k, block_table, picks, mods=Non
         g = h // grp
         L = int(seqlen_k[b])
         if (b, g) not in gathered:
-            gathered = {(b, g): (gather_paged(k_cache, block_table[b], L, g, k_descale),
-                                 gather_paged(v_cache, block_table[b], L, g, v_descale))}
+            gathered = {(b, g): (gather_paged(k_cache, block_table[b], L, g, k_descale, layout, "k"),
+                                 gather_paged(v_cache, block_table[b], L, g, v_descale, layout, "v"))}
         kh, vh = gathered[(b, g)]
         q0, q1 = cu_q[b], cu_q[b + 1]
         rows = np.array([i for _, i in lst])

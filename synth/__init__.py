@@ -17,6 +17,7 @@ Recipes (seed = 1000 + 10*config + subcase):
   * block masks: uint8 [B*Hq, nQB, nKB], Bernoulli(p) or block-causal.
 """
 from .gen import (  # noqa: F401
+    to_vectorized,
     seed_for,
     randn_bf16,
     quantize_e4m3,

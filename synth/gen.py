@@ -168,6 +168,19 @@ def make_paged(lengths_q, lengths_k, Hq, Hkv, Dqk, Dv, page_size, seed, device="
     )
 
 
+def to_vectorized(d, x=16):
+    """Copy of a make_paged() dict with its caches in the vectorized 5-D page
+    layout: K [P, Hkv, Dqk/x, page_size, x], V [P, Hkv, page_size/x, Dv, x]
+    (x elements of 16 bytes per vector).  A pure re-layout of the same bytes."""
+    k, v = d["k_cache"], d["v_cache"]
+    P, Hkv, ps, Dqk = k.shape
+    Dv = v.shape[3]
+    e = dict(d)
+    e["k_cache"] = k.reshape(P, Hkv, ps, Dqk // x, x).permute(0, 1, 3, 2, 4).contiguous()
+    e["v_cache"] = v.reshape(P, Hkv, ps // x, x, Dv).permute(0, 1, 2, 4, 3).contiguous()
+    return e
+
+
 def bernoulli_block_mask(bh, nqb, nkb, p, seed):
     """uint8 [bh, nqb, nkb]: 1 with probability p (seeded)."""
     g = _generator(seed + 400_000, "cpu")

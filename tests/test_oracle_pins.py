@@ -13,6 +13,8 @@ import pytest
 import torch
 
 import oracle
+import synth
+from tests.helpers import f64
 from oracle import attention as oatt
 from oracle import layouts as olay
 
@@ -346,3 +348,37 @@ def test_paged_4gib_golden_geometry():
     assert round(gd["cache_bytes"] / 1e9, 1) == gd["cache_bytes_approx_gb"]
     assert gd["high_page"] * kpb >= 2 ** 32 and gd["high_page"] * vpb >= 2 ** 32
     assert (gd["high_page"] - 1) * vpb < 2 ** 32
+
+
+# ----------------------------------------------------------------------------- vectorized pages
+def test_vectorized_gather_matches_the_pages_inverse_permutes():
+    """The 5-D page layout as the pages state it: permuting a K cache
+    [P, Hkv, D/16, ps, 16] by (0,3,1,2,4), and a V cache [P, Hkv, ps/16, Dv, 16]
+    by (0,2,4,1,3), gives token-major pages [P, ps, Hkv, D]; the oracle's
+    gather must read exactly those rows."""
+    rng = np.random.default_rng(11)
+    P, Hkv, ps, D, Dv, x = 5, 2, 32, 48, 32, 16
+    k5 = rng.integers(0, 120, size=(P, Hkv, D // x, ps, x)).astype(np.uint8)
+    v5 = rng.integers(0, 120, size=(P, Hkv, ps // x, Dv, x)).astype(np.uint8)
+    kt = k5.transpose(0, 3, 1, 2, 4).reshape(P, ps, Hkv, D)
+    vt = v5.transpose(0, 2, 4, 1, 3).reshape(P, ps, Hkv, Dv)
+    block_row = [3, 0, 4]
+    L = 77
+    for g in range(Hkv):
+        kg = oracle.gather_paged(k5, block_row, L, g, layout="vectorized", kind="k")
+        vg = oracle.gather_paged(v5, block_row, L, g, layout="vectorized", kind="v")
+        for j in range(L):
+            p, sl = block_row[j // ps], j % ps
+            assert np.array_equal(kg[j], oracle.decode_e4m3(kt[p, sl, g]))
+            assert np.array_equal(vg[j], oracle.decode_e4m3(vt[p, sl, g]))
+
+
+def test_vectorized_pages_give_the_head_major_result():
+    """The same logical cache in both page layouts gives identical fp64
+    attention (the layout only moves bytes)."""
+    d = synth.make_paged([3, 40], [70, 40], 4, 2, 64, 32, page_size=32, seed=171, extra_pages=2)
+    e = synth.to_vectorized(d)
+    args = (d["cu_q"], d["seqlen_k"], d["block_table"], dict(causal=True), float(d["k_descale"]), float(d["v_descale"]))
+    o1, l1 = oracle.attention_paged(f64(d["q"]), d["k_cache"].numpy(), d["v_cache"].numpy(), *args)
+    o2, l2 = oracle.attention_paged(f64(e["q"]), e["k_cache"].numpy(), e["v_cache"].numpy(), *args, layout="vectorized")
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
