@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     fa_fwd_dense,
     fa_fwd_varlen,
     fa_fwd_paged,
+    fa_fwd_paged_vec,
     fa_fwd_paged_workspace_size,
     fa_last_error,
     fa_abi_version,

@@ -54,6 +54,8 @@ lib.fa_fwd_varlen.restype = ctypes.c_int
 lib.fa_fwd_paged.argtypes = ([_vp] * 8 + [_i64] * 11 + [ctypes.c_int, _vp, _vp, _vp, _sz,
                                                          ctypes.POINTER(_FaMods), _vp])
 lib.fa_fwd_paged.restype = ctypes.c_int
+lib.fa_fwd_paged_vec.argtypes = lib.fa_fwd_paged.argtypes
+lib.fa_fwd_paged_vec.restype = ctypes.c_int
 lib.fa_fwd_paged_workspace_size.argtypes = [_i64] * 9 + [ctypes.c_int]
 lib.fa_fwd_paged_workspace_size.restype = _sz
 lib.fa_last_error.argtypes = []
@@ -183,15 +185,40 @@ def fa_fwd_paged(q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_tabl
 
     k_cache/v_cache: uint8 (FP8 E4M3 codes) or bf16, [num_pages, Hkv, page_size, D].
     """
-    Tq, Hq, Dqk = q.shape
-    P, Hkv, ps, _ = k_cache.shape
+    P, Hkv, ps, Dqk = k_cache.shape
     Dv = v_cache.shape[3]
-    B = cu_seqlens_q.shape[0] - 1
     fp8 = k_cache.dtype == torch.uint8
     cdt = torch.uint8 if fp8 else torch.bfloat16
-    _need(q, "q", torch.bfloat16)
     _need(k_cache, "k_cache", cdt, (P, Hkv, ps, Dqk))
     _need(v_cache, "v_cache", cdt, (P, Hkv, ps, Dv))
+    _paged_call(lib.fa_fwd_paged, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, max_seqlen_q,
+                max_seqlen_k, P, Hkv, ps, Dqk, Dv, fp8, k_descale, v_descale, workspace, mods, stream)
+
+
+def fa_fwd_paged_vec(q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, max_seqlen_q,
+                     max_seqlen_k, k_descale=None, v_descale=None, workspace=None, mods=None, stream=None):
+    """fa_fwd_paged over vectorised FP8 pages (see include/fa.h).
+
+    k_cache: uint8 [num_pages, Hkv, D_qk/16, page_size, 16];
+    v_cache: uint8 [num_pages, Hkv, page_size/16, D_v, 16].
+    """
+    if k_cache.dim() != 5 or v_cache.dim() != 5:
+        raise ValueError("vectorised caches are 5-D")
+    P, Hkv, nc, ps, x = k_cache.shape
+    Dqk = nc * x
+    Dv = v_cache.shape[3]
+    _need(k_cache, "k_cache", torch.uint8, (P, Hkv, Dqk // 16, ps, 16))
+    _need(v_cache, "v_cache", torch.uint8, (P, Hkv, ps // 16, Dv, 16))
+    _paged_call(lib.fa_fwd_paged_vec, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table,
+                max_seqlen_q, max_seqlen_k, P, Hkv, ps, Dqk, Dv, True, k_descale, v_descale, workspace, mods,
+                stream)
+
+
+def _paged_call(fn, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, max_seqlen_q, max_seqlen_k,
+                P, Hkv, ps, Dqk, Dv, fp8, k_descale, v_descale, workspace, mods, stream):
+    Tq, Hq = q.shape[0], q.shape[1]
+    B = cu_seqlens_q.shape[0] - 1
+    _need(q, "q", torch.bfloat16, (Tq, Hq, Dqk))
     _need(o, "o", torch.bfloat16, (Tq, Hq, Dv))
     _need(lse, "lse", torch.float32, (Hq, Tq))
     _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, (B + 1,))
@@ -206,9 +233,9 @@ def fa_fwd_paged(q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_tabl
     if workspace is not None:
         _need(workspace, "workspace")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    _check(lib.fa_fwd_paged(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                            cu_seqlens_q.data_ptr(), seqlen_k.data_ptr(), block_table.data_ptr(),
-                            B, Tq, int(max_seqlen_q), int(max_seqlen_k), P, ps, block_table.shape[1],
-                            Hq, Hkv, Dqk, Dv, FA_FP8_E4M3 if fp8 else FA_BF16,
-                            k_descale.data_ptr() if fp8 else None, v_descale.data_ptr() if fp8 else None,
-                            ws_ptr or None, ws_bytes, _mods(mods), _stream(stream, q.device)))
+    _check(fn(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), lse.data_ptr(),
+              cu_seqlens_q.data_ptr(), seqlen_k.data_ptr(), block_table.data_ptr(),
+              B, Tq, int(max_seqlen_q), int(max_seqlen_k), P, ps, block_table.shape[1],
+              Hq, Hkv, Dqk, Dv, FA_FP8_E4M3 if fp8 else FA_BF16,
+              k_descale.data_ptr() if fp8 else None, v_descale.data_ptr() if fp8 else None,
+              ws_ptr or None, ws_bytes, _mods(mods), _stream(stream, q.device)))

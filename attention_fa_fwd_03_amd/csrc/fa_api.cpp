@@ -125,7 +125,7 @@ int mod_bits(const Mods& m) {
   return ((m.flags & FA_ALIBI) ? fa::kModAlibi : 0) | ((m.flags & FA_SOFTCAP) ? fa::kModSoftcap : 0);
 }
 
-int launch_prefill(const fa::PrefillArgs& a_in, int64_t dqk, int64_t dv, bool fp8, bool paged, int mods,
+int launch_prefill(const fa::PrefillArgs& a_in, int64_t dqk, int64_t dv, bool fp8, bool paged, bool vec, int mods,
                    int64_t B, int64_t Hq, int64_t max_sq, hipStream_t stream) {
   const int64_t n_bh = B * Hq;
   const int64_t n_qt = (max_sq + kBM - 1) / kBM;
@@ -136,7 +136,8 @@ int launch_prefill(const fa::PrefillArgs& a_in, int64_t dqk, int64_t dv, bool fp
   fa::PrefillArgs a = a_in;
   a.n_bh = (int)n_bh;
   bool supported = false;
-  hipError_t e = fa::prefill_dispatch(a, (int)dqk, (int)dv, fp8, paged, mods, (int)n_bh, (int)n_qt, stream, &supported);
+  hipError_t e = fa::prefill_dispatch(a, (int)dqk, (int)dv, fp8, paged, vec, mods, (int)n_bh, (int)n_qt, stream,
+                                       &supported);
   if (!supported) return fail(FA_ERR_UNSUPPORTED, "no kernel built for d_qk=%lld d_v=%lld fp8=%d paged=%d mods=%d",
                               (long long)dqk, (long long)dv, (int)fp8, (int)paged, mods);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -242,7 +243,7 @@ int fa_fwd_dense(const void* q, const void* k, const void* v, void* o, float* ls
   a.Sq = (int)Sq; a.Skv = (int)Skv;
   a.Hq = (int)Hq; a.group = (int)(Hq / Hkv);
   fill_mods(a, m);
-  return launch_prefill(a, d_qk, d_v, false, false, mod_bits(m), B, Hq, Sq, (hipStream_t)stream);
+  return launch_prefill(a, d_qk, d_v, false, false, false, mod_bits(m), B, Hq, Sq, (hipStream_t)stream);
 }
 
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -288,7 +289,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   a.lse_tq = total_q;
   a.Hq = (int)Hq; a.group = (int)(Hq / Hkv);
   fill_mods(a, m);
-  return launch_prefill(a, d_qk, d_v, false, false, mod_bits(m), B, Hq, max_seqlen_q, (hipStream_t)stream);
+  return launch_prefill(a, d_qk, d_v, false, false, false, mod_bits(m), B, Hq, max_seqlen_q, (hipStream_t)stream);
 }
 
 size_t fa_fwd_paged_workspace_size(int64_t B, int64_t total_q, int64_t max_seqlen_q, int64_t max_seqlen_k,
@@ -297,23 +298,32 @@ size_t fa_fwd_paged_workspace_size(int64_t B, int64_t total_q, int64_t max_seqle
   return workspace_bytes(B, total_q, max_seqlen_q, max_seqlen_k, Hq, Hkv, d_qk, d_v, kv_dtype, page_size);
 }
 
-int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
-                 const int32_t* cu_seqlens_q, const int32_t* seqlen_k, const int32_t* block_table,
-                 int64_t B, int64_t total_q, int64_t max_seqlen_q, int64_t max_seqlen_k,
-                 int64_t num_pages, int64_t page_size, int64_t max_pages_per_seq,
-                 int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v, fa_dtype kv_dtype,
-                 const float* k_descale, const float* v_descale,
-                 void* workspace, size_t workspace_bytes_in,
-                 const fa_mods* mods, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both paged entry points: vec selects the vectorised page format.
+int paged_impl(bool vec, const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+               const int32_t* cu_seqlens_q, const int32_t* seqlen_k, const int32_t* block_table,
+               int64_t B, int64_t total_q, int64_t max_seqlen_q, int64_t max_seqlen_k,
+               int64_t num_pages, int64_t page_size, int64_t max_pages_per_seq,
+               int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v, fa_dtype kv_dtype,
+               const float* k_descale, const float* v_descale,
+               void* workspace, size_t workspace_bytes_in,
+               const fa_mods* mods, void* stream) {
   g_err.clear();
   int rc = check_common(B, Hq, Hkv, d_qk, d_v);
   if (rc) return rc;
   if (kv_dtype != FA_BF16 && kv_dtype != FA_FP8_E4M3) return fail(FA_ERR_INVALID, "unknown kv_dtype %d", (int)kv_dtype);
+  if (vec && kv_dtype != FA_FP8_E4M3) return fail(FA_ERR_UNSUPPORTED, "vectorised pages hold FP8 E4M3 K/V only");
   if (total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_pages < 0 || max_pages_per_seq < 0)
     return fail(FA_ERR_INVALID, "sizes must be >= 0");
   if (max_seqlen_q > total_q) return fail(FA_ERR_INVALID, "max_seqlen_q exceeds total_q");
   if (page_size < 1 || page_size > 1024 || (page_size & (page_size - 1)))
     return fail(FA_ERR_UNSUPPORTED, "page_size must be a power of two in [1, 1024], got %lld", (long long)page_size);
+  if (vec && page_size < 16)
+    return fail(FA_ERR_UNSUPPORTED, "vectorised pages hold whole 16-key blocks: page_size >= 16, got %lld",
+                (long long)page_size);
   if (total_q >= kI32 || max_seqlen_k >= kI32 || num_pages >= kI32 || max_pages_per_seq >= kI32)
     return fail(FA_ERR_LIMIT, "token and page counts must stay below 2^31");
   if (B * max_pages_per_seq >= kI32) return fail(FA_ERR_LIMIT, "block_table extent exceeds 2^31");
@@ -392,7 +402,7 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* 
     d.win_left = (m.flags & FA_WINDOW) ? clamp_i32(m.wl) : -1;
     d.win_right = (m.flags & FA_WINDOW) ? clamp_i32(m.wr) : -1;
     bool supported = false;
-    hipError_t e = fa::decode_dispatch(pl, d, (int)d_qk, (int)d_v, fp8, st, &supported);
+    hipError_t e = fa::decode_dispatch(pl, d, (int)d_qk, (int)d_v, fp8, vec, st, &supported);
     if (!supported) return fail(FA_ERR_UNSUPPORTED, "no decode kernel for (%lld, %lld)", (long long)d_qk, (long long)d_v);
     if (e != hipSuccess) return fail(FA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
     fa::CombineArgs c{};
@@ -434,7 +444,37 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* 
   a.page_shift = shift;
   a.num_pages = (int)num_pages;
   fill_mods(a, m);
-  return launch_prefill(a, d_qk, d_v, fp8, true, 0, B, Hq, max_seqlen_q, st);
+  return launch_prefill(a, d_qk, d_v, fp8, true, vec, 0, B, Hq, max_seqlen_q, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                 const int32_t* cu_seqlens_q, const int32_t* seqlen_k, const int32_t* block_table,
+                 int64_t B, int64_t total_q, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                 int64_t num_pages, int64_t page_size, int64_t max_pages_per_seq,
+                 int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v, fa_dtype kv_dtype,
+                 const float* k_descale, const float* v_descale,
+                 void* workspace, size_t workspace_bytes_in,
+                 const fa_mods* mods, void* stream) {
+  return paged_impl(false, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, B, total_q,
+                    max_seqlen_q, max_seqlen_k, num_pages, page_size, max_pages_per_seq, Hq, Hkv, d_qk, d_v,
+                    kv_dtype, k_descale, v_descale, workspace, workspace_bytes_in, mods, stream);
+}
+
+int fa_fwd_paged_vec(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                     const int32_t* cu_seqlens_q, const int32_t* seqlen_k, const int32_t* block_table,
+                     int64_t B, int64_t total_q, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                     int64_t num_pages, int64_t page_size, int64_t max_pages_per_seq,
+                     int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v, fa_dtype kv_dtype,
+                     const float* k_descale, const float* v_descale,
+                     void* workspace, size_t workspace_bytes_in,
+                     const fa_mods* mods, void* stream) {
+  return paged_impl(true, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, B, total_q,
+                    max_seqlen_q, max_seqlen_k, num_pages, page_size, max_pages_per_seq, Hq, Hkv, d_qk, d_v,
+                    kv_dtype, k_descale, v_descale, workspace, workspace_bytes_in, mods, stream);
 }
 
 }  // extern "C"

@@ -48,6 +48,17 @@
 // Page lookups are bounded to the sequence's own pages and every byte offset
 // is 64-bit, so caches beyond 4 GiB are addressed correctly; keys past
 // seqlen_k are clamped for the load and removed by select before the softmax.
+//
+// Vectorised pages (the 5-D layout of the paged FP8 PR review: K page
+// [Hkv, D/16, page, 16], V page [Hkv, page/16, Dv, 16]) take the same LDS
+// K tile and a different V tile.  A K load instruction covers two 16-byte
+// columns c of the tile's 32 keys (lanes 0-31 column 2i, lanes 32-63 column
+// 2i+1; each half is 512 contiguous bytes) and is stored to the key-row
+// layout above.  A V load covers 64 head dims of one 16-key block (1 KB
+// contiguous): these are already V^T rows, so the tile is kept as V^T
+// [Dv][32 keys] with each row's keys in the order the P^T operand enumerates
+// them, and the A fragments are plain 8-byte reads.  Value bytes past the
+// sequence's end share a 16-byte load with live ones and are cleared.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -179,7 +190,7 @@ __global__ __launch_bounds__(256) void fa_decode_plan_kernel(const DecodePlanArg
 // worker that owns tile i of T in a split over W workers
 __device__ __forceinline__ int worker_of(int64_t i, int64_t T, int W) { return (int)(((i + 1) * W - 1) / T); }
 
-template <int DQK, int DV, int NRB, int NBUF>
+template <int DQK, int DV, int NRB, int NBUF, bool VEC>
 __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(NBUF >= 3 ? 1 : (NRB == 1 && NBUF == 1 ? 3 : 2))))
 void fa_decode_kernel(const DecodeArgs a) {
   static_assert(DQK % 32 == 0 && DV == 128 && (kDecKT * DQK) % 1024 == 0, "decode tile shapes");
@@ -205,8 +216,10 @@ void fa_decode_kernel(const DecodeArgs a) {
   int kst[T::kKLoads], vst[T::kVLoads];
 #pragma unroll
   for (int i = 0; i < T::kKLoads; ++i) {
-    const int off = i * 1024 + lane * 16, row = off / DQK;
-    kst[i] = row * DQK + ((((off % DQK) >> 4) ^ dec_kswz(row)) << 4);
+    const int off = i * 1024 + lane * 16;
+    const int row = VEC ? (lane & 31) : off / DQK;
+    const int c = VEC ? 2 * i + (lane >> 5) : (off % DQK) >> 4;
+    kst[i] = row * DQK + ((c ^ dec_kswz(row)) << 4);
   }
 #pragma unroll
   for (int n = 0; n < T::kVLoads; ++n) {
@@ -218,6 +231,14 @@ void fa_decode_kernel(const DecodeArgs a) {
   const int vrow = t8 < 4 ? 4 * kgrp + t8 : 16 + 4 * kgrp + (t8 - 4);
   const char FA_LDS* vrd = vlds + vrow * DV + vq * 8;
   const int vsw = dec_vswz(vrow);
+  // V^T tile (vectorised pages): row d is 32 bytes, byte 8 kgrp + e holds key
+  // (e / 4) * 16 + 4 kgrp + e % 4, so the lanes of key group kgrp read their
+  // 8 bytes of row 16 blk + lane%16 at 8-byte unit kgrp.  Rows 8-15 of every
+  // 16 swap unit pairs (0,1) <-> (2,3): the 16 rows x 2 units of a half
+  // wavefront then cover the 64 banks once.
+  const char FA_LDS* vtrd = vlds + (lane & 15) * 32 + ((kgrp ^ (((lane >> 3) & 1) << 1)) << 3);
+  const int vtst = lane * 32;                         // row d = lane (and 64 + lane)
+  const int vtsw = ((lane >> 3) & 1) << 4;            // 16-byte half swap of rows 8-15
   // K fragment reads: row kh*16 + lane%16 (the swizzle of r and r+16 agree),
   // chunk 2 st + kgrp/2, half kgrp%2
   const int krow = lane & 15, kx = dec_kswz(krow);
@@ -281,6 +302,33 @@ void fa_decode_kernel(const DecodeArgs a) {
     auto load_tile = [&](int t, KBuf& kb, VBuf& vb) {
       const int k0 = k_lo + t * kDecKT;
       const int nv = skv - k0;                          // rows of the tile inside the sequence
+      if (VEC) {
+        // the tile's two 16-key blocks: one page when pages hold 32 keys or
+        // more, else the pages of keys k0 and k0 + 16 (clamped to the sequence)
+        const int64_t p0 = min(max(load_uniform_i32(bt, k0 >> a.page_shift), 0), a.num_pages - 1);
+        const int64_t p1 = a.page_shift >= 5
+                               ? p0
+                               : min(max(load_uniform_i32(bt, (k0 + min(16, nv - 1)) >> a.page_shift), 0),
+                                     a.num_pages - 1);
+        // K: lane l of load i takes column 2i + l/32 of key row min(l%32, nv-1)
+        const int r = min(lane & 31, nv - 1);
+        const uint8_t* kp = kbase + (r >= 16 ? p1 : p0) * a.k_pg + ((k0 + r) & pmask) * 16 +
+                            ((lane >> 5) << (a.page_shift + 4));
+#pragma unroll
+        for (int i = 0; i < T::kKLoads; ++i)
+          kb[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(kp + ((2 * i) << (a.page_shift + 4))));
+        // V: load n takes dims 64 (n%2) + l of block n/2
+        const uint8_t* vt0 = vbase + p0 * a.v_pg + ((k0 & pmask) >> 4) * (DV * 16) + lane * 16;
+        const uint8_t* vt1 = vbase + p1 * a.v_pg + (((k0 + 16) & pmask) >> 4) * (DV * 16) + lane * 16;
+#pragma unroll
+        for (int n = 0; n < T::kVLoads; ++n)
+          vb[n] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>((n < 2 ? vt0 : vt1) + (n & 1) * 1024));
+        if (nv < kDecKT) {
+#pragma unroll
+          for (int n = 0; n < T::kVLoads; ++n) vb[n] = keep_bytes(vb[n], nv - 16 * (n >> 1));
+        }
+        return;
+      }
       if (a.page_shift < 5) {
         // pages smaller than a tile: each lane looks up the page of the key
         // row its 16 bytes belong to (a chunk never straddles a row)
@@ -359,8 +407,20 @@ void fa_decode_kernel(const DecodeArgs a) {
     auto step = [&](int t, KBuf& kb, VBuf& vb, bool refill) {
 #pragma unroll
       for (int i = 0; i < T::kKLoads; ++i) *reinterpret_cast<i32x4 FA_LDS*>(klds + kst[i]) = kb[i];
+      if (VEC) {
+        // row d = lane from loads 0 (block 0) and 2 (block 1), row 64 + lane
+        // from loads 1 and 3: dword j of block b goes to dword 2 j + b
 #pragma unroll
-      for (int n = 0; n < T::kVLoads; ++n) *reinterpret_cast<i32x4 FA_LDS*>(vlds + vst[n]) = vb[n];
+        for (int hr = 0; hr < 2; ++hr) {
+          const i32x4 b0 = vb[hr], b1 = vb[2 + hr];
+          char FA_LDS* row = vlds + vtst + hr * 64 * 32;
+          *reinterpret_cast<i32x4 FA_LDS*>(row + vtsw) = i32x4{b0[0], b1[0], b0[1], b1[1]};
+          *reinterpret_cast<i32x4 FA_LDS*>(row + (16 ^ vtsw)) = i32x4{b0[2], b1[2], b0[3], b1[3]};
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < T::kVLoads; ++n) *reinterpret_cast<i32x4 FA_LDS*>(vlds + vst[n]) = vb[n];
+      }
       if (refill) load_tile(min(t + NBUF, last), kb, vb);
 
       // ---- S^T = K Q^T ----  (fragment n = (kh, st); each read runs two
@@ -429,12 +489,16 @@ void fa_decode_kernel(const DecodeArgs a) {
       }
 
       // ---- O^T += V^T P^T ----  (same two-ahead chunking)
+      auto vread = [&](int d) {
+        if (VEC) return *reinterpret_cast<const i32x2 FA_LDS*>(vtrd + d * 16 * 32);
+        return lds_read_tr8(vrd + ((d ^ vsw) << 4));
+      };
       i32x2 vraw[kDB];
-      vraw[0] = lds_read_tr8(vrd + ((0 ^ vsw) << 4));
-      vraw[1] = lds_read_tr8(vrd + ((1 ^ vsw) << 4));
+      vraw[0] = vread(0);
+      vraw[1] = vread(1);
 #pragma unroll
       for (int d = 0; d < kDB; ++d) {
-        if (d + 2 < kDB) vraw[d + 2] = lds_read_tr8(vrd + (((d + 2) ^ vsw) << 4));
+        if (d + 2 < kDB) vraw[d + 2] = vread(d + 2);
         const bf16x8 vf = fp8x8_to_bf16(vraw[d]);
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) oacc[rb][d] = mfma16(vf, pf[rb], oacc[rb][d]);
@@ -561,7 +625,7 @@ __global__ __launch_bounds__(256) void fa_combine_kernel(const CombineArgs a) {
   if (lane == 0) a.lse[(int64_t)h * a.total_q + tok] = lse;
 }
 
-hipError_t decode_dispatch(const DecodePlanArgs& plan, const DecodeArgs& a, int dqk, int dv, bool fp8,
+hipError_t decode_dispatch(const DecodePlanArgs& plan, const DecodeArgs& a, int dqk, int dv, bool fp8, bool vec,
                            hipStream_t stream, bool* supported) {
   *supported = fp8 && dv == 128 && (dqk == 192 || dqk == 128);
   if (!*supported) return hipSuccess;
@@ -570,14 +634,16 @@ hipError_t decode_dispatch(const DecodePlanArgs& plan, const DecodeArgs& a, int 
   if (e != hipSuccess) return e;
   const dim3 grid((a.n_workers + kDecWaves - 1) / kDecWaves);
   const bool two = a.slot_rows > 16;
-#define FA_DEC(DQ)                                                                                       \
-  if (dqk == DQ) {                                                                                       \
-    if (two) hipLaunchKernelGGL((fa_decode_kernel<DQ, 128, 2, 1>), grid, dim3(kDecWaves * 64), 0, stream, a); \
-    else hipLaunchKernelGGL((fa_decode_kernel<DQ, 128, 1, 2>), grid, dim3(kDecWaves * 64), 0, stream, a);  \
-    return hipGetLastError();                                                                            \
+#define FA_DEC(DQ, VC)                                                                                       \
+  if (dqk == DQ && vec == VC) {                                                                              \
+    if (two) hipLaunchKernelGGL((fa_decode_kernel<DQ, 128, 2, 1, VC>), grid, dim3(kDecWaves * 64), 0, stream, a); \
+    else hipLaunchKernelGGL((fa_decode_kernel<DQ, 128, 1, 2, VC>), grid, dim3(kDecWaves * 64), 0, stream, a);  \
+    return hipGetLastError();                                                                                \
   }
-  FA_DEC(192)
-  FA_DEC(128)
+  FA_DEC(192, false)
+  FA_DEC(128, false)
+  FA_DEC(192, true)
+  FA_DEC(128, true)
 #undef FA_DEC
   *supported = false;
   return hipSuccess;

@@ -114,6 +114,21 @@ __device__ __forceinline__ void fp8x16_to_bf16(i32x4 w, bf16x8& lo, bf16x8& hi) 
   }
 }
 
+// w with its bytes k..15 cleared (k <= 0: all cleared; k >= 16: unchanged).
+// Cache bytes past a sequence's end that share a load with live bytes may
+// hold anything, NaN codes included; their scores are removed by select, but
+// a NaN value would survive the zero weight of its product, so such value
+// bytes are cleared before they reach a product.
+__device__ __forceinline__ i32x4 keep_bytes(i32x4 w, int k) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = k - 4 * j;
+    const unsigned m = n >= 4 ? 0xffffffffu : (n <= 0 ? 0u : (1u << (8 * n)) - 1u);
+    w[j] &= (int)m;
+  }
+  return w;
+}
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -11,7 +11,10 @@ constexpr int kModSoftcap = 2;
 
 // Strides are in elements.  Contiguous K/V: element (token t, kv-head g, d) at
 // t*k_st + g*k_sh + d.  Paged K/V: element (page p, kv-head g, slot s, d) at
-// p*k_pg + g*k_sh + s*k_st + d.
+// p*k_pg + g*k_sh + s*k_st + d.  Vectorised FP8 pages (kernels built with the
+// vec flag): the (p, g) block starts at p*k_pg + g*k_sh as well, and inside
+// it K byte (s, d) sits at (d/16)*page*16 + s*16 + d%16 and V byte (s, d) at
+// (s/16)*Dv*16 + d*16 + s%16; k_st / v_st are not used.
 struct PrefillArgs {
   const __bf16* q;
   const void* k;
@@ -93,9 +96,9 @@ struct CombineArgs {
   int n_workers, slot_rows;
 };
 
-hipError_t prefill_dispatch(const PrefillArgs& a, int dqk, int dv, bool fp8, bool paged, int mods,
+hipError_t prefill_dispatch(const PrefillArgs& a, int dqk, int dv, bool fp8, bool paged, bool vec, int mods,
                             int n_bh, int n_qtiles, hipStream_t stream, bool* supported);
-hipError_t decode_dispatch(const DecodePlanArgs& plan, const DecodeArgs& a, int dqk, int dv, bool fp8,
+hipError_t decode_dispatch(const DecodePlanArgs& plan, const DecodeArgs& a, int dqk, int dv, bool fp8, bool vec,
                            hipStream_t stream, bool* supported);
 hipError_t combine_dispatch(const CombineArgs& a, int dv, hipStream_t stream, bool* supported);
 

@@ -164,6 +164,120 @@ struct Fp8Stager {
   }
 };
 
+// Vectorised FP8 pages (paged FP8 PR review: K page [Hkv, D/16, page, 16],
+// V page [Hkv, page/16, Dv, 16]).  The (page, kv-head) block starts at
+// page*pg + g*sh; page_shift >= 4.
+
+// K: item idx is 16-byte column f = idx / 64 of tile row r = idx % 64, so one
+// wavefront's load covers 64 keys of one column: 1 KB contiguous when the
+// tile sits in one page.  Stored to the same swizzled key rows as above.
+template <int D>
+struct Fp8VecK {
+  static constexpr int kItems = BN * D / 16;
+  static constexpr int kPer = (kItems + NTHREADS - 1) / NTHREADS;
+  static constexpr int kRow = D * 2;
+  static_assert(kItems % NTHREADS == 0, "whole K items per thread");
+  i32x4 w[kPer];
+  int off[kPer];
+  __device__ __forceinline__ void init(int page_shift, int tid) {
+#pragma unroll
+    for (int it = 0; it < kPer; ++it) {
+      const int idx = it * NTHREADS + tid;
+      off[it] = ((idx / BN) << (page_shift + 4)) + (idx % BN) * 16;
+    }
+  }
+  __device__ __forceinline__ void load(const PrefillArgs& a, const SeqView& sv, const uint8_t* base, int k0,
+                                       bool fast, int tid) {
+    const int pmask = (1 << a.page_shift) - 1;
+    if (fast) {
+      int page = load_uniform_i32(a.block_table, (int64_t)sv.b * a.max_pages + (k0 >> a.page_shift));
+      page = min(max(page, 0), a.num_pages - 1);
+      const uint8_t* tb = base + (int64_t)page * a.k_pg + (int64_t)sv.g * a.k_sh + (k0 & pmask) * 16;
+#pragma unroll
+      for (int it = 0; it < kPer; ++it) w[it] = *reinterpret_cast<const i32x4*>(tb + off[it]);
+    } else {
+#pragma unroll
+      for (int it = 0; it < kPer; ++it) {
+        const int idx = it * NTHREADS + tid;
+        const int j = min(k0 + idx % BN, sv.skv - 1);
+        int page = a.block_table[(int64_t)sv.b * a.max_pages + (j >> a.page_shift)];
+        page = min(max(page, 0), a.num_pages - 1);
+        w[it] = *reinterpret_cast<const i32x4*>(base + (int64_t)page * a.k_pg + (int64_t)sv.g * a.k_sh +
+                                                ((idx / BN) << (a.page_shift + 4)) + (j & pmask) * 16);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(char FA_LDS* tile, int tid) const {
+#pragma unroll
+    for (int it = 0; it < kPer; ++it) {
+      const int idx = it * NTHREADS + tid;
+      const int r = idx % BN, f = idx / BN;
+      bf16x8 lo, hi;
+      fp8x16_to_bf16(w[it], lo, hi);
+      char FA_LDS* rowp = tile + r * kRow;
+      *reinterpret_cast<bf16x8 FA_LDS*>(rowp + (((2 * f) ^ swz<kRow>(r)) << 4)) = lo;
+      *reinterpret_cast<bf16x8 FA_LDS*>(rowp + (((2 * f + 1) ^ swz<kRow>(r)) << 4)) = hi;
+    }
+  }
+};
+
+// V: item idx is head dim d = idx % D of 16-key block sb = idx / D (16 bytes,
+// one dim of 16 keys), so one wavefront's load covers 64 dims of one block.
+// The tile is kept as V^T: row d holds the tile's 64 keys in bf16 (128
+// bytes), each 16-key group in the order the P^T operand enumerates them
+// (position p holds key p with bits 2 and 3 swapped), so a lane's A fragment
+// is one 16-byte read.  Chunk c of row d is stored at c ^ ((d >> 1) & 7):
+// the 16 rows that 16 lanes read at one chunk then fall in distinct bank
+// quarters.  Value bytes past the sequence's end are cleared.
+template <int D>
+struct Fp8VecV {
+  static constexpr int kItems = (BN / 16) * D;
+  static constexpr int kPer = (kItems + NTHREADS - 1) / NTHREADS;
+  static constexpr int kRow = BN * 2;
+  static_assert(kItems % NTHREADS == 0, "whole V items per thread");
+  i32x4 w[kPer];
+  __device__ __forceinline__ void load(const PrefillArgs& a, const SeqView& sv, const uint8_t* base, int k0,
+                                       bool fast, int tid) {
+    const int pmask = (1 << a.page_shift) - 1;
+    if (fast) {
+      int page = load_uniform_i32(a.block_table, (int64_t)sv.b * a.max_pages + (k0 >> a.page_shift));
+      page = min(max(page, 0), a.num_pages - 1);
+      const uint8_t* tb =
+          base + (int64_t)page * a.v_pg + (int64_t)sv.g * a.v_sh + ((k0 & pmask) >> 4) * (D * 16);
+#pragma unroll
+      for (int it = 0; it < kPer; ++it) w[it] = *reinterpret_cast<const i32x4*>(tb + (it * NTHREADS + tid) * 16);
+    } else {
+#pragma unroll
+      for (int it = 0; it < kPer; ++it) {
+        const int idx = it * NTHREADS + tid;
+        const int j = k0 + (idx / D) * 16;               // first key of the block
+        const int jc = min(j, sv.skv - 1);
+        int page = a.block_table[(int64_t)sv.b * a.max_pages + (jc >> a.page_shift)];
+        page = min(max(page, 0), a.num_pages - 1);
+        const i32x4 x = *reinterpret_cast<const i32x4*>(base + (int64_t)page * a.v_pg + (int64_t)sv.g * a.v_sh +
+                                                        ((jc & pmask) >> 4) * (D * 16) + (idx % D) * 16);
+        w[it] = keep_bytes(x, sv.skv - j);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(char FA_LDS* tile, int tid) const {
+#pragma unroll
+    for (int it = 0; it < kPer; ++it) {
+      const int idx = it * NTHREADS + tid;
+      const int d = idx % D, sb = idx / D;
+      bf16x8 lo, hi;
+      fp8x16_to_bf16(w[it], lo, hi);
+      // keys 0-3, 8-11 | 4-7, 12-15 of the block
+      const bf16x8 c0 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const bf16x8 c1 = {lo[4], lo[5], lo[6], lo[7], hi[4], hi[5], hi[6], hi[7]};
+      char FA_LDS* rowp = tile + d * kRow;
+      const int sw = (d >> 1) & 7;
+      *reinterpret_cast<bf16x8 FA_LDS*>(rowp + (((2 * sb) ^ sw) << 4)) = c0;
+      *reinterpret_cast<bf16x8 FA_LDS*>(rowp + (((2 * sb + 1) ^ sw) << 4)) = c1;
+    }
+  }
+};
+
 // Active-tile bits of the block-mask rows that a workgroup spans (one per
 // 128-query half), 64 mask key-blocks at a time: one vector load and a ballot
 // per row and 64 blocks; the per-tile tests are scalar.  tile_bits(t) has bit
@@ -201,9 +315,10 @@ struct MaskBits {
   }
 };
 
-template <int DQK, int DV, bool FP8, bool PAGED, int MODS>
+template <int DQK, int DV, bool FP8, bool PAGED, bool VEC, int MODS>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_prefill_kernel(const PrefillArgs a) {
+  static_assert(!VEC || (FP8 && PAGED), "vectorised pages hold FP8 K/V");
   using T = PrefillTraits<DQK, DV, FP8>;
   __shared__ __attribute__((aligned(1024))) char lds_raw[T::kLds];
   char FA_LDS* lds = (char FA_LDS*)(lds_raw);
@@ -323,8 +438,12 @@ void fa_prefill_kernel(const PrefillArgs a) {
   Bf16Stager<DV, PAGED> vdma;
   Fp8Stager<DQK, PAGED> k8;
   Fp8Stager<DV, PAGED> v8;
+  Fp8VecK<DQK> kv8;
+  Fp8VecV<DV> vv8;
   constexpr int kDmaPerTile = Bf16Stager<DQK, PAGED>::kPerWave + Bf16Stager<DV, PAGED>::kPerWave;
-  if (FP8) {
+  if (VEC) {
+    kv8.init(a.page_shift, tid);
+  } else if (FP8) {
     k8.init(a.k_st, tid);
     v8.init(a.v_st, tid);
   } else {
@@ -336,7 +455,10 @@ void fa_prefill_kernel(const PrefillArgs a) {
   auto issue = [&](int t, char FA_LDS* st) {
     const int k0 = t * BN;
     const bool fast = fast_tile(k0);
-    if (FP8) {
+    if (VEC) {
+      kv8.load(a, sv, reinterpret_cast<const uint8_t*>(a.k), k0, fast, tid);
+      vv8.load(a, sv, reinterpret_cast<const uint8_t*>(a.v), k0, fast, tid);
+    } else if (FP8) {
       k8.load(a, sv, reinterpret_cast<const uint8_t*>(a.k), a.k_st, a.k_sh, kpg, k0, fast, tid);
       v8.load(a, sv, reinterpret_cast<const uint8_t*>(a.v), a.v_st, a.v_sh, vpg, k0, fast, tid);
     } else {
@@ -346,8 +468,13 @@ void fa_prefill_kernel(const PrefillArgs a) {
     }
   };
   auto fp8_store = [&](char FA_LDS* st) {
-    k8.store(st, tid);
-    v8.store(st + T::kTileK, tid);
+    if (VEC) {
+      kv8.store(st, tid);
+      vv8.store(st + T::kTileK, tid);
+    } else {
+      k8.store(st, tid);
+      v8.store(st + T::kTileK, tid);
+    }
   };
 
   // Tile pipeline: t (computed now, stage sc), t1 and t2 (the next two
@@ -473,7 +600,17 @@ void fa_prefill_kernel(const PrefillArgs a) {
       }
 
       // ---------------- O^T += V^T P^T ----------------
-      {
+      if (VEC) {
+        // V^T tile: row d = 32 blk + lane%32, chunk 2u + lane/32
+        const char FA_LDS* vt = cur + T::kTileK + (lane & 31) * (BN * 2);
+        const int sw = ((lane & 31) >> 1) & 7;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = ((2 * u + (lane >> 5)) ^ sw) << 4;
+#pragma unroll
+          for (int d = 0; d < DV / 32; ++d) oacc[d] = mfma32(lds_read_b128(vt + d * 32 * (BN * 2) + c), pf[u], oacc[d]);
+        }
+      } else {
         const char FA_LDS* vt = cur + T::kTileK;
         const int grp = lane >> 4, i16 = lane & 15;
         const int hsel = grp >> 1;
@@ -546,30 +683,34 @@ void fa_prefill_kernel(const PrefillArgs a) {
   }
 }
 
-template <int DQK, int DV, bool FP8, bool PAGED, int MODS>
+template <int DQK, int DV, bool FP8, bool PAGED, bool VEC, int MODS>
 static hipError_t launch_prefill(const PrefillArgs& a, int n_bh, int n_qtiles, hipStream_t stream) {
   dim3 grid((n_bh + 7) / 8 * 8, n_qtiles);
-  hipLaunchKernelGGL((fa_prefill_kernel<DQK, DV, FP8, PAGED, MODS>), grid, dim3(NTHREADS), 0, stream, a);
+  hipLaunchKernelGGL((fa_prefill_kernel<DQK, DV, FP8, PAGED, VEC, MODS>), grid, dim3(NTHREADS), 0, stream, a);
   return hipGetLastError();
 }
 
 // Instantiated shapes: (D_qk, D_v) in {(64,64), (128,128)} for bf16 K/V
 // (dense, varlen, paged) with every score-mod combination; (192,128) and
-// (128,128) for FP8 E4M3 paged caches without score mods.
-hipError_t prefill_dispatch(const PrefillArgs& a, int dqk, int dv, bool fp8, bool paged, int mods,
+// (128,128) for FP8 E4M3 paged caches without score mods, head-major or
+// vectorised pages.
+hipError_t prefill_dispatch(const PrefillArgs& a, int dqk, int dv, bool fp8, bool paged, bool vec, int mods,
                             int n_bh, int n_qtiles, hipStream_t stream, bool* supported) {
   *supported = true;
-#define FA_CASE(DQ, DVV, F8, PG, MD)                                                     \
-  if (dqk == DQ && dv == DVV && fp8 == F8 && paged == PG && mods == MD)                  \
-    return launch_prefill<DQ, DVV, F8, PG, MD>(a, n_bh, n_qtiles, stream);
-#define FA_MODS4(DQ, DVV, F8, PG) \
-  FA_CASE(DQ, DVV, F8, PG, 0) FA_CASE(DQ, DVV, F8, PG, 1) FA_CASE(DQ, DVV, F8, PG, 2) FA_CASE(DQ, DVV, F8, PG, 3)
+#define FA_CASE(DQ, DVV, F8, PG, VC, MD)                                                       \
+  if (dqk == DQ && dv == DVV && fp8 == F8 && paged == PG && vec == VC && mods == MD)           \
+    return launch_prefill<DQ, DVV, F8, PG, VC, MD>(a, n_bh, n_qtiles, stream);
+#define FA_MODS4(DQ, DVV, F8, PG)                                                          \
+  FA_CASE(DQ, DVV, F8, PG, false, 0) FA_CASE(DQ, DVV, F8, PG, false, 1)                    \
+  FA_CASE(DQ, DVV, F8, PG, false, 2) FA_CASE(DQ, DVV, F8, PG, false, 3)
   FA_MODS4(64, 64, false, false)
   FA_MODS4(128, 128, false, false)
-  FA_CASE(128, 128, false, true, 0)
-  FA_CASE(64, 64, false, true, 0)
-  FA_CASE(192, 128, true, true, 0)
-  FA_CASE(128, 128, true, true, 0)
+  FA_CASE(128, 128, false, true, false, 0)
+  FA_CASE(64, 64, false, true, false, 0)
+  FA_CASE(192, 128, true, true, false, 0)
+  FA_CASE(128, 128, true, true, false, 0)
+  FA_CASE(192, 128, true, true, true, 0)
+  FA_CASE(128, 128, true, true, true, 0)
 #undef FA_MODS4
 #undef FA_CASE
   *supported = false;

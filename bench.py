@@ -10,12 +10,15 @@ before timing starts.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
                   [--flex alibi|softcap|window|bernoulli|block_causal|none|causal] [--page-size P]
+                  [--layout head_major|vec]
                   [--no-cpu-baseline]
                   [--copy-calibration]
   python bench.py --config N --traffic-from FETCH_CSV WRITE_CSV
 
 --config selects another workload for investigation (1 dense D64, 3 paged
 FP8 prefill, 4 paged FP8 decode, 5 flex); the default line is config 2.
+--layout vec runs configs 3 and 4 on the vectorised 5-D page format
+(fa_fwd_paged_vec) instead of head-major pages.
 Prints ONE JSON line.
 """
 from __future__ import annotations
@@ -112,7 +115,7 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, key: str, kind: str) -
     return entry
 
 
-def build_workload(cfg: int, flex: str, torch, synth, fa, page_size: int = 64):
+def build_workload(cfg: int, flex: str, torch, synth, fa, page_size: int = 64, layout: str = "head_major"):
     """Returns (name, run_fn, work dict, oracle sample fn)."""
     dev = "cuda"
     if cfg == 1:
@@ -148,20 +151,27 @@ def build_workload(cfg: int, flex: str, torch, synth, fa, page_size: int = 64):
     if cfg == 3:
         L = [2048] * 4
         d = synth.make_paged(L, L, 16, 16, 192, 128, page_size=64, seed=synth.seed_for(3), device=dev)
+        if layout == "vec":
+            d = synth.to_vectorized(d)
+        fn = fa.fa_fwd_paged_vec if layout == "vec" else fa.fa_fwd_paged
         o = torch.empty(8192, 16, 128, dtype=torch.bfloat16, device=dev)
         lse = torch.empty(16, 8192, dtype=torch.float32, device=dev)
         mods = fa.Mods(causal=True)
         flops = 64 * 2048 * 2049 // 2 * (2 * 192 + 2 * 128)
-        run = lambda: fa.fa_fwd_paged(d["q"], d["k_cache"], d["v_cache"], o, lse, d["cu_q"], d["seqlen_k"],
-                                      d["block_table"], 2048, 2048, d["k_descale"], d["v_descale"], None, mods)
-        name = "paged FP8 causal prefill 4x2048 H16 Dqk192 Dv128 page64"
+        run = lambda: fn(d["q"], d["k_cache"], d["v_cache"], o, lse, d["cu_q"], d["seqlen_k"],
+                         d["block_table"], 2048, 2048, d["k_descale"], d["v_descale"], None, mods)
+        name = "paged FP8 causal prefill 4x2048 H16 Dqk192 Dv128 page64" + (" vectorised" if layout == "vec" else "")
         return name, run, dict(flops=flops, kind="prefill", bound="mfma"), \
-            {"B": 4, "S": 2048, "H": 16, "d_qk": 192, "d_v": 128, "page_size": 64}, None
+            {"B": 4, "S": 2048, "H": 16, "d_qk": 192, "d_v": 128, "page_size": 64, "layout": layout}, None
     if cfg == 4:
         lk = synth.make_decode_lengths(synth.seed_for(4))
         lq = [1] * 64
         ps = page_size
         d = synth.make_paged(lq, lk, 64, 8, 192, 128, page_size=ps, seed=synth.seed_for(4), device=dev)
+        if layout == "vec":
+            d = synth.to_vectorized(d)
+            torch.cuda.empty_cache()
+        fn = fa.fa_fwd_paged_vec if layout == "vec" else fa.fa_fwd_paged
         o = torch.empty(64, 64, 128, dtype=torch.bfloat16, device=dev)
         lse = torch.empty(64, 64, dtype=torch.float32, device=dev)
         n = fa.fa_fwd_paged_workspace_size(64, 64, 1, max(lk), 64, 8, 192, 128, ps)
@@ -170,9 +180,10 @@ def build_workload(cfg: int, flex: str, torch, synth, fa, page_size: int = 64):
         kv_bytes = sum(lk) * 8 * (192 + 128)
         io_bytes = 64 * 64 * 192 * 2 + 64 * 64 * 128 * 2 + 64 * 64 * 4 + sum(math.ceil(x / ps) for x in lk) * 4
         flops = sum(lk) * 64 * (2 * 192 + 2 * 128)
-        run = lambda: fa.fa_fwd_paged(d["q"], d["k_cache"], d["v_cache"], o, lse, d["cu_q"], d["seqlen_k"],
-                                      d["block_table"], 1, max(lk), d["k_descale"], d["v_descale"], ws, mods)
-        name = f"paged FP8 decode 64 seqs ctx U[1024,32768] GQA 64/8 Dqk192 Dv128 page{ps}"
+        run = lambda: fn(d["q"], d["k_cache"], d["v_cache"], o, lse, d["cu_q"], d["seqlen_k"],
+                         d["block_table"], 1, max(lk), d["k_descale"], d["v_descale"], ws, mods)
+        name = f"paged FP8 decode 64 seqs ctx U[1024,32768] GQA 64/8 Dqk192 Dv128 page{ps}" + \
+            (" vectorised" if layout == "vec" else "")
 
         def sample():
             import oracle
@@ -191,12 +202,14 @@ def build_workload(cfg: int, flex: str, torch, synth, fa, page_size: int = 64):
             cu = torch.arange(n_seq + 1).numpy()
             kd, vd = float(d["k_descale"]), float(d["v_descale"])
             dt, reps = _timed_reps(lambda: oracle.attention_paged(qh, kc, vc, cu, lk[:n_seq], cbt.numpy(),
-                                                                  dict(causal=True), kd, vd, workers=_cores()))
+                                                                  dict(causal=True), kd, vd, workers=_cores(),
+                                                                  layout="vectorized" if layout == "vec"
+                                                                  else "head_major"))
             sbytes = sum(lk[:n_seq]) * 8 * (192 + 128)
             return dict(seconds=dt, work=sbytes * reps,
                         sample=f"sequences 0-{n_seq - 1} ({sum(lk[:n_seq])} cached tokens, all heads), {reps} passes")
         return name, run, dict(flops=flops, bytes=kv_bytes + io_bytes, kind="decode", bound="hbm"), \
-            {"B": 64, "ctx_total": sum(lk), "Hq": 64, "Hkv": 8, "page_size": ps}, sample
+            {"B": 64, "ctx_total": sum(lk), "Hq": 64, "Hkv": 8, "page_size": ps, "layout": layout}, sample
     if cfg == 5:
         B, H, S, D = 2, 16, 8192, 128
         d = synth.make_dense(B, S, S, H, H, D, D, seed=synth.seed_for(5), device=dev)
@@ -261,6 +274,8 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--flex", default="alibi")
     ap.add_argument("--page-size", type=int, default=64, help="decode config: cache page size (power of two)")
+    ap.add_argument("--layout", choices=["head_major", "vec"], default="head_major",
+                    help="paged configs: head-major or vectorised 5-D pages")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (reference for HBM byte counters)")
@@ -270,6 +285,8 @@ def main():
     key = f"config{args.config}" + (f"_{args.flex}" if args.config == 5 else "")
     if args.config == 4 and args.page_size != 64:
         key += f"_ps{args.page_size}"
+    if args.config in (3, 4) and args.layout == "vec":
+        key += "_vec"
     if args.traffic_from:
         kind = "decode" if args.config == 4 else "prefill"
         print(json.dumps({key: traffic_from_counters(args.traffic_from[0], args.traffic_from[1], key, kind)}))
@@ -284,7 +301,8 @@ def main():
     import attention_fa_fwd_03_amd as fa
 
     torch.cuda.init()
-    name, run, work, cfg_extra, sample = build_workload(args.config, args.flex, torch, synth, fa, args.page_size)
+    name, run, work, cfg_extra, sample = build_workload(args.config, args.flex, torch, synth, fa, args.page_size,
+                                                       args.layout)
     if args.copy_calibration:
         # reference for the HBM byte counters: one device-to-device copy of
         # COPY_BYTES through the HIP runtime's own copy kernel

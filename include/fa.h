@@ -139,7 +139,32 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* 
                  void* workspace, size_t workspace_bytes,
                  const fa_mods* mods, void* stream);
 
-/* Workspace bytes fa_fwd_paged needs for these sizes (0 when it needs none). */
+/*
+ * Paged KV cache in the vectorised 5-D page format (review of "Support paged
+ * FP8 Flash attention with asymmetric K/V head dim on gfx950", which gives
+ * the two cache shapes and the permutes that take them back to token-major):
+ *   K [num_pages, Hkv, d_qk / 16, page_size, 16]  byte (page, g, c, s, x) is
+ *     element d = 16 c + x of key slot s;
+ *   V [num_pages, Hkv, page_size / 16, d_v, 16]   byte (page, g, j, d, x) is
+ *     element d of key slot 16 j + x.
+ * Elements are FP8 E4M3 only (kv_dtype must be FA_FP8_E4M3; FA_BF16 gives
+ * FA_ERR_UNSUPPORTED), page_size a power of two in [16, 1024].  Every other
+ * argument, the built head dims, the mods, the workspace (same size rule:
+ * fa_fwd_paged_workspace_size) and the error behaviour are those of
+ * fa_fwd_paged, and for the same logical cache the result is bitwise the one
+ * fa_fwd_paged gives with head-major pages.
+ */
+int fa_fwd_paged_vec(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                     const int32_t* cu_seqlens_q, const int32_t* seqlen_k, const int32_t* block_table,
+                     int64_t B, int64_t total_q, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                     int64_t num_pages, int64_t page_size, int64_t max_pages_per_seq,
+                     int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v, fa_dtype kv_dtype,
+                     const float* k_descale, const float* v_descale,
+                     void* workspace, size_t workspace_bytes,
+                     const fa_mods* mods, void* stream);
+
+/* Workspace bytes fa_fwd_paged and fa_fwd_paged_vec need for these sizes (0
+ * when they need none). */
 size_t fa_fwd_paged_workspace_size(int64_t B, int64_t total_q, int64_t max_seqlen_q,
                                    int64_t max_seqlen_k, int64_t Hq, int64_t Hkv, int64_t d_qk,
                                    int64_t d_v, int64_t page_size, fa_dtype kv_dtype);

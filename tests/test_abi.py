@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ["fa_fwd_dense", "fa_fwd_varlen", "fa_fwd_paged", "fa_fwd_paged_workspace_size",
+    for n in ["fa_fwd_dense", "fa_fwd_varlen", "fa_fwd_paged", "fa_fwd_paged_vec", "fa_fwd_paged_workspace_size",
               "fa_last_error", "fa_abi_version"]:
         assert n in names
 
@@ -107,15 +107,16 @@ def test_mods_validation():
     assert rc == -1 and "unknown" in msg
 
 
-def _paged(**kw):
+def _paged(vec=False, **kw):
     fa = _lib()
     a = dict(q=FAKE, kc=FAKE * 2, vc=FAKE * 3, o=FAKE * 4, lse=FAKE * 5, cu=FAKE * 6, sk=FAKE * 7, bt=FAKE * 8,
              B=2, Tq=2, msq=1, msk=100, P=10, ps=64, mp=2, Hq=16, Hkv=2, dqk=192, dv=128, kv=1,
              kd=FAKE * 9, vd=FAKE * 10, ws=FAKE * 64, wsb=1 << 30, mods=None)
     a.update(kw)
-    rc = fa.lib.fa_fwd_paged(a["q"], a["kc"], a["vc"], a["o"], a["lse"], a["cu"], a["sk"], a["bt"], a["B"], a["Tq"],
-                             a["msq"], a["msk"], a["P"], a["ps"], a["mp"], a["Hq"], a["Hkv"], a["dqk"], a["dv"],
-                             a["kv"], a["kd"], a["vd"], a["ws"], a["wsb"], a["mods"], None)
+    fn = fa.lib.fa_fwd_paged_vec if vec else fa.lib.fa_fwd_paged
+    rc = fn(a["q"], a["kc"], a["vc"], a["o"], a["lse"], a["cu"], a["sk"], a["bt"], a["B"], a["Tq"],
+            a["msq"], a["msk"], a["P"], a["ps"], a["mp"], a["Hq"], a["Hkv"], a["dqk"], a["dv"],
+            a["kv"], a["kd"], a["vd"], a["ws"], a["wsb"], a["mods"], None)
     return rc, fa.fa_last_error()
 
 
@@ -134,6 +135,22 @@ def _paged(**kw):
 ])
 def test_paged_rejects(kw, code, frag):
     rc, msg = _paged(**kw)
+    assert rc == code and frag in msg, (rc, msg)
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(kv=0), -2, "FP8"),
+    (dict(ps=8, mp=16), -2, "page_size >= 16"),
+    (dict(ps=1, mp=128), -2, "page_size >= 16"),
+    (dict(ps=48), -2, "power of two"),
+    (dict(mp=1), -1, "max_pages_per_seq"),
+    (dict(ws=0), -4, "workspace"),
+    (dict(dqk=256, dv=256, msq=100, Tq=200), -2, "not built"),
+])
+def test_paged_vec_rejects(kw, code, frag):
+    """The vectorised format holds FP8 whole 16-key blocks; every other check
+    is the head-major entry point's."""
+    rc, msg = _paged(vec=True, **kw)
     assert rc == code and frag in msg, (rc, msg)
 
 

@@ -277,6 +277,63 @@ def test_paged_full_prefill_sampled():
     compare(og, lg, o_ref, l_ref, TOL_O_FP8, what="paged full")
 
 
+# ----------------------------------------------------------------------------- vectorised pages
+def _paged_vec_run(d, mods_kw, Dv):
+    """fa_fwd_paged_vec over the vectorised copy of a make_paged() cache."""
+    e = synth.to_vectorized(d)
+    q = d["q"].to(DEV)
+    kc, vc = e["k_cache"].to(DEV), e["v_cache"].to(DEV)
+    Tq, Hq, Dqk = q.shape
+    P, Hkv, _, ps, _ = kc.shape
+    B = len(d["lengths_k"])
+    msq, msk = max(d["lengths_q"]), max(d["lengths_k"])
+    o = _nan_like((Tq, Hq, Dv), torch.bfloat16)
+    lse = _nan_like((Hq, Tq), torch.float32)
+    n = fa.fa_fwd_paged_workspace_size(B, Tq, msq, msk, Hq, Hkv, Dqk, Dv, ps, fa.FA_FP8_E4M3)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+    fa.fa_fwd_paged_vec(q, kc, vc, o, lse, d["cu_q"].to(DEV), d["seqlen_k"].to(DEV), d["block_table"].to(DEV),
+                        msq, msk, d["k_descale"].to(DEV), d["v_descale"].to(DEV), ws, fa.Mods(**mods_kw))
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# (lengths_q, lengths_k, Hq, Hkv, Dqk, mods): prefill, chunked prefill with
+# GQA, decode with one row block, decode with two row blocks and a window
+VEC_CASES = {
+    "prefill": ([70, 3, 128, 129, 600], [70, 3, 128, 129, 600], 4, 4, 192, dict(causal=True)),
+    "chunked": ([40, 64, 100], [300, 64, 1000], 4, 2, 128, dict(causal=True)),
+    "decode": ([1] * 8, [1, 31, 32, 33, 64, 1000, 3000, 257], 16, 2, 192, dict(causal=True)),
+    "decode2rb": ([2, 1, 2, 2, 2, 2, 0, 2], [0, 1, 2, 33, 500, 2100, 64, 5000], 32, 2, 192,
+                  dict(causal=True, window=(100, 0))),
+}
+
+
+@pytest.mark.parametrize("ps", [16, 32, 64, 1024])
+@pytest.mark.parametrize("case", sorted(VEC_CASES))
+def test_paged_vec_is_bitwise_head_major(case, ps):
+    """The vectorised page format gives bitwise the head-major result for the
+    same logical cache (unused pages and bytes past seqlen_k hold NaN codes
+    in both: value bytes that share a load with live ones are cleared)."""
+    lq, lk, Hq, Hkv, Dqk, mods_kw = VEC_CASES[case]
+    d = synth.make_paged(lq, lk, Hq, Hkv, Dqk, 128, page_size=ps, seed=171 + ps, extra_pages=5)
+    o1, l1 = _paged_run(d, mods_kw, 128)
+    o2, l2 = _paged_vec_run(d, mods_kw, 128)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), f"{case} ps{ps}"
+
+
+@pytest.mark.parametrize("case,ps", [("decode", 16), ("prefill", 64), ("chunked", 1024)])
+def test_paged_vec_matches_oracle(case, ps):
+    """Oracle parity with the oracle reading the vectorised pages itself."""
+    lq, lk, Hq, Hkv, Dqk, mods_kw = VEC_CASES[case]
+    d = synth.make_paged(lq, lk, Hq, Hkv, Dqk, 128, page_size=ps, seed=191 + ps, extra_pages=2)
+    o, lse = _paged_vec_run(d, mods_kw, 128)
+    e = synth.to_vectorized(d)
+    o_ref, l_ref = oracle.attention_paged(f64(d["q"]), f64(e["k_cache"]), f64(e["v_cache"]), d["cu_q"],
+                                          d["seqlen_k"], d["block_table"], dict(mods_kw),
+                                          float(d["k_descale"]), float(d["v_descale"]), layout="vectorized")
+    compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_FP8, what=f"vec {case} ps{ps}")
+
+
 # ----------------------------------------------------------------------------- decode
 @pytest.mark.parametrize("Hq,Hkv,Dqk,sq", [(16, 2, 192, 1), (8, 8, 128, 1), (16, 2, 192, 4), (64, 8, 192, 1)])
 def test_decode_small(Hq, Hkv, Dqk, sq):
