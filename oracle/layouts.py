@@ -13,7 +13,10 @@ Layouts (readings of the pages, see the package docstring):
             head-major caches K [P,Hkv,page_size,Dqk], V [P,Hkv,page_size,Dv],
             or in the vectorized 5-D caches K [P,Hkv,Dqk/x,page_size,x],
             V [P,Hkv,page_size/x,Dv,x] (see gather_paged); seqlen_k[b] keys;
-            FP8 caches hold OCP E4M3 codes scaled by a per-tensor descale.
+            FP8 caches hold OCP E4M3 codes scaled by a per-tensor descale;
+            Q may be OCP E4M3 codes too (uint8) with its own descale
+            ("Support paged FP8 Flash attention with asymmetric K/V head dim
+            on gfx950", PR description: E4M3 Q/K/V with scalar descales).
   * GQA     q-head h reads kv-head h // (Hq / Hkv) (consecutive q-heads share
             a kv-head; the pages are silent, Hkv = 1 there).
   * scale   default 1/sqrt(Dqk) (RL-Kernel PR: default softmax scale).
@@ -154,6 +157,19 @@ def varlen_rows(q, k, v, cu_q, cu_k, picks, mods=None):
     return o, lse
 
 
+def paged_queries(q, q_descale=None):
+    """Query values of a paged call: bf16 values as they are, or E4M3 codes
+    (uint8) decoded and multiplied by the per-tensor q_descale."""
+    q = np.asarray(q)
+    if q.dtype == np.uint8:
+        if q_descale is None:
+            raise ValueError("E4M3 queries need q_descale")
+        return decode_e4m3(q) * float(q_descale)
+    if q_descale is not None:
+        raise ValueError("q_descale applies to E4M3 queries only")
+    return _f64(q)
+
+
 def gather_paged(cache, block_row, length, g, descale=None, layout="head_major", kind="k"):
     """Token-major [length, D] float64 rows of kv-head g for one sequence.
 
@@ -197,10 +213,11 @@ def gather_paged(cache, block_row, length, g, descale=None, layout="head_major",
 
 
 def attention_paged(q, k_cache, v_cache, cu_q, seqlen_k, block_table, mods=None,
-                    k_descale=None, v_descale=None, workers=1, layout="head_major"):
-    """Paged-KV attention over either page layout (see gather_paged).
+                    k_descale=None, v_descale=None, workers=1, layout="head_major", q_descale=None):
+    """Paged-KV attention over either page layout (see gather_paged), with
+    bf16 or E4M3 queries (see paged_queries).
     Returns (O [Tq,Hq,Dv], LSE [Hq,Tq]) in float64."""
-    q = _f64(q)
+    q = paged_queries(q, q_descale)
     cu_q = np.asarray(cu_q, dtype=np.int64)
     seqlen_k = np.asarray(seqlen_k, dtype=np.int64)
     block_table = np.asarray(block_table, dtype=np.int64)
@@ -234,9 +251,10 @@ def attention_paged(q, k_cache, v_cache, cu_q, seqlen_k, block_table, mods=None,
 
 
 def paged_rows(q, k_cache, v_cache, cu_q, seqlen_k, block_table, picks, mods=None,
-               k_descale=None, v_descale=None, layout="head_major"):
+               k_descale=None, v_descale=None, layout="head_major", q_descale=None):
     """Selected rows (b, h, i) of paged attention over either page layout;
     returns (O [n, Dv], LSE [n])."""
+    q = paged_queries(q, q_descale)
     cu_q = np.asarray(cu_q, dtype=np.int64)
     seqlen_k = np.asarray(seqlen_k, dtype=np.int64)
     block_table = np.asarray(block_table, dtype=np.int64)

@@ -92,7 +92,7 @@ def make_varlen(lengths_q, lengths_k, Hq, Hkv, Dqk, Dv, seed, device="cpu"):
 
 
 def make_paged(lengths_q, lengths_k, Hq, Hkv, Dqk, Dv, page_size, seed, device="cpu",
-               kv_dtype="fp8", extra_pages=0, min_pages=0, place_high=0, poison=True):
+               kv_dtype="fp8", extra_pages=0, min_pages=0, place_high=0, poison=True, q_dtype="bf16"):
     """Paged K/V caches with head-major pages.
 
     K cache [num_pages, Hkv, page_size, Dqk], V cache [num_pages, Hkv, page_size, Dv]
@@ -103,7 +103,9 @@ def make_paged(lengths_q, lengths_k, Hq, Hkv, Dqk, Dv, page_size, seed, device="
     the first `place_high` used pages to the highest page ids (large offsets).
     Unused pages and the bytes past seqlen_k in a sequence's last page are
     filled with E4M3 NaN bytes (or bf16 NaN) when `poison` is set.
-    Returns dict(q, k_cache, v_cache, cu_q, seqlen_k, block_table, k_descale,
+    q_dtype="fp8" quantises the same bf16 queries to E4M3 codes (uint8) with a
+    per-tensor q_descale (amax/448); q_descale is None for bf16 queries.
+    Returns dict(q, q_descale, k_cache, v_cache, cu_q, seqlen_k, block_table, k_descale,
     v_descale, num_pages, k_logical, v_logical) where *_logical are the
     token-major [Tk, Hkv, D] caches before paging (CPU, for reference only
     when small; None when the cache is large).
@@ -131,6 +133,9 @@ def make_paged(lengths_q, lengths_k, Hq, Hkv, Dqk, Dv, page_size, seed, device="
     cu_q = cu_from_lengths(lengths_q)
     tq, tk = int(cu_q[-1]), sum(int(l) for l in lengths_k)
     q = randn_bf16((tq, Hq, Dqk), seed, device)
+    q_descale = None
+    if q_dtype == "fp8":
+        q, q_descale = quantize_e4m3(q)
     kf = torch.randn((tk, Hkv, Dqk), generator=_generator(seed + 100_000, device), device=device)
     vf = torch.randn((tk, Hkv, Dv), generator=_generator(seed + 200_000, device), device=device)
     if kv_dtype == "fp8":
@@ -157,7 +162,8 @@ def make_paged(lengths_q, lengths_k, Hq, Hkv, Dqk, Dv, page_size, seed, device="
         v_cache[tok_page, :, tok_slot, :] = vq
     small = tk * Hkv * (Dqk + Dv) <= (1 << 26)
     return dict(
-        q=q, k_cache=k_cache, v_cache=v_cache,
+        q=q, q_descale=None if q_descale is None else q_descale.to(device),
+        k_cache=k_cache, v_cache=v_cache,
         cu_q=cu_q.to(device),
         seqlen_k=torch.tensor([int(l) for l in lengths_k], dtype=torch.int32, device=device),
         block_table=block_table.to(device),

@@ -382,3 +382,51 @@ def test_vectorized_pages_give_the_head_major_result():
     o1, l1 = oracle.attention_paged(f64(d["q"]), d["k_cache"].numpy(), d["v_cache"].numpy(), *args)
     o2, l2 = oracle.attention_paged(f64(e["q"]), e["k_cache"].numpy(), e["v_cache"].numpy(), *args, layout="vectorized")
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ----------------------------------------------------------------------------- E4M3 queries
+def test_fp8_query_codes_decode_to_the_golden_points_times_descale():
+    """Q codes are read by the same OCP E4M3 rule as the caches, then scaled."""
+    with open(os.path.join(os.path.dirname(__file__), "golden", "e4m3_points.json")) as f:
+        pts = [(int(c, 16), v) for c, v in json.load(f)["points"] if v != "nan"]
+    codes = np.array([c for c, _ in pts], dtype=np.uint8).reshape(1, 1, -1)
+    got = olay.paged_queries(codes, 0.375).reshape(-1)
+    assert np.array_equal(got, np.array([v for _, v in pts]) * 0.375)
+    with pytest.raises(ValueError):
+        olay.paged_queries(codes)
+    with pytest.raises(ValueError):
+        olay.paged_queries(np.zeros((1, 1, 4)), 0.5)
+
+
+def test_fp8_query_zero_codes_give_log_count_and_mean():
+    """All-zero Q codes (any q_descale): every visible key has logit 0, so
+    LSE = ln(visible count) and O = mean of the visible V rows."""
+    lq, lk = [3, 1, 40], [9, 70, 40]
+    d = synth.make_paged(lq, lk, 4, 2, 64, 32, page_size=16, seed=7, q_dtype="fp8")
+    q = np.zeros(tuple(d["q"].shape), dtype=np.uint8)
+    kd, vd = float(d["k_descale"]), float(d["v_descale"])
+    o, lse = oracle.attention_paged(q, f64(d["k_cache"]), f64(d["v_cache"]), d["cu_q"], d["seqlen_k"],
+                                    d["block_table"], dict(causal=True), kd, vd, q_descale=3.0)
+    cu = d["cu_q"].tolist()
+    vlog = d["v_logical"].double().numpy() if d["v_logical"].dtype != torch.uint8 else \
+        oracle.decode_e4m3(d["v_logical"].numpy()) * vd
+    ks = np.cumsum([0] + lk)
+    for b in range(3):
+        for i in range(lq[b]):
+            n = i + lk[b] - lq[b] + 1
+            for h in range(4):
+                assert abs(lse[h, cu[b] + i] - math.log(n)) < 1e-12
+                assert np.allclose(o[cu[b] + i, h], vlog[ks[b]:ks[b] + n, h // 2].mean(axis=0), atol=1e-12)
+
+
+def test_fp8_query_descale_acts_as_a_logit_scale():
+    """q_descale multiplies every logit: (q_descale 2c, scale s) equals
+    (q_descale c, scale 2s), and differs from (q_descale c, scale s)."""
+    d = synth.make_paged([5, 17], [30, 17], 4, 4, 64, 64, page_size=8, seed=11, q_dtype="fp8")
+    args = (f64(d["q"]), f64(d["k_cache"]), f64(d["v_cache"]), d["cu_q"], d["seqlen_k"], d["block_table"])
+    kd, vd, c = float(d["k_descale"]), float(d["v_descale"]), float(d["q_descale"])
+    o1, l1 = oracle.attention_paged(*args, dict(causal=True, scale=0.1), kd, vd, q_descale=2 * c)
+    o2, l2 = oracle.attention_paged(*args, dict(causal=True, scale=0.2), kd, vd, q_descale=c)
+    o3, l3 = oracle.attention_paged(*args, dict(causal=True, scale=0.1), kd, vd, q_descale=c)
+    assert np.allclose(o1, o2, atol=1e-12) and np.allclose(l1, l2, atol=1e-12)
+    assert not np.allclose(l1, l3, atol=1e-3)
