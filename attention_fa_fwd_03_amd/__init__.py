@@ -19,6 +19,8 @@ from .binding import (  # noqa: F401
     fa_fwd_varlen,
     fa_fwd_paged,
     fa_fwd_paged_vec,
+    FA_PAGES_HEAD_MAJOR,
+    FA_PAGES_VECTORIZED,
     fa_fwd_paged_workspace_size,
     fa_last_error,
     fa_abi_version,

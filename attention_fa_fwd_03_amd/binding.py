@@ -46,6 +46,16 @@ class _FaMods(ctypes.Structure):
     ]
 
 
+class _FaPagedOpts(ctypes.Structure):
+    _fields_ = [
+        ("q_dtype", ctypes.c_int),
+        ("q_descale", ctypes.c_void_p),
+        ("page_layout", ctypes.c_int32),
+    ]
+
+
+FA_PAGES_HEAD_MAJOR, FA_PAGES_VECTORIZED = 0, 1
+
 _vp, _i64, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
 lib.fa_fwd_dense.argtypes = [_vp] * 5 + [_i64] * 7 + [ctypes.POINTER(_FaMods), _vp]
 lib.fa_fwd_dense.restype = ctypes.c_int
@@ -56,6 +66,9 @@ lib.fa_fwd_paged.argtypes = ([_vp] * 8 + [_i64] * 11 + [ctypes.c_int, _vp, _vp, 
 lib.fa_fwd_paged.restype = ctypes.c_int
 lib.fa_fwd_paged_vec.argtypes = lib.fa_fwd_paged.argtypes
 lib.fa_fwd_paged_vec.restype = ctypes.c_int
+lib.fa_fwd_paged_ex.argtypes = ([_vp] * 8 + [_i64] * 11 + [ctypes.c_int, _vp, _vp, _vp, _sz,
+                                                            ctypes.POINTER(_FaPagedOpts), ctypes.POINTER(_FaMods), _vp])
+lib.fa_fwd_paged_ex.restype = ctypes.c_int
 lib.fa_fwd_paged_workspace_size.argtypes = [_i64] * 9 + [ctypes.c_int]
 lib.fa_fwd_paged_workspace_size.restype = _sz
 lib.fa_last_error.argtypes = []
@@ -180,10 +193,11 @@ def fa_fwd_paged_workspace_size(B, total_q, max_seqlen_q, max_seqlen_k, Hq, Hkv,
 
 
 def fa_fwd_paged(q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, max_seqlen_q, max_seqlen_k,
-                 k_descale=None, v_descale=None, workspace=None, mods=None, stream=None):
+                 k_descale=None, v_descale=None, workspace=None, mods=None, stream=None, q_descale=None):
     """O [Tq,Hq,Dv] and LSE [Hq,Tq] over a paged cache (see include/fa.h).
 
     k_cache/v_cache: uint8 (FP8 E4M3 codes) or bf16, [num_pages, Hkv, page_size, D].
+    q: bf16, or uint8 E4M3 codes with q_descale (fa_fwd_paged_ex).
     """
     P, Hkv, ps, Dqk = k_cache.shape
     Dv = v_cache.shape[3]
@@ -191,12 +205,14 @@ def fa_fwd_paged(q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_tabl
     cdt = torch.uint8 if fp8 else torch.bfloat16
     _need(k_cache, "k_cache", cdt, (P, Hkv, ps, Dqk))
     _need(v_cache, "v_cache", cdt, (P, Hkv, ps, Dv))
-    _paged_call(lib.fa_fwd_paged, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, max_seqlen_q,
-                max_seqlen_k, P, Hkv, ps, Dqk, Dv, fp8, k_descale, v_descale, workspace, mods, stream)
+    _paged_call(FA_PAGES_HEAD_MAJOR, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table,
+                max_seqlen_q, max_seqlen_k, P, Hkv, ps, Dqk, Dv, fp8, k_descale, v_descale, workspace, mods, stream,
+                q_descale)
 
 
 def fa_fwd_paged_vec(q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, max_seqlen_q,
-                     max_seqlen_k, k_descale=None, v_descale=None, workspace=None, mods=None, stream=None):
+                     max_seqlen_k, k_descale=None, v_descale=None, workspace=None, mods=None, stream=None,
+                     q_descale=None):
     """fa_fwd_paged over vectorised FP8 pages (see include/fa.h).
 
     k_cache: uint8 [num_pages, Hkv, D_qk/16, page_size, 16];
@@ -209,16 +225,23 @@ def fa_fwd_paged_vec(q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_
     Dv = v_cache.shape[3]
     _need(k_cache, "k_cache", torch.uint8, (P, Hkv, Dqk // 16, ps, 16))
     _need(v_cache, "v_cache", torch.uint8, (P, Hkv, ps // 16, Dv, 16))
-    _paged_call(lib.fa_fwd_paged_vec, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table,
+    _paged_call(FA_PAGES_VECTORIZED, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table,
                 max_seqlen_q, max_seqlen_k, P, Hkv, ps, Dqk, Dv, True, k_descale, v_descale, workspace, mods,
-                stream)
+                stream, q_descale)
 
 
-def _paged_call(fn, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, max_seqlen_q, max_seqlen_k,
-                P, Hkv, ps, Dqk, Dv, fp8, k_descale, v_descale, workspace, mods, stream):
+def _paged_call(layout, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, max_seqlen_q,
+                max_seqlen_k, P, Hkv, ps, Dqk, Dv, fp8, k_descale, v_descale, workspace, mods, stream, q_descale):
+    """bf16 queries go through fa_fwd_paged / fa_fwd_paged_vec, E4M3 queries
+    (uint8) through fa_fwd_paged_ex."""
     Tq, Hq = q.shape[0], q.shape[1]
     B = cu_seqlens_q.shape[0] - 1
-    _need(q, "q", torch.bfloat16, (Tq, Hq, Dqk))
+    q8 = q.dtype == torch.uint8
+    _need(q, "q", torch.uint8 if q8 else torch.bfloat16, (Tq, Hq, Dqk))
+    if q8:
+        _need(q_descale, "q_descale", torch.float32)
+    elif q_descale is not None:
+        raise ValueError("q_descale is for uint8 (E4M3) queries")
     _need(o, "o", torch.bfloat16, (Tq, Hq, Dv))
     _need(lse, "lse", torch.float32, (Hq, Tq))
     _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, (B + 1,))
@@ -233,9 +256,15 @@ def _paged_call(fn, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_t
     if workspace is not None:
         _need(workspace, "workspace")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    _check(fn(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), lse.data_ptr(),
-              cu_seqlens_q.data_ptr(), seqlen_k.data_ptr(), block_table.data_ptr(),
-              B, Tq, int(max_seqlen_q), int(max_seqlen_k), P, ps, block_table.shape[1],
-              Hq, Hkv, Dqk, Dv, FA_FP8_E4M3 if fp8 else FA_BF16,
-              k_descale.data_ptr() if fp8 else None, v_descale.data_ptr() if fp8 else None,
-              ws_ptr or None, ws_bytes, _mods(mods), _stream(stream, q.device)))
+    args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            cu_seqlens_q.data_ptr(), seqlen_k.data_ptr(), block_table.data_ptr(),
+            B, Tq, int(max_seqlen_q), int(max_seqlen_k), P, ps, block_table.shape[1],
+            Hq, Hkv, Dqk, Dv, FA_FP8_E4M3 if fp8 else FA_BF16,
+            k_descale.data_ptr() if fp8 else None, v_descale.data_ptr() if fp8 else None,
+            ws_ptr or None, ws_bytes)
+    if q8:
+        opts = _FaPagedOpts(FA_FP8_E4M3, q_descale.data_ptr(), layout)
+        _check(lib.fa_fwd_paged_ex(*args, ctypes.byref(opts), _mods(mods), _stream(stream, q.device)))
+    else:
+        fn = lib.fa_fwd_paged_vec if layout == FA_PAGES_VECTORIZED else lib.fa_fwd_paged
+        _check(fn(*args, _mods(mods), _stream(stream, q.device)))

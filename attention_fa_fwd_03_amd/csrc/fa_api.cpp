@@ -231,7 +231,7 @@ int fa_fwd_dense(const void* q, const void* k, const void* v, void* o, float* ls
       overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nk) || overlaps(lse, nl, v, nv))
     return fail(FA_ERR_INVALID, "outputs must not overlap inputs");
   fa::PrefillArgs a{};
-  a.q = (const __bf16*)q;
+  a.q = q;
   a.k = k;
   a.v = v;
   a.o = (__bf16*)o;
@@ -275,7 +275,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
       overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nk) || overlaps(lse, nl, v, nv))
     return fail(FA_ERR_INVALID, "outputs must not overlap inputs");
   fa::PrefillArgs a{};
-  a.q = (const __bf16*)q;
+  a.q = q;
   a.k = k;
   a.v = v;
   a.o = (__bf16*)o;
@@ -302,8 +302,8 @@ size_t fa_fwd_paged_workspace_size(int64_t B, int64_t total_q, int64_t max_seqle
 
 namespace {
 
-// Both paged entry points: vec selects the vectorised page format.
-int paged_impl(bool vec, const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+// The paged entry points.
+int paged_impl(const fa_paged_opts* opts, const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                const int32_t* cu_seqlens_q, const int32_t* seqlen_k, const int32_t* block_table,
                int64_t B, int64_t total_q, int64_t max_seqlen_q, int64_t max_seqlen_k,
                int64_t num_pages, int64_t page_size, int64_t max_pages_per_seq,
@@ -315,7 +315,17 @@ int paged_impl(bool vec, const void* q, const void* k_cache, const void* v_cache
   int rc = check_common(B, Hq, Hkv, d_qk, d_v);
   if (rc) return rc;
   if (kv_dtype != FA_BF16 && kv_dtype != FA_FP8_E4M3) return fail(FA_ERR_INVALID, "unknown kv_dtype %d", (int)kv_dtype);
+  const fa_paged_opts def{FA_BF16, nullptr, FA_PAGES_HEAD_MAJOR};
+  if (!opts) opts = &def;
+  if (opts->q_dtype != FA_BF16 && opts->q_dtype != FA_FP8_E4M3)
+    return fail(FA_ERR_INVALID, "unknown q_dtype %d", (int)opts->q_dtype);
+  if (opts->page_layout != FA_PAGES_HEAD_MAJOR && opts->page_layout != FA_PAGES_VECTORIZED)
+    return fail(FA_ERR_INVALID, "unknown page_layout %d", (int)opts->page_layout);
+  const bool vec = opts->page_layout == FA_PAGES_VECTORIZED;
+  const bool q8 = opts->q_dtype == FA_FP8_E4M3;
   if (vec && kv_dtype != FA_FP8_E4M3) return fail(FA_ERR_UNSUPPORTED, "vectorised pages hold FP8 E4M3 K/V only");
+  if (q8 && kv_dtype != FA_FP8_E4M3) return fail(FA_ERR_UNSUPPORTED, "E4M3 queries need an FP8 E4M3 cache");
+  if (q8 && !opts->q_descale) return fail(FA_ERR_INVALID, "E4M3 queries need q_descale");
   if (total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_pages < 0 || max_pages_per_seq < 0)
     return fail(FA_ERR_INVALID, "sizes must be >= 0");
   if (max_seqlen_q > total_q) return fail(FA_ERR_INVALID, "max_seqlen_q exceeds total_q");
@@ -346,7 +356,7 @@ int paged_impl(bool vec, const void* q, const void* k_cache, const void* v_cache
   if (max_seqlen_k > 0 && num_pages == 0) return fail(FA_ERR_INVALID, "num_pages is 0 but max_seqlen_k > 0");
   if (fp8 && (!k_descale || !v_descale)) return fail(FA_ERR_INVALID, "FP8 caches need k_descale and v_descale");
   const size_t es = fp8 ? 1 : 2;
-  const size_t nq = (size_t)(total_q * Hq * d_qk) * 2, no = (size_t)(total_q * Hq * d_v) * 2;
+  const size_t nq = (size_t)(total_q * Hq * d_qk) * (q8 ? 1 : 2), no = (size_t)(total_q * Hq * d_v) * 2;
   const size_t nk = (size_t)num_pages * Hkv * page_size * d_qk * es, nv = (size_t)num_pages * Hkv * page_size * d_v * es;
   const size_t nl = (size_t)(Hq * total_q) * 4;
   if (overlaps(o, no, lse, nl)) return fail(FA_ERR_INVALID, "lse must not overlap o");
@@ -376,7 +386,8 @@ int paged_impl(bool vec, const void* q, const void* k_cache, const void* v_cache
     pl.B = (int)B;
     pl.kv_cap = (int)L.kv_cap;
     fa::DecodeArgs d{};
-    d.q = (const __bf16*)q;
+    d.q = q;
+    d.q_descale = q8 ? opts->q_descale : nullptr;
     d.k = k_cache;
     d.v = v_cache;
     d.part_o = part_o;
@@ -402,7 +413,7 @@ int paged_impl(bool vec, const void* q, const void* k_cache, const void* v_cache
     d.win_left = (m.flags & FA_WINDOW) ? clamp_i32(m.wl) : -1;
     d.win_right = (m.flags & FA_WINDOW) ? clamp_i32(m.wr) : -1;
     bool supported = false;
-    hipError_t e = fa::decode_dispatch(pl, d, (int)d_qk, (int)d_v, fp8, vec, st, &supported);
+    hipError_t e = fa::decode_dispatch(pl, d, (int)d_qk, (int)d_v, fp8, vec, q8, st, &supported);
     if (!supported) return fail(FA_ERR_UNSUPPORTED, "no decode kernel for (%lld, %lld)", (long long)d_qk, (long long)d_v);
     if (e != hipSuccess) return fail(FA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
     fa::CombineArgs c{};
@@ -424,7 +435,8 @@ int paged_impl(bool vec, const void* q, const void* k_cache, const void* v_cache
   }
 
   fa::PrefillArgs a{};
-  a.q = (const __bf16*)q;
+  a.q = q;
+  a.q_descale = q8 ? opts->q_descale : nullptr;
   a.k = k_cache;
   a.v = v_cache;
   a.o = (__bf16*)o;
@@ -459,7 +471,7 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* 
                  const float* k_descale, const float* v_descale,
                  void* workspace, size_t workspace_bytes_in,
                  const fa_mods* mods, void* stream) {
-  return paged_impl(false, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, B, total_q,
+  return paged_impl(nullptr, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, B, total_q,
                     max_seqlen_q, max_seqlen_k, num_pages, page_size, max_pages_per_seq, Hq, Hkv, d_qk, d_v,
                     kv_dtype, k_descale, v_descale, workspace, workspace_bytes_in, mods, stream);
 }
@@ -472,7 +484,21 @@ int fa_fwd_paged_vec(const void* q, const void* k_cache, const void* v_cache, vo
                      const float* k_descale, const float* v_descale,
                      void* workspace, size_t workspace_bytes_in,
                      const fa_mods* mods, void* stream) {
-  return paged_impl(true, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, B, total_q,
+  const fa_paged_opts vec{FA_BF16, nullptr, FA_PAGES_VECTORIZED};
+  return paged_impl(&vec, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, B, total_q,
+                    max_seqlen_q, max_seqlen_k, num_pages, page_size, max_pages_per_seq, Hq, Hkv, d_qk, d_v,
+                    kv_dtype, k_descale, v_descale, workspace, workspace_bytes_in, mods, stream);
+}
+
+int fa_fwd_paged_ex(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                    const int32_t* cu_seqlens_q, const int32_t* seqlen_k, const int32_t* block_table,
+                    int64_t B, int64_t total_q, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                    int64_t num_pages, int64_t page_size, int64_t max_pages_per_seq,
+                    int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v, fa_dtype kv_dtype,
+                    const float* k_descale, const float* v_descale,
+                    void* workspace, size_t workspace_bytes_in,
+                    const fa_paged_opts* opts, const fa_mods* mods, void* stream) {
+  return paged_impl(opts, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, B, total_q,
                     max_seqlen_q, max_seqlen_k, num_pages, page_size, max_pages_per_seq, Hq, Hkv, d_qk, d_v,
                     kv_dtype, k_descale, v_descale, workspace, workspace_bytes_in, mods, stream);
 }

@@ -35,7 +35,8 @@
 // logit constant.  Each product is exact (3-bit x 3-bit mantissas) and
 // accumulated in fp32, so the logits differ from the bf16-Q logits only by
 // the split's rounding (about 1e-3 in natural-log units at the largest
-// logits of N(0,1) data).
+// logits of N(0,1) data).  E4M3 queries (with their own descale) are the B
+// operand as they are: one exact product per step, no split.
 //
 // The cache streams through registers with coalesced 16-byte loads (lane l
 // of load i takes bytes [1024 i + 16 l, +16) of the tile, so every load
@@ -82,17 +83,6 @@ __device__ __forceinline__ int dec_kswz(int r) { return (r >> 2) & 3; }
 
 __device__ __forceinline__ i32x2 lds_read_tr8(const char FA_LDS* __restrict__ p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 FA_LDS*)(p));
-}
-
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(i32x2 w) {
-  bf16x8 r;
-  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
-  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
-  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
-  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-  return r;
 }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -190,7 +180,7 @@ __global__ __launch_bounds__(256) void fa_decode_plan_kernel(const DecodePlanArg
 // worker that owns tile i of T in a split over W workers
 __device__ __forceinline__ int worker_of(int64_t i, int64_t T, int W) { return (int)(((i + 1) * W - 1) / T); }
 
-template <int DQK, int DV, int NRB, int NBUF, bool VEC>
+template <int DQK, int DV, int NRB, int NBUF, bool VEC, bool Q8>
 __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(NBUF >= 3 ? 1 : (NRB == 1 && NBUF == 1 ? 3 : 2))))
 void fa_decode_kernel(const DecodeArgs a) {
   static_assert(DQK % 32 == 0 && DV == 128 && (kDecKT * DQK) % 1024 == 0, "decode tile shapes");
@@ -244,7 +234,8 @@ void fa_decode_kernel(const DecodeArgs a) {
   const int krow = lane & 15, kx = dec_kswz(krow);
   const char FA_LDS* krd = klds + krow * DQK + (kgrp & 1) * 8;
   const float kdesc = *a.k_descale, vdesc = *a.v_descale;
-  const float C = a.qk_scale * kLog2e * kdesc * (1.0f / 16.0f);   // Q enters scaled by 16
+  // bf16 Q enters scaled by 16 (split below); E4M3 Q enters as it is, with its descale
+  const float C = Q8 ? a.qk_scale * kLog2e * kdesc * *a.q_descale : a.qk_scale * kLog2e * kdesc * (1.0f / 16.0f);
   const int pmask = (1 << a.page_shift) - 1;
 
   // One unit segment: sequence b, kv-head g, tiles [t0, t1) -> partial slot.
@@ -377,12 +368,19 @@ void fa_decode_kernel(const DecodeArgs a) {
     i32x2 qhi[NRB][kSteps], qlo[NRB][kSteps];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-      const bf16* qp = a.q + tok[rb] * a.q_st + (int64_t)hq[rb] * a.q_sh + kgrp * 8;
+      const int64_t qoff = tok[rb] * a.q_st + (int64_t)hq[rb] * a.q_sh + kgrp * 8;
 #pragma unroll
       for (int st = 0; st < kSteps; ++st) {
-        bf16x8 x = *reinterpret_cast<const bf16x8*>(qp + 32 * st);
-        if (!rvalid[rb]) x = bf16x8{};
-        split_e4m3(x, qhi[rb][st], qlo[rb][st]);
+        if (Q8) {
+          // E4M3 queries are the B operand as they are (one product per step)
+          i32x2 x = *reinterpret_cast<const i32x2*>(reinterpret_cast<const uint8_t*>(a.q) + qoff + 32 * st);
+          qhi[rb][st] = rvalid[rb] ? x : i32x2{};
+          qlo[rb][st] = i32x2{};
+        } else {
+          bf16x8 x = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(a.q) + qoff + 32 * st);
+          if (!rvalid[rb]) x = bf16x8{};
+          split_e4m3(x, qhi[rb][st], qlo[rb][st]);
+        }
       }
     }
 #pragma unroll
@@ -443,7 +441,7 @@ void fa_decode_kernel(const DecodeArgs a) {
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
           sacc[rb][n / kSteps] = mfma16_fp8(kraw[n], qhi[rb][n % kSteps], sacc[rb][n / kSteps]);
-          sacc[rb][n / kSteps] = mfma16_fp8(kraw[n], qlo[rb][n % kSteps], sacc[rb][n / kSteps]);
+          if (!Q8) sacc[rb][n / kSteps] = mfma16_fp8(kraw[n], qlo[rb][n % kSteps], sacc[rb][n / kSteps]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -626,7 +624,7 @@ __global__ __launch_bounds__(256) void fa_combine_kernel(const CombineArgs a) {
 }
 
 hipError_t decode_dispatch(const DecodePlanArgs& plan, const DecodeArgs& a, int dqk, int dv, bool fp8, bool vec,
-                           hipStream_t stream, bool* supported) {
+                           bool q8, hipStream_t stream, bool* supported) {
   *supported = fp8 && dv == 128 && (dqk == 192 || dqk == 128);
   if (!*supported) return hipSuccess;
   hipLaunchKernelGGL(fa_decode_plan_kernel, dim3(1), dim3(256), 0, stream, plan);
@@ -634,16 +632,18 @@ hipError_t decode_dispatch(const DecodePlanArgs& plan, const DecodeArgs& a, int 
   if (e != hipSuccess) return e;
   const dim3 grid((a.n_workers + kDecWaves - 1) / kDecWaves);
   const bool two = a.slot_rows > 16;
-#define FA_DEC(DQ, VC)                                                                                       \
-  if (dqk == DQ && vec == VC) {                                                                              \
-    if (two) hipLaunchKernelGGL((fa_decode_kernel<DQ, 128, 2, 1, VC>), grid, dim3(kDecWaves * 64), 0, stream, a); \
-    else hipLaunchKernelGGL((fa_decode_kernel<DQ, 128, 1, 2, VC>), grid, dim3(kDecWaves * 64), 0, stream, a);  \
-    return hipGetLastError();                                                                                \
+#define FA_DEC(DQ, VC, Q)                                                                                  \
+  if (dqk == DQ && vec == VC && q8 == Q) {                                                                 \
+    if (two) hipLaunchKernelGGL((fa_decode_kernel<DQ, 128, 2, 1, VC, Q>), grid, dim3(kDecWaves * 64), 0, stream, a); \
+    else hipLaunchKernelGGL((fa_decode_kernel<DQ, 128, 1, 2, VC, Q>), grid, dim3(kDecWaves * 64), 0, stream, a);  \
+    return hipGetLastError();                                                                              \
   }
-  FA_DEC(192, false)
-  FA_DEC(128, false)
-  FA_DEC(192, true)
-  FA_DEC(128, true)
+#define FA_DEC2(DQ, VC) FA_DEC(DQ, VC, false) FA_DEC(DQ, VC, true)
+  FA_DEC2(192, false)
+  FA_DEC2(128, false)
+  FA_DEC2(192, true)
+  FA_DEC2(128, true)
+#undef FA_DEC2
 #undef FA_DEC
   *supported = false;
   return hipSuccess;

@@ -99,6 +99,18 @@ __device__ __forceinline__ void global_to_lds16(const void* gsrc, char FA_LDS* l
   __builtin_amdgcn_global_load_lds((const FA_GLOBAL void*)(gsrc), (FA_LDS void*)(lds_base), 16, 0, 0);
 }
 
+// 8 OCP E4M3 bytes -> 8 bf16 (exact).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(i32x2 w) {
+  bf16x8 r;
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
 // 16 OCP E4M3 bytes -> 16 bf16 (exact).
 __device__ __forceinline__ void fp8x16_to_bf16(i32x4 w, bf16x8& lo, bf16x8& hi) {
 #pragma unroll

@@ -16,7 +16,8 @@ constexpr int kModSoftcap = 2;
 // it K byte (s, d) sits at (d/16)*page*16 + s*16 + d%16 and V byte (s, d) at
 // (s/16)*Dv*16 + d*16 + s%16; k_st / v_st are not used.
 struct PrefillArgs {
-  const __bf16* q;
+  const void* q;               // bf16, or OCP E4M3 codes when q_descale is set
+  const float* q_descale;      // FP8 queries: per-tensor descale (device scalar); else null
   const void* k;
   const void* v;
   __bf16* o;
@@ -52,7 +53,8 @@ struct PrefillArgs {
 // result per unit it touches, into slot w + u.  A unit's rows are
 // (query i, q-head h in the kv-head's group), rows <= 32.
 struct DecodeArgs {
-  const __bf16* q;
+  const void* q;               // bf16, or OCP E4M3 codes (kernels built with the q8 flag)
+  const float* q_descale;      // FP8 queries: per-tensor descale (device scalar)
   const void* k;
   const void* v;
   float* part_o;               // [n_slots, slot_rows, Dv] fp32 (normalised by own l)
@@ -99,7 +101,7 @@ struct CombineArgs {
 hipError_t prefill_dispatch(const PrefillArgs& a, int dqk, int dv, bool fp8, bool paged, bool vec, int mods,
                             int n_bh, int n_qtiles, hipStream_t stream, bool* supported);
 hipError_t decode_dispatch(const DecodePlanArgs& plan, const DecodeArgs& a, int dqk, int dv, bool fp8, bool vec,
-                           hipStream_t stream, bool* supported);
+                           bool q8, hipStream_t stream, bool* supported);
 hipError_t combine_dispatch(const CombineArgs& a, int dv, hipStream_t stream, bool* supported);
 
 }  // namespace fa

@@ -382,8 +382,18 @@ void fa_prefill_kernel(const PrefillArgs a) {
   const int qrow = q0 + wave * 32 + (lane & 31);
   const bool qvalid = qrow < sv.sq;
   bf16x8 qf[DQK / 16];
-  {
-    const bf16* qp = a.q + (sv.qstart + (qvalid ? qrow : 0)) * a.q_st + (int64_t)sv.h * a.q_sh + (lane >> 5) * 8;
+  const int64_t qoff = (sv.qstart + (qvalid ? qrow : 0)) * a.q_st + (int64_t)sv.h * a.q_sh + (lane >> 5) * 8;
+  if (FP8 && a.q_descale) {
+    // E4M3 queries: converted exactly, the descale folded into the logit constant
+    const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.q) + qoff;
+#pragma unroll
+    for (int s = 0; s < DQK / 16; ++s) {
+      i32x2 v = *reinterpret_cast<const i32x2*>(qp + s * 16);
+      if (!qvalid) v = i32x2{};
+      qf[s] = fp8x8_to_bf16(v);
+    }
+  } else {
+    const bf16* qp = reinterpret_cast<const bf16*>(a.q) + qoff;
 #pragma unroll
     for (int s = 0; s < DQK / 16; ++s) {
       bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + s * 16);
@@ -405,6 +415,7 @@ void fa_prefill_kernel(const PrefillArgs a) {
   if (FP8) {
     kdesc = *a.k_descale;
     vdesc = *a.v_descale;
+    if (a.q_descale) kdesc *= *a.q_descale;       // both descales scale every logit
   }
   // C: multiplier from the raw MFMA dot product to log2-domain scaled logits
   const float C = ANYMOD ? 1.0f : a.qk_scale * kLog2e * kdesc;

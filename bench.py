@@ -10,7 +10,7 @@ before timing starts.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
                   [--flex alibi|softcap|window|bernoulli|block_causal|none|causal] [--page-size P]
-                  [--layout head_major|vec]
+                  [--layout head_major|vec] [--q-dtype bf16|fp8]
                   [--no-cpu-baseline]
                   [--copy-calibration]
   python bench.py --config N --traffic-from FETCH_CSV WRITE_CSV
@@ -18,7 +18,8 @@ before timing starts.
 --config selects another workload for investigation (1 dense D64, 3 paged
 FP8 prefill, 4 paged FP8 decode, 5 flex); the default line is config 2.
 --layout vec runs configs 3 and 4 on the vectorised 5-D page format
-(fa_fwd_paged_vec) instead of head-major pages.
+(fa_fwd_paged_vec) instead of head-major pages; --q-dtype fp8 gives them
+E4M3 queries with a per-tensor descale (fa_fwd_paged_ex).
 Prints ONE JSON line.
 """
 from __future__ import annotations
@@ -115,7 +116,8 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, key: str, kind: str) -
     return entry
 
 
-def build_workload(cfg: int, flex: str, torch, synth, fa, page_size: int = 64, layout: str = "head_major"):
+def build_workload(cfg: int, flex: str, torch, synth, fa, page_size: int = 64, layout: str = "head_major",
+                   q_dtype: str = "bf16"):
     """Returns (name, run_fn, work dict, oracle sample fn)."""
     dev = "cuda"
     if cfg == 1:
@@ -150,7 +152,8 @@ def build_workload(cfg: int, flex: str, torch, synth, fa, page_size: int = 64, l
             {"seqlens": lens, "total_tokens": T, "H": 16, "D": 128, "causal": True}, sample
     if cfg == 3:
         L = [2048] * 4
-        d = synth.make_paged(L, L, 16, 16, 192, 128, page_size=64, seed=synth.seed_for(3), device=dev)
+        d = synth.make_paged(L, L, 16, 16, 192, 128, page_size=64, seed=synth.seed_for(3), device=dev,
+                             q_dtype=q_dtype)
         if layout == "vec":
             d = synth.to_vectorized(d)
         fn = fa.fa_fwd_paged_vec if layout == "vec" else fa.fa_fwd_paged
@@ -159,15 +162,19 @@ def build_workload(cfg: int, flex: str, torch, synth, fa, page_size: int = 64, l
         mods = fa.Mods(causal=True)
         flops = 64 * 2048 * 2049 // 2 * (2 * 192 + 2 * 128)
         run = lambda: fn(d["q"], d["k_cache"], d["v_cache"], o, lse, d["cu_q"], d["seqlen_k"],
-                         d["block_table"], 2048, 2048, d["k_descale"], d["v_descale"], None, mods)
-        name = "paged FP8 causal prefill 4x2048 H16 Dqk192 Dv128 page64" + (" vectorised" if layout == "vec" else "")
+                         d["block_table"], 2048, 2048, d["k_descale"], d["v_descale"], None, mods,
+                         q_descale=d["q_descale"])
+        name = "paged FP8 causal prefill 4x2048 H16 Dqk192 Dv128 page64" + (" vectorised" if layout == "vec" else "") \
+            + (" fp8-q" if q_dtype == "fp8" else "")
         return name, run, dict(flops=flops, kind="prefill", bound="mfma"), \
-            {"B": 4, "S": 2048, "H": 16, "d_qk": 192, "d_v": 128, "page_size": 64, "layout": layout}, None
+            {"B": 4, "S": 2048, "H": 16, "d_qk": 192, "d_v": 128, "page_size": 64, "layout": layout,
+             "q_dtype": q_dtype}, None
     if cfg == 4:
         lk = synth.make_decode_lengths(synth.seed_for(4))
         lq = [1] * 64
         ps = page_size
-        d = synth.make_paged(lq, lk, 64, 8, 192, 128, page_size=ps, seed=synth.seed_for(4), device=dev)
+        d = synth.make_paged(lq, lk, 64, 8, 192, 128, page_size=ps, seed=synth.seed_for(4), device=dev,
+                             q_dtype=q_dtype)
         if layout == "vec":
             d = synth.to_vectorized(d)
             torch.cuda.empty_cache()
@@ -178,12 +185,13 @@ def build_workload(cfg: int, flex: str, torch, synth, fa, page_size: int = 64, l
         ws = torch.empty(n, dtype=torch.uint8, device=dev)
         mods = fa.Mods(causal=True)
         kv_bytes = sum(lk) * 8 * (192 + 128)
-        io_bytes = 64 * 64 * 192 * 2 + 64 * 64 * 128 * 2 + 64 * 64 * 4 + sum(math.ceil(x / ps) for x in lk) * 4
+        io_bytes = 64 * 64 * 192 * (1 if q_dtype == "fp8" else 2) + 64 * 64 * 128 * 2 + 64 * 64 * 4 + sum(math.ceil(x / ps) for x in lk) * 4
         flops = sum(lk) * 64 * (2 * 192 + 2 * 128)
         run = lambda: fn(d["q"], d["k_cache"], d["v_cache"], o, lse, d["cu_q"], d["seqlen_k"],
-                         d["block_table"], 1, max(lk), d["k_descale"], d["v_descale"], ws, mods)
+                         d["block_table"], 1, max(lk), d["k_descale"], d["v_descale"], ws, mods,
+                         q_descale=d["q_descale"])
         name = f"paged FP8 decode 64 seqs ctx U[1024,32768] GQA 64/8 Dqk192 Dv128 page{ps}" + \
-            (" vectorised" if layout == "vec" else "")
+            (" vectorised" if layout == "vec" else "") + (" fp8-q" if q_dtype == "fp8" else "")
 
         def sample():
             import oracle
@@ -198,18 +206,20 @@ def build_workload(cfg: int, flex: str, torch, synth, fa, page_size: int = 64, l
             for b in range(n_seq):
                 cbt[b, :npg[b]] = torch.arange(pos, pos + npg[b])
                 pos += npg[b]
-            qh = d["q"][:n_seq].float().cpu().double().numpy()
+            qh = d["q"][:n_seq].cpu().numpy() if q_dtype == "fp8" else d["q"][:n_seq].float().cpu().double().numpy()
+            qd = float(d["q_descale"]) if q_dtype == "fp8" else None
             cu = torch.arange(n_seq + 1).numpy()
             kd, vd = float(d["k_descale"]), float(d["v_descale"])
             dt, reps = _timed_reps(lambda: oracle.attention_paged(qh, kc, vc, cu, lk[:n_seq], cbt.numpy(),
                                                                   dict(causal=True), kd, vd, workers=_cores(),
                                                                   layout="vectorized" if layout == "vec"
-                                                                  else "head_major"))
+                                                                  else "head_major", q_descale=qd))
             sbytes = sum(lk[:n_seq]) * 8 * (192 + 128)
             return dict(seconds=dt, work=sbytes * reps,
                         sample=f"sequences 0-{n_seq - 1} ({sum(lk[:n_seq])} cached tokens, all heads), {reps} passes")
         return name, run, dict(flops=flops, bytes=kv_bytes + io_bytes, kind="decode", bound="hbm"), \
-            {"B": 64, "ctx_total": sum(lk), "Hq": 64, "Hkv": 8, "page_size": ps, "layout": layout}, sample
+            {"B": 64, "ctx_total": sum(lk), "Hq": 64, "Hkv": 8, "page_size": ps, "layout": layout,
+             "q_dtype": q_dtype}, sample
     if cfg == 5:
         B, H, S, D = 2, 16, 8192, 128
         d = synth.make_dense(B, S, S, H, H, D, D, seed=synth.seed_for(5), device=dev)
@@ -276,6 +286,8 @@ def main():
     ap.add_argument("--page-size", type=int, default=64, help="decode config: cache page size (power of two)")
     ap.add_argument("--layout", choices=["head_major", "vec"], default="head_major",
                     help="paged configs: head-major or vectorised 5-D pages")
+    ap.add_argument("--q-dtype", choices=["bf16", "fp8"], default="bf16",
+                    help="paged configs: bf16 or E4M3 queries")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (reference for HBM byte counters)")
@@ -287,6 +299,8 @@ def main():
         key += f"_ps{args.page_size}"
     if args.config in (3, 4) and args.layout == "vec":
         key += "_vec"
+    if args.config in (3, 4) and args.q_dtype == "fp8":
+        key += "_q8"
     if args.traffic_from:
         kind = "decode" if args.config == 4 else "prefill"
         print(json.dumps({key: traffic_from_counters(args.traffic_from[0], args.traffic_from[1], key, kind)}))
@@ -302,7 +316,7 @@ def main():
 
     torch.cuda.init()
     name, run, work, cfg_extra, sample = build_workload(args.config, args.flex, torch, synth, fa, args.page_size,
-                                                       args.layout)
+                                                       args.layout, args.q_dtype)
     if args.copy_calibration:
         # reference for the HBM byte counters: one device-to-device copy of
         # COPY_BYTES through the HIP runtime's own copy kernel
@@ -376,7 +390,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-kv/bf16" if args.config in (3, 4) else "bf16",
+        "dtype": ("fp8-qkv/bf16" if args.q_dtype == "fp8" else "fp8-kv/bf16") if args.config in (3, 4) else "bf16",
         "data": "synthetic",
         "config": {"workload": name, **cfg_extra},
         "roofline": roof,

@@ -163,8 +163,39 @@ int fa_fwd_paged_vec(const void* q, const void* k_cache, const void* v_cache, vo
                      void* workspace, size_t workspace_bytes,
                      const fa_mods* mods, void* stream);
 
-/* Workspace bytes fa_fwd_paged and fa_fwd_paged_vec need for these sizes (0
- * when they need none). */
+/* fa_paged_opts.page_layout */
+#define FA_PAGES_HEAD_MAJOR 0  /* fa_fwd_paged's pages */
+#define FA_PAGES_VECTORIZED 1  /* fa_fwd_paged_vec's pages */
+
+/* Query type and page format of fa_fwd_paged_ex.  A NULL fa_paged_opts*
+ * means bf16 queries and head-major pages (fa_fwd_paged). */
+typedef struct fa_paged_opts {
+  fa_dtype q_dtype;         /* FA_BF16, or FA_FP8_E4M3 (FP8 caches only) */
+  const float* q_descale;   /* FA_FP8_E4M3 queries: device fp32 scalar, real q = code * q_descale */
+  int32_t page_layout;      /* FA_PAGES_HEAD_MAJOR or FA_PAGES_VECTORIZED */
+} fa_paged_opts;
+
+/*
+ * fa_fwd_paged with a choice of query type and page format.  E4M3 queries
+ * follow the description of "Support paged FP8 Flash attention with
+ * asymmetric K/V head dim on gfx950" (OCP E4M3 Q/K/V with scalar descales):
+ * Q is [total_q, Hq, d_qk] E4M3 codes (1 byte each) and every logit carries
+ * q_descale * k_descale; they need kv_dtype FA_FP8_E4M3 (else
+ * FA_ERR_UNSUPPORTED) and a non-NULL q_descale (else FA_ERR_INVALID).  O
+ * stays bf16.  Everything else is fa_fwd_paged's (or, for vectorised pages,
+ * fa_fwd_paged_vec's), the workspace rule included.
+ */
+int fa_fwd_paged_ex(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                    const int32_t* cu_seqlens_q, const int32_t* seqlen_k, const int32_t* block_table,
+                    int64_t B, int64_t total_q, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                    int64_t num_pages, int64_t page_size, int64_t max_pages_per_seq,
+                    int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v, fa_dtype kv_dtype,
+                    const float* k_descale, const float* v_descale,
+                    void* workspace, size_t workspace_bytes,
+                    const fa_paged_opts* opts, const fa_mods* mods, void* stream);
+
+/* Workspace bytes the paged entry points need for these sizes (0 when they
+ * need none). */
 size_t fa_fwd_paged_workspace_size(int64_t B, int64_t total_q, int64_t max_seqlen_q,
                                    int64_t max_seqlen_k, int64_t Hq, int64_t Hkv, int64_t d_qk,
                                    int64_t d_v, int64_t page_size, fa_dtype kv_dtype);

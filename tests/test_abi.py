@@ -23,7 +23,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ["fa_fwd_dense", "fa_fwd_varlen", "fa_fwd_paged", "fa_fwd_paged_vec", "fa_fwd_paged_workspace_size",
+    for n in ["fa_fwd_dense", "fa_fwd_varlen", "fa_fwd_paged", "fa_fwd_paged_vec", "fa_fwd_paged_ex",
+              "fa_fwd_paged_workspace_size",
               "fa_last_error", "fa_abi_version"]:
         assert n in names
 
@@ -107,13 +108,15 @@ def test_mods_validation():
     assert rc == -1 and "unknown" in msg
 
 
-def _paged(vec=False, **kw):
+def _paged(vec=False, opts=None, **kw):
     fa = _lib()
     a = dict(q=FAKE, kc=FAKE * 2, vc=FAKE * 3, o=FAKE * 4, lse=FAKE * 5, cu=FAKE * 6, sk=FAKE * 7, bt=FAKE * 8,
              B=2, Tq=2, msq=1, msk=100, P=10, ps=64, mp=2, Hq=16, Hkv=2, dqk=192, dv=128, kv=1,
              kd=FAKE * 9, vd=FAKE * 10, ws=FAKE * 64, wsb=1 << 30, mods=None)
     a.update(kw)
     fn = fa.lib.fa_fwd_paged_vec if vec else fa.lib.fa_fwd_paged
+    if opts is not None:
+        fn = lambda *x: fa.lib.fa_fwd_paged_ex(*x[:-2], ctypes.byref(opts), *x[-2:])
     rc = fn(a["q"], a["kc"], a["vc"], a["o"], a["lse"], a["cu"], a["sk"], a["bt"], a["B"], a["Tq"],
             a["msq"], a["msk"], a["P"], a["ps"], a["mp"], a["Hq"], a["Hkv"], a["dqk"], a["dv"],
             a["kv"], a["kd"], a["vd"], a["ws"], a["wsb"], a["mods"], None)
@@ -151,6 +154,24 @@ def test_paged_vec_rejects(kw, code, frag):
     """The vectorised format holds FP8 whole 16-key blocks; every other check
     is the head-major entry point's."""
     rc, msg = _paged(vec=True, **kw)
+    assert rc == code and frag in msg, (rc, msg)
+
+
+def _opts(q_dtype=1, q_descale=FAKE * 11, layout=0):
+    from attention_fa_fwd_03_amd.binding import _FaPagedOpts
+    return _FaPagedOpts(q_dtype, q_descale, layout)
+
+
+@pytest.mark.parametrize("opt_kw,kw,code,frag", [
+    (dict(q_descale=0), dict(), -1, "q_descale"),
+    (dict(), dict(kv=0), -2, "FP8 E4M3 cache"),
+    (dict(q_dtype=5), dict(), -1, "q_dtype"),
+    (dict(layout=2), dict(), -1, "page_layout"),
+    (dict(layout=1), dict(ps=8, mp=16), -2, "page_size >= 16"),
+    (dict(q_dtype=0, layout=1), dict(kv=0), -2, "FP8"),
+])
+def test_paged_ex_rejects(opt_kw, kw, code, frag):
+    rc, msg = _paged(opts=_opts(**opt_kw), **kw)
     assert rc == code and frag in msg, (rc, msg)
 
 

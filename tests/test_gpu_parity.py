@@ -334,6 +334,53 @@ def test_paged_vec_matches_oracle(case, ps):
     compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_FP8, what=f"vec {case} ps{ps}")
 
 
+# ----------------------------------------------------------------------------- E4M3 queries
+def _paged_q8_run(d, mods_kw, Dv, vec=False):
+    """Paged call with E4M3 queries (fa_fwd_paged_ex), head-major or vectorised pages."""
+    e = synth.to_vectorized(d) if vec else d
+    q, qd = d["q"].to(DEV), d["q_descale"].to(DEV)
+    kc, vc = e["k_cache"].to(DEV), e["v_cache"].to(DEV)
+    Tq, Hq, Dqk = q.shape
+    Hkv, ps = kc.shape[1], (kc.shape[3] if vec else kc.shape[2])
+    B = len(d["lengths_k"])
+    msq, msk = max(d["lengths_q"]), max(d["lengths_k"])
+    o = _nan_like((Tq, Hq, Dv), torch.bfloat16)
+    lse = _nan_like((Hq, Tq), torch.float32)
+    n = fa.fa_fwd_paged_workspace_size(B, Tq, msq, msk, Hq, Hkv, Dqk, Dv, ps, fa.FA_FP8_E4M3)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+    fn = fa.fa_fwd_paged_vec if vec else fa.fa_fwd_paged
+    fn(q, kc, vc, o, lse, d["cu_q"].to(DEV), d["seqlen_k"].to(DEV), d["block_table"].to(DEV), msq, msk,
+       d["k_descale"].to(DEV), d["v_descale"].to(DEV), ws, fa.Mods(**mods_kw), q_descale=qd)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("case,ps", [("prefill", 64), ("chunked", 16), ("decode", 64), ("decode2rb", 32)])
+def test_paged_fp8_queries_match_oracle(case, ps):
+    """E4M3 queries with a per-tensor q descale (prefill converts them
+    exactly to bf16; decode feeds the codes to the FP8 product as they are);
+    head-major and vectorised pages give bitwise the same result."""
+    lq, lk, Hq, Hkv, Dqk, mods_kw = VEC_CASES[case]
+    d = synth.make_paged(lq, lk, Hq, Hkv, Dqk, 128, page_size=ps, seed=211 + ps, extra_pages=3, q_dtype="fp8")
+    o, lse = _paged_q8_run(d, mods_kw, 128)
+    o_ref, l_ref = oracle.attention_paged(f64(d["q"]), f64(d["k_cache"]), f64(d["v_cache"]), d["cu_q"],
+                                          d["seqlen_k"], d["block_table"], dict(mods_kw), float(d["k_descale"]),
+                                          float(d["v_descale"]), q_descale=float(d["q_descale"]))
+    compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_FP8, what=f"q8 {case} ps{ps}")
+    o2, l2 = _paged_q8_run(d, mods_kw, 128, vec=True)
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
+
+
+def test_paged_fp8_queries_need_q_descale():
+    d = synth.make_paged([1], [40], 16, 2, 192, 128, page_size=64, seed=5, q_dtype="fp8")
+    with pytest.raises(TypeError):
+        fa.fa_fwd_paged(d["q"].to(DEV), d["k_cache"].to(DEV), d["v_cache"].to(DEV),
+                        torch.empty((1, 16, 128), dtype=torch.bfloat16, device=DEV),
+                        torch.empty((16, 1), dtype=torch.float32, device=DEV), d["cu_q"].to(DEV),
+                        d["seqlen_k"].to(DEV), d["block_table"].to(DEV), 1, 40, d["k_descale"].to(DEV),
+                        d["v_descale"].to(DEV))
+
+
 # ----------------------------------------------------------------------------- decode
 @pytest.mark.parametrize("Hq,Hkv,Dqk,sq", [(16, 2, 192, 1), (8, 8, 128, 1), (16, 2, 192, 4), (64, 8, 192, 1)])
 def test_decode_small(Hq, Hkv, Dqk, sq):
