@@ -103,7 +103,7 @@ int clamp_i32(int64_t w) {
 }
 
 bool prefill_dims_built(int64_t dqk, int64_t dv, bool fp8, bool paged) {
-  if (fp8) return paged && ((dqk == 192 && dv == 128) || (dqk == 128 && dv == 128));
+  if (fp8) return paged && ((dqk == 192 && dv == 128) || (dqk == 128 && dv == 128) || (dqk == 192 && dv == 192));
   return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128);
 }
 
@@ -156,16 +156,19 @@ int check_common(int64_t B, int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v) 
 // Decode workers: one wavefront each.  With one 16-row block per wavefront
 // the kernel keeps two tiles in flight per wavefront and runs one wavefront
 // per SIMD (256 CUs x 4), which measured faster than two; with two row
-// blocks it keeps one tile in flight and runs two per SIMD.  Capped by the
-// tile count so small calls keep small workspaces.
-int64_t decode_workers(int64_t B, int64_t Hkv, int64_t slot_rows, int64_t kv_cap) {
-  const int64_t wmax = slot_rows > 16 ? 2048 : 1024;
+// blocks it keeps one tile in flight and runs two per SIMD.  Value width 192
+// needs the register file of one wavefront per SIMD: 1024 workers, two
+// tiles in flight.  Capped by the tile count so small calls keep small
+// workspaces.
+int64_t decode_workers(int64_t B, int64_t Hkv, int64_t slot_rows, int64_t kv_cap, int64_t d_v) {
+  const int64_t wmax = (slot_rows > 16 && d_v <= 128) ? 2048 : 1024;
   const int64_t tiles = B * Hkv * ((kv_cap + 31) / 32);
   return std::max<int64_t>(1, std::min(wmax, tiles));
 }
 
 bool uses_decode(int64_t max_sq, int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v, fa_dtype kv, int64_t page_size) {
-  if (kv != FA_FP8_E4M3 || d_v != 128 || (d_qk != 192 && d_qk != 128)) return false;
+  if (kv != FA_FP8_E4M3) return false;
+  if (!((d_v == 128 && (d_qk == 192 || d_qk == 128)) || (d_v == 192 && d_qk == 192))) return false;
   return max_sq >= 1 && max_sq * (Hq / Hkv) <= kDecodeRows;
 }
 
@@ -182,7 +185,7 @@ DecodeLayout decode_layout(int64_t B, int64_t max_sq, int64_t max_sk, int64_t Hq
   DecodeLayout L;
   L.slot_rows = max_sq * (Hq / Hkv);
   L.kv_cap = std::min(kv_cap, max_sk);
-  L.workers = decode_workers(B, Hkv, L.slot_rows, L.kv_cap);
+  L.workers = decode_workers(B, Hkv, L.slot_rows, L.kv_cap, d_v);
   L.slots = L.workers + B * Hkv;
   L.tiles_bytes = (size_t)((B + 1) * 4 + 255) / 256 * 256;
   L.o_bytes = (size_t)(L.slots * L.slot_rows * d_v) * sizeof(float);

@@ -68,12 +68,20 @@ namespace fa {
 constexpr int kDecWaves = 4;
 constexpr int kDecKT = 32;       // keys per tile
 
-// V tile rows are 128 bytes = 8 chunks of 16; chunk c of row r is stored at
-// c ^ dec_vswz(r).  A transposed read instruction takes, per group of 16
-// lanes g, rows {4g..4g+3, 16+4g..16+4g+3} at one chunk (two 8-byte halves):
-// with this map the even rows of lanes 0-31 (and of lanes 32-63), and the odd
-// rows, each cover all eight chunks, i.e. the 64 banks exactly once.
-__device__ __forceinline__ int dec_vswz(int r) { return ((r >> 1) & 3) | (((r >> 4) & 1) << 2); }
+// V tile rows are D_v bytes; chunk c (16 bytes) of row r is stored at
+// c ^ dec_vswz<D_v>(r).  A transposed read instruction takes, per group of 16
+// lanes g, rows {4g..4g+3, 16+4g..16+4g+3} at one chunk (two 8-byte halves).
+// 128-byte rows: with this map the even rows of lanes 0-31 (and of lanes
+// 32-63), and the odd rows, each cover all eight chunks, i.e. the 64 banks
+// exactly once.  192-byte rows (12 chunks): a row starts 48 banks after the
+// previous one, so rows 4 apart share banks; the map (inside the aligned
+// group of four chunks) gives the four rows of a half wavefront that share a
+// residue mod 4 four different chunks.
+template <int DV>
+__device__ __forceinline__ int dec_vswz(int r) {
+  if (DV == 192) return ((r >> 2) & 1) | (((r >> 4) & 1) << 1);
+  return ((r >> 1) & 3) | (((r >> 4) & 1) << 2);
+}
 
 // K tile rows are D_qk bytes (48 banks at 192); chunk c of row r is stored at
 // c ^ dec_kswz(r), which stays inside the aligned group of four chunks.  A
@@ -181,9 +189,11 @@ __global__ __launch_bounds__(256) void fa_decode_plan_kernel(const DecodePlanArg
 __device__ __forceinline__ int worker_of(int64_t i, int64_t T, int W) { return (int)(((i + 1) * W - 1) / T); }
 
 template <int DQK, int DV, int NRB, int NBUF, bool VEC, bool Q8>
-__global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(NBUF >= 3 ? 1 : (NRB == 1 && NBUF == 1 ? 3 : 2))))
+__global__ __launch_bounds__(kDecWaves * 64)
+__attribute__((amdgpu_waves_per_eu((NBUF >= 3 || DV > 128) ? 1 : (NRB == 1 && NBUF == 1 ? 3 : 2))))
 void fa_decode_kernel(const DecodeArgs a) {
-  static_assert(DQK % 32 == 0 && DV == 128 && (kDecKT * DQK) % 1024 == 0, "decode tile shapes");
+  static_assert(DQK % 32 == 0 && (DV == 128 || DV == 192) && (kDecKT * DQK) % 1024 == 0, "decode tile shapes");
+  constexpr int kVPerBlk = DV / 64;                     // V loads per 16-key block (vectorised pages)
   using T = DecTraits<DQK, DV>;
   constexpr int kSteps = DQK / 32;                      // K.Q^T MFMA steps per 16-key half
   constexpr int kDB = DV / 16;                          // 16-wide blocks of the output
@@ -214,20 +224,20 @@ void fa_decode_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int n = 0; n < T::kVLoads; ++n) {
     const int off = n * 1024 + lane * 16, row = off / DV;
-    vst[n] = row * DV + ((((off % DV) >> 4) ^ dec_vswz(row)) << 4);
+    vst[n] = row * DV + ((((off % DV) >> 4) ^ dec_vswz<DV>(row)) << 4);
   }
   // transposed V reads: lanes 2t+q of key group kgrp take row vrow(t), half q
   const int t8 = (lane & 15) >> 1, vq = lane & 1;
   const int vrow = t8 < 4 ? 4 * kgrp + t8 : 16 + 4 * kgrp + (t8 - 4);
   const char FA_LDS* vrd = vlds + vrow * DV + vq * 8;
-  const int vsw = dec_vswz(vrow);
+  const int vsw = dec_vswz<DV>(vrow);
   // V^T tile (vectorised pages): row d is 32 bytes, byte 8 kgrp + e holds key
   // (e / 4) * 16 + 4 kgrp + e % 4, so the lanes of key group kgrp read their
   // 8 bytes of row 16 blk + lane%16 at 8-byte unit kgrp.  Rows 8-15 of every
   // 16 swap unit pairs (0,1) <-> (2,3): the 16 rows x 2 units of a half
   // wavefront then cover the 64 banks once.
   const char FA_LDS* vtrd = vlds + (lane & 15) * 32 + ((kgrp ^ (((lane >> 3) & 1) << 1)) << 3);
-  const int vtst = lane * 32;                         // row d = lane (and 64 + lane)
+  const int vtst = lane * 32;                         // row d = lane (and 64 + lane, ...)
   const int vtsw = ((lane >> 3) & 1) << 4;            // 16-byte half swap of rows 8-15
   // K fragment reads: row kh*16 + lane%16 (the swizzle of r and r+16 agree),
   // chunk 2 st + kgrp/2, half kgrp%2
@@ -308,15 +318,16 @@ void fa_decode_kernel(const DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < T::kKLoads; ++i)
           kb[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(kp + ((2 * i) << (a.page_shift + 4))));
-        // V: load n takes dims 64 (n%2) + l of block n/2
+        // V: load n takes dims 64 (n % kVPerBlk) + l of block n / kVPerBlk
         const uint8_t* vt0 = vbase + p0 * a.v_pg + ((k0 & pmask) >> 4) * (DV * 16) + lane * 16;
         const uint8_t* vt1 = vbase + p1 * a.v_pg + (((k0 + 16) & pmask) >> 4) * (DV * 16) + lane * 16;
 #pragma unroll
         for (int n = 0; n < T::kVLoads; ++n)
-          vb[n] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>((n < 2 ? vt0 : vt1) + (n & 1) * 1024));
+          vb[n] = __builtin_nontemporal_load(
+              reinterpret_cast<const i32x4*>((n < kVPerBlk ? vt0 : vt1) + (n % kVPerBlk) * 1024));
         if (nv < kDecKT) {
 #pragma unroll
-          for (int n = 0; n < T::kVLoads; ++n) vb[n] = keep_bytes(vb[n], nv - 16 * (n >> 1));
+          for (int n = 0; n < T::kVLoads; ++n) vb[n] = keep_bytes(vb[n], nv - 16 * (n / kVPerBlk));
         }
         return;
       }
@@ -406,11 +417,11 @@ void fa_decode_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < T::kKLoads; ++i) *reinterpret_cast<i32x4 FA_LDS*>(klds + kst[i]) = kb[i];
       if (VEC) {
-        // row d = lane from loads 0 (block 0) and 2 (block 1), row 64 + lane
-        // from loads 1 and 3: dword j of block b goes to dword 2 j + b
+        // row d = 64 hr + lane from loads hr (block 0) and kVPerBlk + hr
+        // (block 1): dword j of block b goes to dword 2 j + b
 #pragma unroll
-        for (int hr = 0; hr < 2; ++hr) {
-          const i32x4 b0 = vb[hr], b1 = vb[2 + hr];
+        for (int hr = 0; hr < kVPerBlk; ++hr) {
+          const i32x4 b0 = vb[hr], b1 = vb[kVPerBlk + hr];
           char FA_LDS* row = vlds + vtst + hr * 64 * 32;
           *reinterpret_cast<i32x4 FA_LDS*>(row + vtsw) = i32x4{b0[0], b1[0], b0[1], b1[1]};
           *reinterpret_cast<i32x4 FA_LDS*>(row + (16 ^ vtsw)) = i32x4{b0[2], b1[2], b0[3], b1[3]};
@@ -625,24 +636,27 @@ __global__ __launch_bounds__(256) void fa_combine_kernel(const CombineArgs a) {
 
 hipError_t decode_dispatch(const DecodePlanArgs& plan, const DecodeArgs& a, int dqk, int dv, bool fp8, bool vec,
                            bool q8, hipStream_t stream, bool* supported) {
-  *supported = fp8 && dv == 128 && (dqk == 192 || dqk == 128);
+  *supported = fp8 && ((dv == 128 && (dqk == 192 || dqk == 128)) || (dv == 192 && dqk == 192));
   if (!*supported) return hipSuccess;
   hipLaunchKernelGGL(fa_decode_plan_kernel, dim3(1), dim3(256), 0, stream, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((a.n_workers + kDecWaves - 1) / kDecWaves);
   const bool two = a.slot_rows > 16;
-#define FA_DEC(DQ, VC, Q)                                                                                  \
-  if (dqk == DQ && vec == VC && q8 == Q) {                                                                 \
-    if (two) hipLaunchKernelGGL((fa_decode_kernel<DQ, 128, 2, 1, VC, Q>), grid, dim3(kDecWaves * 64), 0, stream, a); \
-    else hipLaunchKernelGGL((fa_decode_kernel<DQ, 128, 1, 2, VC, Q>), grid, dim3(kDecWaves * 64), 0, stream, a);  \
+#define FA_DEC(DQ, DVV, VC, Q)                                                                           \
+  if (dqk == DQ && dv == DVV && vec == VC && q8 == Q) {                                                    \
+    if (two) hipLaunchKernelGGL((fa_decode_kernel<DQ, DVV, 2, (DVV > 128 ? 2 : 1), VC, Q>), grid, dim3(kDecWaves * 64), 0, \
+                                stream, a);                                                                \
+    else hipLaunchKernelGGL((fa_decode_kernel<DQ, DVV, 1, 2, VC, Q>), grid, dim3(kDecWaves * 64), 0, stream, a);  \
     return hipGetLastError();                                                                              \
   }
-#define FA_DEC2(DQ, VC) FA_DEC(DQ, VC, false) FA_DEC(DQ, VC, true)
-  FA_DEC2(192, false)
-  FA_DEC2(128, false)
-  FA_DEC2(192, true)
-  FA_DEC2(128, true)
+#define FA_DEC2(DQ, DVV, VC) FA_DEC(DQ, DVV, VC, false) FA_DEC(DQ, DVV, VC, true)
+  FA_DEC2(192, 128, false)
+  FA_DEC2(128, 128, false)
+  FA_DEC2(192, 128, true)
+  FA_DEC2(128, 128, true)
+  FA_DEC2(192, 192, false)
+  FA_DEC2(192, 192, true)
 #undef FA_DEC2
 #undef FA_DEC
   *supported = false;
@@ -655,6 +669,10 @@ hipError_t combine_dispatch(const CombineArgs& a, int dv, hipStream_t stream, bo
   const dim3 grid((unsigned)((items + 3) / 4));
   if (dv == 128) {
     hipLaunchKernelGGL((fa_combine_kernel<128>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  if (dv == 192) {
+    hipLaunchKernelGGL((fa_combine_kernel<192>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   *supported = false;

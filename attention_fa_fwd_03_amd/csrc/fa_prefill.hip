@@ -703,8 +703,8 @@ static hipError_t launch_prefill(const PrefillArgs& a, int n_bh, int n_qtiles, h
 
 // Instantiated shapes: (D_qk, D_v) in {(64,64), (128,128)} for bf16 K/V
 // (dense, varlen, paged) with every score-mod combination; (192,128) and
-// (128,128) for FP8 E4M3 paged caches without score mods, head-major or
-// vectorised pages.
+// (128,128) and (192,192) for FP8 E4M3 paged caches without score mods,
+// head-major or vectorised pages.
 hipError_t prefill_dispatch(const PrefillArgs& a, int dqk, int dv, bool fp8, bool paged, bool vec, int mods,
                             int n_bh, int n_qtiles, hipStream_t stream, bool* supported) {
   *supported = true;
@@ -722,6 +722,8 @@ hipError_t prefill_dispatch(const PrefillArgs& a, int dqk, int dv, bool fp8, boo
   FA_CASE(128, 128, true, true, false, 0)
   FA_CASE(192, 128, true, true, true, 0)
   FA_CASE(128, 128, true, true, true, 0)
+  FA_CASE(192, 192, true, true, false, 0)
+  FA_CASE(192, 192, true, true, true, 0)
 #undef FA_MODS4
 #undef FA_CASE
   *supported = false;

@@ -122,11 +122,12 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  * Only the first ceil(seqlen_k[b] / page_size) entries of a block-table row
  * are read, and bytes past seqlen_k in a page never influence the result.
  * page_size: a power of two in [1, 1024].
- * Built: FP8 (d_qk, d_v) in {(192, 128), (128, 128)}; bf16 (64, 64), (128, 128).
+ * Built: FP8 (d_qk, d_v) in {(192, 128), (128, 128), (192, 192)} (192/192:
+ * the V192 variant of the paged FP8 PR); bf16 (64, 64), (128, 128).
  * Mods: FA_CAUSAL and FA_WINDOW only.
- * When max_seqlen_q * (Hq / Hkv) <= 32 (decode), kv_dtype is FP8 and d_v is
- * 128, the keys are split and partial results merged; that path needs a
- * device workspace of fa_fwd_paged_workspace_size(...) bytes (else
+ * When max_seqlen_q * (Hq / Hkv) <= 32 (decode) and kv_dtype is FP8, the
+ * keys are split and partial results merged; that path needs a device
+ * workspace of fa_fwd_paged_workspace_size(...) bytes (else
  * FA_ERR_WORKSPACE).
  * The workspace is scratch, overwritten by the call.
  */

@@ -381,6 +381,41 @@ def test_paged_fp8_queries_need_q_descale():
                         d["v_descale"].to(DEV))
 
 
+# ----------------------------------------------------------------------------- value width 192
+# (lengths_q, lengths_k, Hq, Hkv, mods): Q/K and V/O width 192
+V192_CASES = {
+    "prefill": ([70, 3, 128, 129, 300], [70, 3, 128, 129, 300], 4, 4, dict(causal=True)),
+    "chunked": ([40, 64, 100], [300, 64, 1000], 4, 2, dict(causal=True)),
+    "decode": ([1] * 6, [1, 31, 33, 64, 1000, 3000], 16, 2, dict(causal=True)),
+    "decode2rb": ([2, 1, 2, 0, 2], [0, 1, 33, 64, 2100], 32, 2, dict(causal=True, window=(100, 0))),
+}
+
+
+@pytest.mark.parametrize("ps", [64, 16])
+@pytest.mark.parametrize("case", sorted(V192_CASES))
+def test_paged_v192_matches_oracle(case, ps):
+    """D_qk = D_v = 192 (the pages' V192 variant) over FP8 pages: oracle
+    parity on head-major pages, bitwise equality on vectorised pages."""
+    lq, lk, Hq, Hkv, mods_kw = V192_CASES[case]
+    d = synth.make_paged(lq, lk, Hq, Hkv, 192, 192, page_size=ps, seed=231 + ps, extra_pages=3)
+    o, lse = _paged_run(d, mods_kw, 192)
+    o_ref, l_ref = _paged_ref(d, mods_kw)
+    compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_FP8, what=f"v192 {case} ps{ps}")
+    o2, l2 = _paged_vec_run(d, mods_kw, 192)
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
+
+
+@pytest.mark.parametrize("case", ["chunked", "decode2rb"])
+def test_paged_v192_fp8_queries(case):
+    lq, lk, Hq, Hkv, mods_kw = V192_CASES[case]
+    d = synth.make_paged(lq, lk, Hq, Hkv, 192, 192, page_size=64, seed=241, extra_pages=2, q_dtype="fp8")
+    o, lse = _paged_q8_run(d, mods_kw, 192, vec=True)
+    o_ref, l_ref = oracle.attention_paged(f64(d["q"]), f64(d["k_cache"]), f64(d["v_cache"]), d["cu_q"],
+                                          d["seqlen_k"], d["block_table"], dict(mods_kw), float(d["k_descale"]),
+                                          float(d["v_descale"]), q_descale=float(d["q_descale"]))
+    compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_FP8, what=f"v192 q8 {case}")
+
+
 # ----------------------------------------------------------------------------- decode
 @pytest.mark.parametrize("Hq,Hkv,Dqk,sq", [(16, 2, 192, 1), (8, 8, 128, 1), (16, 2, 192, 4), (64, 8, 192, 1)])
 def test_decode_small(Hq, Hkv, Dqk, sq):
