@@ -10,7 +10,7 @@ before timing starts.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
                   [--flex alibi|softcap|window|bernoulli|block_causal|none|causal] [--page-size P]
-                  [--layout head_major|vec] [--q-dtype bf16|fp8]
+                  [--layout head_major|vec] [--q-dtype bf16|fp8] [--dv 128|192]
                   [--no-cpu-baseline]
                   [--copy-calibration]
   python bench.py --config N --traffic-from FETCH_CSV WRITE_CSV
@@ -19,7 +19,8 @@ before timing starts.
 FP8 prefill, 4 paged FP8 decode, 5 flex); the default line is config 2.
 --layout vec runs configs 3 and 4 on the vectorised 5-D page format
 (fa_fwd_paged_vec) instead of head-major pages; --q-dtype fp8 gives them
-E4M3 queries with a per-tensor descale (fa_fwd_paged_ex).
+E4M3 queries with a per-tensor descale (fa_fwd_paged_ex); --dv 192 runs them
+with value/output width 192.
 Prints ONE JSON line.
 """
 from __future__ import annotations
@@ -117,7 +118,7 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, key: str, kind: str) -
 
 
 def build_workload(cfg: int, flex: str, torch, synth, fa, page_size: int = 64, layout: str = "head_major",
-                   q_dtype: str = "bf16"):
+                   q_dtype: str = "bf16", dv: int = 128):
     """Returns (name, run_fn, work dict, oracle sample fn)."""
     dev = "cuda"
     if cfg == 1:
@@ -152,45 +153,45 @@ def build_workload(cfg: int, flex: str, torch, synth, fa, page_size: int = 64, l
             {"seqlens": lens, "total_tokens": T, "H": 16, "D": 128, "causal": True}, sample
     if cfg == 3:
         L = [2048] * 4
-        d = synth.make_paged(L, L, 16, 16, 192, 128, page_size=64, seed=synth.seed_for(3), device=dev,
+        d = synth.make_paged(L, L, 16, 16, 192, dv, page_size=64, seed=synth.seed_for(3), device=dev,
                              q_dtype=q_dtype)
         if layout == "vec":
             d = synth.to_vectorized(d)
         fn = fa.fa_fwd_paged_vec if layout == "vec" else fa.fa_fwd_paged
-        o = torch.empty(8192, 16, 128, dtype=torch.bfloat16, device=dev)
+        o = torch.empty(8192, 16, dv, dtype=torch.bfloat16, device=dev)
         lse = torch.empty(16, 8192, dtype=torch.float32, device=dev)
         mods = fa.Mods(causal=True)
-        flops = 64 * 2048 * 2049 // 2 * (2 * 192 + 2 * 128)
+        flops = 64 * 2048 * 2049 // 2 * (2 * 192 + 2 * dv)
         run = lambda: fn(d["q"], d["k_cache"], d["v_cache"], o, lse, d["cu_q"], d["seqlen_k"],
                          d["block_table"], 2048, 2048, d["k_descale"], d["v_descale"], None, mods,
                          q_descale=d["q_descale"])
-        name = "paged FP8 causal prefill 4x2048 H16 Dqk192 Dv128 page64" + (" vectorised" if layout == "vec" else "") \
+        name = f"paged FP8 causal prefill 4x2048 H16 Dqk192 Dv{dv} page64" + (" vectorised" if layout == "vec" else "") \
             + (" fp8-q" if q_dtype == "fp8" else "")
         return name, run, dict(flops=flops, kind="prefill", bound="mfma"), \
-            {"B": 4, "S": 2048, "H": 16, "d_qk": 192, "d_v": 128, "page_size": 64, "layout": layout,
+            {"B": 4, "S": 2048, "H": 16, "d_qk": 192, "d_v": dv, "page_size": 64, "layout": layout,
              "q_dtype": q_dtype}, None
     if cfg == 4:
         lk = synth.make_decode_lengths(synth.seed_for(4))
         lq = [1] * 64
         ps = page_size
-        d = synth.make_paged(lq, lk, 64, 8, 192, 128, page_size=ps, seed=synth.seed_for(4), device=dev,
+        d = synth.make_paged(lq, lk, 64, 8, 192, dv, page_size=ps, seed=synth.seed_for(4), device=dev,
                              q_dtype=q_dtype)
         if layout == "vec":
             d = synth.to_vectorized(d)
             torch.cuda.empty_cache()
         fn = fa.fa_fwd_paged_vec if layout == "vec" else fa.fa_fwd_paged
-        o = torch.empty(64, 64, 128, dtype=torch.bfloat16, device=dev)
+        o = torch.empty(64, 64, dv, dtype=torch.bfloat16, device=dev)
         lse = torch.empty(64, 64, dtype=torch.float32, device=dev)
-        n = fa.fa_fwd_paged_workspace_size(64, 64, 1, max(lk), 64, 8, 192, 128, ps)
+        n = fa.fa_fwd_paged_workspace_size(64, 64, 1, max(lk), 64, 8, 192, dv, ps)
         ws = torch.empty(n, dtype=torch.uint8, device=dev)
         mods = fa.Mods(causal=True)
-        kv_bytes = sum(lk) * 8 * (192 + 128)
-        io_bytes = 64 * 64 * 192 * (1 if q_dtype == "fp8" else 2) + 64 * 64 * 128 * 2 + 64 * 64 * 4 + sum(math.ceil(x / ps) for x in lk) * 4
-        flops = sum(lk) * 64 * (2 * 192 + 2 * 128)
+        kv_bytes = sum(lk) * 8 * (192 + dv)
+        io_bytes = 64 * 64 * 192 * (1 if q_dtype == "fp8" else 2) + 64 * 64 * dv * 2 + 64 * 64 * 4 + sum(math.ceil(x / ps) for x in lk) * 4
+        flops = sum(lk) * 64 * (2 * 192 + 2 * dv)
         run = lambda: fn(d["q"], d["k_cache"], d["v_cache"], o, lse, d["cu_q"], d["seqlen_k"],
                          d["block_table"], 1, max(lk), d["k_descale"], d["v_descale"], ws, mods,
                          q_descale=d["q_descale"])
-        name = f"paged FP8 decode 64 seqs ctx U[1024,32768] GQA 64/8 Dqk192 Dv128 page{ps}" + \
+        name = f"paged FP8 decode 64 seqs ctx U[1024,32768] GQA 64/8 Dqk192 Dv{dv} page{ps}" + \
             (" vectorised" if layout == "vec" else "") + (" fp8-q" if q_dtype == "fp8" else "")
 
         def sample():
@@ -214,11 +215,11 @@ def build_workload(cfg: int, flex: str, torch, synth, fa, page_size: int = 64, l
                                                                   dict(causal=True), kd, vd, workers=_cores(),
                                                                   layout="vectorized" if layout == "vec"
                                                                   else "head_major", q_descale=qd))
-            sbytes = sum(lk[:n_seq]) * 8 * (192 + 128)
+            sbytes = sum(lk[:n_seq]) * 8 * (192 + dv)
             return dict(seconds=dt, work=sbytes * reps,
                         sample=f"sequences 0-{n_seq - 1} ({sum(lk[:n_seq])} cached tokens, all heads), {reps} passes")
         return name, run, dict(flops=flops, bytes=kv_bytes + io_bytes, kind="decode", bound="hbm"), \
-            {"B": 64, "ctx_total": sum(lk), "Hq": 64, "Hkv": 8, "page_size": ps, "layout": layout,
+            {"B": 64, "ctx_total": sum(lk), "Hq": 64, "Hkv": 8, "d_v": dv, "page_size": ps, "layout": layout,
              "q_dtype": q_dtype}, sample
     if cfg == 5:
         B, H, S, D = 2, 16, 8192, 128
@@ -288,6 +289,7 @@ def main():
                     help="paged configs: head-major or vectorised 5-D pages")
     ap.add_argument("--q-dtype", choices=["bf16", "fp8"], default="bf16",
                     help="paged configs: bf16 or E4M3 queries")
+    ap.add_argument("--dv", type=int, choices=[128, 192], default=128, help="paged configs: value/output width")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (reference for HBM byte counters)")
@@ -301,6 +303,8 @@ def main():
         key += "_vec"
     if args.config in (3, 4) and args.q_dtype == "fp8":
         key += "_q8"
+    if args.config in (3, 4) and args.dv != 128:
+        key += f"_dv{args.dv}"
     if args.traffic_from:
         kind = "decode" if args.config == 4 else "prefill"
         print(json.dumps({key: traffic_from_counters(args.traffic_from[0], args.traffic_from[1], key, kind)}))
@@ -316,7 +320,7 @@ def main():
 
     torch.cuda.init()
     name, run, work, cfg_extra, sample = build_workload(args.config, args.flex, torch, synth, fa, args.page_size,
-                                                       args.layout, args.q_dtype)
+                                                       args.layout, args.q_dtype, args.dv)
     if args.copy_calibration:
         # reference for the HBM byte counters: one device-to-device copy of
         # COPY_BYTES through the HIP runtime's own copy kernel
