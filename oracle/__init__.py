@@ -18,6 +18,9 @@ beyond optional row chunking that does not change any result):
   * FP8 caches  OCP E4M3 (e4m3fn) bytes decoded bit-field by bit-field, times
                 the per-tensor descale
   * split-KV    merging per-split (O_s, LSE_s) partials by their LSE weights
+  * KV write    E4M3 encoding (ties to even, saturating) of x / descale with the
+                per-tensor descale amax/448, placed by a slot mapping into
+                head-major or vectorised pages (oracle.kvcache)
 
 Sources (pages of the method):
   * "Add forward LSE output to FlyDSL flash attention kernels" (FlyDSL PR 844),
@@ -43,7 +46,8 @@ Every function here is pinned by CPU tests (closed forms, brute force,
 library special cases); none is "parity unpinned" except the *semantics* of
 the score mods, which the pages name but print no values for.
 """
-from .e4m3 import decode_e4m3  # noqa: F401
+from .e4m3 import decode_e4m3, encode_e4m3  # noqa: F401
+from .kvcache import amax_descale, quantize_rows, kv_cache_write  # noqa: F401
 from .attention import visible, attend, lse_merge  # noqa: F401
 from .layouts import (  # noqa: F401
     attention_dense,

@@ -430,3 +430,106 @@ def test_fp8_query_descale_acts_as_a_logit_scale():
     o3, l3 = oracle.attention_paged(*args, dict(causal=True, scale=0.1), kd, vd, q_descale=c)
     assert np.allclose(o1, o2, atol=1e-12) and np.allclose(l1, l2, atol=1e-12)
     assert not np.allclose(l1, l3, atol=1e-3)
+
+
+# ----------------------------------------------------------------------------- E4M3 encoding, KV-cache write
+def _golden_points():
+    with open(os.path.join(os.path.dirname(__file__), "golden", "e4m3_points.json")) as f:
+        return [(int(c, 16), v) for c, v in json.load(f)["points"]]
+
+
+def test_e4m3_encode_golden_points():
+    for c, v in _golden_points():
+        if v == "nan":
+            assert oracle.encode_e4m3(np.float32("nan")) & 0x7F == 0x7F
+        else:
+            assert int(oracle.encode_e4m3(np.float32(v))) == c, (hex(c), v)
+
+
+def test_e4m3_encode_round_trips_every_code():
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    vals = oracle.decode_e4m3(codes).astype(np.float32)
+    assert np.array_equal(oracle.encode_e4m3(vals), codes)
+
+
+def test_e4m3_encode_ties_go_to_even_and_halves_split():
+    """Midpoints between neighbouring codes go to the even code; a hair
+    either side goes to the nearer one (brute force over the code table)."""
+    for c in range(0, 0x7E):
+        lo, hi = oracle.decode_e4m3(np.uint8(c)), oracle.decode_e4m3(np.uint8(c + 1))
+        mid = np.float32((lo + hi) / 2)
+        assert float(mid) == (lo + hi) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert int(oracle.encode_e4m3(mid)) == even
+        assert int(oracle.encode_e4m3(np.nextafter(mid, np.float32(0)))) == c
+        assert int(oracle.encode_e4m3(np.nextafter(mid, np.float32(1e9)))) == c + 1
+        assert int(oracle.encode_e4m3(-mid)) == even | 0x80
+
+
+def test_e4m3_encode_saturates():
+    big = np.array([448.0, 464.0, 479.9, 1e6, np.inf], dtype=np.float32)
+    assert np.all(oracle.encode_e4m3(big) == 0x7E)
+    assert np.all(oracle.encode_e4m3(-big) == 0xFE)
+
+
+def test_e4m3_encode_matches_torch_cast_in_range():
+    x = torch.randn(200000, generator=torch.Generator().manual_seed(5)) * 60
+    x = x.clamp(-448, 448)
+    x[:1000] = x[:1000] * 1e-3            # subnormal range
+    want = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.encode_e4m3(x.numpy()), want)
+
+
+def test_amax_descale_rule():
+    assert oracle.amax_descale(np.array([0.0, 3.5, -896.0])) == np.float32(2.0)
+    assert oracle.amax_descale(np.zeros(5)) == np.float32(2.0 ** -126)
+    x = np.array([1.0, -0.3], dtype=np.float32)
+    assert oracle.amax_descale(x) == np.float32(np.float32(1.0) / np.float32(448.0))
+
+
+@pytest.mark.parametrize("layout", ["head_major", "vectorized"])
+def test_kv_cache_write_places_and_quantises(layout):
+    """Each mapped token lands in its slot with codes within half an E4M3
+    step of x / descale; skipped and untouched slots keep their bytes; the
+    vectorised cache is the head-major one under the pages' layout map."""
+    g = np.random.default_rng(3)
+    T, Hkv, Dqk, Dv, P, ps = 37, 2, 64, 32, 6, 16
+    k = g.standard_normal((T, Hkv, Dqk)).astype(np.float32)
+    v = g.standard_normal((T, Hkv, Dv)).astype(np.float32)
+    slots = g.permutation(P * ps)[:T].astype(np.int64)
+    slots[4], slots[9] = -1, P * ps + 3
+    kc0 = np.full((P, Hkv, ps, Dqk), 0x7F, np.uint8)
+    vc0 = np.full((P, Hkv, ps, Dv), 0x7F, np.uint8)
+    kc, vc, kd, vd = oracle.kv_cache_write(k, v, slots, kc0, vc0, ps)
+    assert kd == oracle.amax_descale(k) and vd == oracle.amax_descale(v)
+    written = set()
+    for t, sl in enumerate(slots):
+        if t in (4, 9):
+            continue
+        p, s = divmod(int(sl), ps)
+        written.add((p, s))
+        for x, c, dsc in ((k[t], kc[p, :, s], kd), (v[t], vc[p, :, s], vd)):
+            y = x / dsc
+            back = oracle.decode_e4m3(c)
+            step = np.exp2(np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -6))) - 3)
+            assert np.all(np.abs(back - y) <= step / 2 + 1e-6)
+    for p in range(P):
+        for s in range(ps):
+            if (p, s) not in written:
+                assert np.all(kc[p, :, s] == 0x7F) and np.all(vc[p, :, s] == 0x7F)
+    if layout == "vectorized":
+        kv0 = synth.to_vectorized(dict(k_cache=torch.from_numpy(kc0), v_cache=torch.from_numpy(vc0)))
+        kcv, vcv, _, _ = oracle.kv_cache_write(k, v, slots, kv0["k_cache"].numpy(), kv0["v_cache"].numpy(), ps,
+                                               layout="vectorized")
+        ref = synth.to_vectorized(dict(k_cache=torch.from_numpy(kc), v_cache=torch.from_numpy(vc)))
+        assert np.array_equal(kcv, ref["k_cache"].numpy()) and np.array_equal(vcv, ref["v_cache"].numpy())
+
+
+def test_kv_cache_write_given_descale():
+    k = np.array([[[1.0] * 16]], dtype=np.float32)
+    v = np.array([[[-2.0] * 16]], dtype=np.float32)
+    kc, vc, kd, vd = oracle.kv_cache_write(k, v, [3], np.zeros((1, 1, 4, 16), np.uint8),
+                                           np.zeros((1, 1, 4, 16), np.uint8), 4, k_descale=0.5, v_descale=0.25)
+    assert kd == np.float32(0.5) and np.all(kc[0, 0, 3] == 0x40)     # 2.0
+    assert np.all(vc[0, 0, 3] == 0xD0)                               # -8.0
+    assert np.all(kc[0, 0, :3] == 0)
