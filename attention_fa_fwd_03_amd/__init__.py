@@ -22,6 +22,10 @@ from .binding import (  # noqa: F401
     FA_PAGES_HEAD_MAJOR,
     FA_PAGES_VECTORIZED,
     fa_fwd_paged_workspace_size,
+    fa_kv_cache_write_fp8,
+    fa_kv_cache_write_fp8_workspace_size,
+    FA_SCALE_GIVEN,
+    FA_SCALE_AMAX,
     fa_last_error,
     fa_abi_version,
     library_path,

@@ -69,6 +69,11 @@ lib.fa_fwd_paged_vec.restype = ctypes.c_int
 lib.fa_fwd_paged_ex.argtypes = ([_vp] * 8 + [_i64] * 11 + [ctypes.c_int, _vp, _vp, _vp, _sz,
                                                             ctypes.POINTER(_FaPagedOpts), ctypes.POINTER(_FaMods), _vp])
 lib.fa_fwd_paged_ex.restype = ctypes.c_int
+lib.fa_kv_cache_write_fp8.argtypes = ([_vp] * 3 + [_i64] * 4 + [_vp, _vp, _i64, _i64, ctypes.c_int32, _vp, _vp,
+                                                                 ctypes.c_int32, _vp, _sz, _vp])
+lib.fa_kv_cache_write_fp8.restype = ctypes.c_int
+lib.fa_kv_cache_write_fp8_workspace_size.argtypes = [_i64] * 4
+lib.fa_kv_cache_write_fp8_workspace_size.restype = _sz
 lib.fa_fwd_paged_workspace_size.argtypes = [_i64] * 9 + [ctypes.c_int]
 lib.fa_fwd_paged_workspace_size.restype = _sz
 lib.fa_last_error.argtypes = []
@@ -268,3 +273,45 @@ def _paged_call(layout, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, blo
     else:
         fn = lib.fa_fwd_paged_vec if layout == FA_PAGES_VECTORIZED else lib.fa_fwd_paged
         _check(fn(*args, _mods(mods), _stream(stream, q.device)))
+
+
+FA_SCALE_GIVEN, FA_SCALE_AMAX = 0, 1
+
+
+def fa_kv_cache_write_fp8_workspace_size(T, Hkv, d_qk, d_v) -> int:
+    return int(lib.fa_kv_cache_write_fp8_workspace_size(T, Hkv, d_qk, d_v))
+
+
+def fa_kv_cache_write_fp8(k, v, slot_mapping, k_cache, v_cache, k_descale, v_descale, compute_scale=True,
+                          workspace=None, stream=None):
+    """Quantise bf16 rows k [T,Hkv,Dqk], v [T,Hkv,Dv] to E4M3 and write them
+    into uint8 paged caches (see include/fa.h).  Caches: head-major 4-D
+    [P,Hkv,page,D] or vectorised 5-D (K [P,Hkv,Dqk/16,page,16], V
+    [P,Hkv,page/16,Dv,16]).  compute_scale: write per-tensor descales
+    amax/448 first (needs a workspace); else use the ones given."""
+    T, Hkv, Dqk = k.shape
+    Dv = v.shape[2]
+    _need(k, "k", torch.bfloat16)
+    _need(v, "v", torch.bfloat16, (T, Hkv, Dv))
+    _need(slot_mapping, "slot_mapping", torch.int64, (T,))
+    _need(k_descale, "k_descale", torch.float32)
+    _need(v_descale, "v_descale", torch.float32)
+    if k_cache.dim() == 5:
+        P, _, _, ps, _ = k_cache.shape
+        _need(k_cache, "k_cache", torch.uint8, (P, Hkv, Dqk // 16, ps, 16))
+        _need(v_cache, "v_cache", torch.uint8, (P, Hkv, ps // 16, Dv, 16))
+        layout = FA_PAGES_VECTORIZED
+    else:
+        P, _, ps, _ = k_cache.shape
+        _need(k_cache, "k_cache", torch.uint8, (P, Hkv, ps, Dqk))
+        _need(v_cache, "v_cache", torch.uint8, (P, Hkv, ps, Dv))
+        layout = FA_PAGES_HEAD_MAJOR
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        _need(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib.fa_kv_cache_write_fp8(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), T, Hkv, Dqk, Dv,
+                                     k_cache.data_ptr(), v_cache.data_ptr(), P, ps, layout,
+                                     k_descale.data_ptr(), v_descale.data_ptr(),
+                                     FA_SCALE_AMAX if compute_scale else FA_SCALE_GIVEN, ws_ptr or None, ws_bytes,
+                                     _stream(stream, k.device)))

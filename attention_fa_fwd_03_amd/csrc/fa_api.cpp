@@ -193,6 +193,13 @@ DecodeLayout decode_layout(int64_t B, int64_t max_sq, int64_t max_sk, int64_t Hq
   return L;
 }
 
+// Reduction blocks of the KV-cache writer's per-tensor maximum: enough to
+// fill the chip, at least 32 elements per thread.
+int kv_amax_blocks(int64_t n) {
+  const int64_t b = (n + 256 * 8 * 4 - 1) / (256 * 8 * 4);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(b, 2048));
+}
+
 size_t workspace_bytes(int64_t B, int64_t total_q, int64_t max_sq, int64_t max_sk, int64_t Hq, int64_t Hkv,
                        int64_t d_qk, int64_t d_v, fa_dtype kv, int64_t page_size) {
   (void)total_q;
@@ -504,6 +511,81 @@ int fa_fwd_paged_ex(const void* q, const void* k_cache, const void* v_cache, voi
   return paged_impl(opts, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, B, total_q,
                     max_seqlen_q, max_seqlen_k, num_pages, page_size, max_pages_per_seq, Hq, Hkv, d_qk, d_v,
                     kv_dtype, k_descale, v_descale, workspace, workspace_bytes_in, mods, stream);
+}
+
+size_t fa_kv_cache_write_fp8_workspace_size(int64_t T, int64_t Hkv, int64_t d_qk, int64_t d_v) {
+  if (T <= 0 || Hkv <= 0 || d_qk <= 0 || d_v <= 0) return 0;
+  return (size_t)(kv_amax_blocks(T * Hkv * d_qk) + kv_amax_blocks(T * Hkv * d_v)) * sizeof(float);
+}
+
+int fa_kv_cache_write_fp8(const void* k, const void* v, const int64_t* slot_mapping,
+                          int64_t T, int64_t Hkv, int64_t d_qk, int64_t d_v,
+                          void* k_cache, void* v_cache, int64_t num_pages, int64_t page_size,
+                          int32_t page_layout, float* k_descale, float* v_descale, int32_t scale_mode,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (T < 0 || num_pages < 0) return fail(FA_ERR_INVALID, "T and num_pages must be >= 0");
+  if (Hkv <= 0 || d_qk <= 0 || d_v <= 0) return fail(FA_ERR_INVALID, "Hkv and head dims must be positive");
+  if (d_qk % 16 || d_v % 16) return fail(FA_ERR_UNSUPPORTED, "head dims must be multiples of 16");
+  if (page_layout != FA_PAGES_HEAD_MAJOR && page_layout != FA_PAGES_VECTORIZED)
+    return fail(FA_ERR_INVALID, "unknown page_layout %d", (int)page_layout);
+  if (scale_mode != FA_SCALE_GIVEN && scale_mode != FA_SCALE_AMAX)
+    return fail(FA_ERR_INVALID, "unknown scale_mode %d", (int)scale_mode);
+  const bool vec = page_layout == FA_PAGES_VECTORIZED;
+  if (page_size < (vec ? 16 : 1) || page_size > 1024 || (page_size & (page_size - 1)))
+    return fail(FA_ERR_UNSUPPORTED, "page_size must be a power of two in [%d, 1024], got %lld", vec ? 16 : 1,
+                (long long)page_size);
+  if (T >= kI32 || Hkv >= kI32 || d_qk > 65536 || d_v > 65536) return fail(FA_ERR_LIMIT, "sizes exceed the limits");
+  if (T == 0) return FA_OK;
+  if (!k || !v || !slot_mapping || !k_descale || !v_descale)
+    return fail(FA_ERR_INVALID, "k, v, slot_mapping and the descales must be non-NULL");
+  if (num_pages > 0 && (!k_cache || !v_cache)) return fail(FA_ERR_INVALID, "caches must be non-NULL");
+  const size_t nk = (size_t)(T * Hkv * d_qk) * 2, nv = (size_t)(T * Hkv * d_v) * 2;
+  const size_t ck = (size_t)num_pages * Hkv * page_size * d_qk, cv = (size_t)num_pages * Hkv * page_size * d_v;
+  if (overlaps(k_cache, ck, v_cache, cv) || overlaps(k_cache, ck, k, nk) || overlaps(k_cache, ck, v, nv) ||
+      overlaps(v_cache, cv, k, nk) || overlaps(v_cache, cv, v, nv))
+    return fail(FA_ERR_INVALID, "caches must not overlap each other or the rows");
+  if (overlaps(k_descale, 4, v_descale, 4)) return fail(FA_ERR_INVALID, "k_descale and v_descale must differ");
+  int shift = 0;
+  while ((1ll << shift) < page_size) ++shift;
+  const hipStream_t st = (hipStream_t)stream;
+  if (scale_mode == FA_SCALE_AMAX) {
+    const size_t need = fa_kv_cache_write_fp8_workspace_size(T, Hkv, d_qk, d_v);
+    if (!workspace || workspace_bytes < need)
+      return fail(FA_ERR_WORKSPACE, "FA_SCALE_AMAX needs a workspace of %zu bytes (got %zu)", need, workspace_bytes);
+    fa::KvAmaxArgs m{};
+    m.k = (const __bf16*)k;
+    m.v = (const __bf16*)v;
+    m.n_k = T * Hkv * d_qk;
+    m.n_v = T * Hkv * d_v;
+    m.nb_k = kv_amax_blocks(m.n_k);
+    m.nb_v = kv_amax_blocks(m.n_v);
+    m.partial = (float*)workspace;
+    m.k_descale = k_descale;
+    m.v_descale = v_descale;
+    hipError_t e = fa::kv_amax_dispatch(m, st);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "amax launch failed: %s", hipGetErrorString(e));
+  }
+  if (num_pages == 0) return FA_OK;
+  fa::KvWriteArgs w{};
+  w.k = (const __bf16*)k;
+  w.v = (const __bf16*)v;
+  w.slot_mapping = slot_mapping;
+  w.k_cache = k_cache;
+  w.v_cache = v_cache;
+  w.k_descale = k_descale;
+  w.v_descale = v_descale;
+  w.T = T;
+  w.Hkv = Hkv;
+  w.d_qk = (int)d_qk;
+  w.d_v = (int)d_v;
+  w.num_pages = num_pages;
+  w.page_shift = shift;
+  const int64_t items = T * Hkv * ((d_qk + d_v) / 16);
+  const int blocks = (int)std::min<int64_t>((items + 255) / 256, 8192);
+  hipError_t e = fa::kv_write_dispatch(w, vec, blocks, st);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "cache write launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
 }
 
 }  // extern "C"

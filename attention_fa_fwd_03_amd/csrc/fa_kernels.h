@@ -98,6 +98,34 @@ struct CombineArgs {
   int n_workers, slot_rows;
 };
 
+// FP8 KV-cache write (fa_kvcache.hip).
+struct KvAmaxArgs {
+  const __bf16* k;
+  const __bf16* v;
+  int64_t n_k, n_v;            // elements of k and v (multiples of 16)
+  int nb_k, nb_v;              // reduction blocks per tensor
+  float* partial;              // [nb_k + nb_v] per-block maxima
+  float* k_descale;            // outputs: max(amax / 448, 2^-126)
+  float* v_descale;
+};
+
+struct KvWriteArgs {
+  const __bf16* k;             // [T, Hkv, d_qk] token-major
+  const __bf16* v;             // [T, Hkv, d_v]
+  const int64_t* slot_mapping; // [T]: page * page_size + slot, < 0 skips
+  void* k_cache;
+  void* v_cache;
+  const float* k_descale;
+  const float* v_descale;
+  int64_t T, Hkv;
+  int d_qk, d_v;
+  int64_t num_pages;
+  int page_shift;
+};
+
+hipError_t kv_amax_dispatch(const KvAmaxArgs& a, hipStream_t stream);
+hipError_t kv_write_dispatch(const KvWriteArgs& a, bool vec, int blocks, hipStream_t stream);
+
 hipError_t prefill_dispatch(const PrefillArgs& a, int dqk, int dv, bool fp8, bool paged, bool vec, int mods,
                             int n_bh, int n_qtiles, hipStream_t stream, bool* supported);
 hipError_t decode_dispatch(const DecodePlanArgs& plan, const DecodeArgs& a, int dqk, int dv, bool fp8, bool vec,

@@ -201,6 +201,43 @@ size_t fa_fwd_paged_workspace_size(int64_t B, int64_t total_q, int64_t max_seqle
                                    int64_t max_seqlen_k, int64_t Hq, int64_t Hkv, int64_t d_qk,
                                    int64_t d_v, int64_t page_size, fa_dtype kv_dtype);
 
+/* fa_kv_cache_write_fp8 scale_mode */
+#define FA_SCALE_GIVEN 0  /* quantise with the descales already in *k_descale / *v_descale */
+#define FA_SCALE_AMAX 1   /* first set *k_descale = max(max|k| / 448, 2^-126), same for v */
+
+/*
+ * Quantise new K/V rows to OCP E4M3 and write them into paged caches (the
+ * step before the FP8 paged entry points).  Method: the GPU quantisation of
+ * the fp8 KV-cache page ("flash_attention: prologue fusion, mma tensor
+ * cores, fp8 KV cache, flex attention + block sparsity", part 3: scale from
+ * the largest magnitude over 448) with the per-tensor descales of the paged
+ * FP8 PR.
+ * k [T, Hkv, d_qk] and v [T, Hkv, d_v] are bf16, token-major; d_qk and d_v
+ * are multiples of 16 (else FA_ERR_UNSUPPORTED).  slot_mapping (device
+ * int64 [T]) sends token t to page slot_mapping[t] / page_size, slot
+ * slot_mapping[t] % page_size; a negative entry, or one at or past
+ * num_pages * page_size, skips the token.  Caches are uint8 in page_layout
+ * (FA_PAGES_HEAD_MAJOR: [num_pages, Hkv, page_size, d]; FA_PAGES_VECTORIZED:
+ * K [num_pages, Hkv, d_qk/16, page_size, 16], V [num_pages, Hkv,
+ * page_size/16, d_v, 16], page_size >= 16); page_size a power of two <= 1024.
+ * Each element becomes E4M3(x * (1 / descale)), fp32 steps with a correctly
+ * rounded division, nearest with ties to even, saturating at +-448.
+ * k_descale / v_descale are device fp32 scalars: read (FA_SCALE_GIVEN; they
+ * must be positive and finite) or written first (FA_SCALE_AMAX, which needs
+ * a device workspace of fa_kv_cache_write_fp8_workspace_size(...) bytes,
+ * else FA_ERR_WORKSPACE).  Inputs must be finite.  Bytes of slots not
+ * written keep their values; two tokens mapped to one slot race.  T = 0
+ * writes nothing, descales included.
+ */
+int fa_kv_cache_write_fp8(const void* k, const void* v, const int64_t* slot_mapping,
+                          int64_t T, int64_t Hkv, int64_t d_qk, int64_t d_v,
+                          void* k_cache, void* v_cache, int64_t num_pages, int64_t page_size,
+                          int32_t page_layout, float* k_descale, float* v_descale, int32_t scale_mode,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_kv_cache_write_fp8 needs in FA_SCALE_AMAX mode. */
+size_t fa_kv_cache_write_fp8_workspace_size(int64_t T, int64_t Hkv, int64_t d_qk, int64_t d_v);
+
 /* Message describing the last non-zero return on this thread ("" if none). */
 const char* fa_last_error(void);
 

@@ -191,3 +191,39 @@ def test_workspace_size_query():
     assert fa.fa_fwd_paged_workspace_size(4, 8192, 2048, 2048, 16, 16, 192, 128, 64) == 0
     # bf16 caches never take the split path
     assert fa.fa_fwd_paged_workspace_size(64, 64, 1, 32768, 64, 8, 192, 128, 64, fa.FA_BF16) == 0
+
+
+def _kvw(**kw):
+    fa = _lib()
+    a = dict(k=FAKE, v=FAKE * 2, sm=FAKE * 3, T=10, Hkv=2, dqk=192, dv=128, kc=FAKE * 4, vc=FAKE * 40,
+             P=4, ps=64, layout=0, kd=FAKE * 80, vd=FAKE * 81, mode=1, ws=FAKE * 90, wsb=1 << 20)
+    a.update(kw)
+    rc = fa.lib.fa_kv_cache_write_fp8(a["k"], a["v"], a["sm"], a["T"], a["Hkv"], a["dqk"], a["dv"], a["kc"], a["vc"],
+                                      a["P"], a["ps"], a["layout"], a["kd"], a["vd"], a["mode"], a["ws"], a["wsb"],
+                                      None)
+    return rc, fa.fa_last_error()
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(dqk=200), -2, "multiples of 16"),
+    (dict(layout=3), -1, "page_layout"),
+    (dict(mode=2), -1, "scale_mode"),
+    (dict(layout=1, ps=8), -2, "[16, 1024]"),
+    (dict(ps=48), -2, "power of two"),
+    (dict(ws=0), -4, "workspace"),
+    (dict(wsb=4), -4, "workspace"),
+    (dict(sm=0), -1, "non-NULL"),
+    (dict(vd=FAKE * 80), -1, "differ"),
+    (dict(T=-1), -1, ">= 0"),
+])
+def test_kv_cache_write_rejects(kw, code, frag):
+    rc, msg = _kvw(**kw)
+    assert rc == code and frag in msg, (rc, msg)
+
+
+def test_kv_cache_write_empty_and_workspace_query():
+    fa = _lib()
+    assert _kvw(T=0, k=0, v=0, sm=0, ws=0)[0] == 0
+    assert fa.fa_kv_cache_write_fp8_workspace_size(0, 8, 192, 128) == 0
+    n = fa.fa_kv_cache_write_fp8_workspace_size(1000, 8, 192, 128)
+    assert 0 < n < 1 << 16 and n % 4 == 0

@@ -416,6 +416,89 @@ def test_paged_v192_fp8_queries(case):
     compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_FP8, what=f"v192 q8 {case}")
 
 
+# ----------------------------------------------------------------------------- FP8 KV-cache write
+def _kv_rows(T, Hkv, Dqk, Dv, seed, special=False):
+    g = torch.Generator().manual_seed(seed)
+    k = (torch.randn((T, Hkv, Dqk), generator=g) * 3).to(torch.bfloat16)
+    v = (torch.randn((T, Hkv, Dv), generator=g) * 0.5).to(torch.bfloat16)
+    if special:
+        # every E4M3 midpoint (ties), values near them, the subnormal range
+        # and values past 448, all exact in bf16
+        codes = torch.arange(0, 0x7E, dtype=torch.int64)
+        lo = torch.from_numpy(oracle.decode_e4m3(codes.numpy().astype("uint8")))
+        hi = torch.from_numpy(oracle.decode_e4m3((codes + 1).numpy().astype("uint8")))
+        mids = ((lo + hi) / 2).to(torch.bfloat16)
+        extra = torch.tensor([448.0, 460.0, 500.0, 1e4, -1e4, 2 ** -10, 3 * 2 ** -10, -(2 ** -8), 0.0, -0.0],
+                             dtype=torch.bfloat16)
+        vals = torch.cat([mids, -mids, extra])
+        flat = k.view(-1)
+        flat[: vals.numel()] = vals
+    return k, v
+
+
+@pytest.mark.parametrize("layout,ps", [("head_major", 64), ("head_major", 1), ("vectorized", 16),
+                                       ("vectorized", 64)])
+@pytest.mark.parametrize("given", [False, True])
+def test_kv_cache_write_is_bitwise_the_oracle(layout, ps, given):
+    """Codes and descales bitwise equal to the oracle: random rows, every
+    E4M3 midpoint, subnormals and saturation (given descale 1 for K), with
+    skipped and out-of-range slots; untouched bytes keep their NaN fill."""
+    T, Hkv, Dqk, Dv, P = 300, 2, 192, 128, 24
+    k, v = _kv_rows(T, Hkv, Dqk, Dv, seed=ps + 7, special=given)
+    g = torch.Generator().manual_seed(ps)
+    slots = torch.randperm(P * ps, generator=g)[:T].to(torch.int64)
+    if P * ps < T:
+        slots = torch.randint(0, P * ps, (T,), generator=g)
+        slots = torch.unique(slots)
+        slots = torch.cat([slots, torch.full((T - slots.numel(),), -1, dtype=torch.int64)])
+    slots[5], slots[17] = -1, P * ps + 100
+    if layout == "head_major":
+        kc0 = torch.full((P, Hkv, ps, Dqk), 0x7F, dtype=torch.uint8)
+        vc0 = torch.full((P, Hkv, ps, Dv), 0x7F, dtype=torch.uint8)
+    else:
+        kc0 = torch.full((P, Hkv, Dqk // 16, ps, 16), 0x7F, dtype=torch.uint8)
+        vc0 = torch.full((P, Hkv, ps // 16, Dv, 16), 0x7F, dtype=torch.uint8)
+    kd0, vd0 = (1.0, 0.02) if given else (None, None)
+    kc_r, vc_r, kd_r, vd_r = oracle.kv_cache_write(k.float().numpy(), v.float().numpy(), slots.numpy(), kc0.numpy(),
+                                                   vc0.numpy(), ps, layout, kd0, vd0)
+    kc, vc = kc0.to(DEV), vc0.to(DEV)
+    kd = torch.tensor([kd0 if given else float("nan")], dtype=torch.float32, device=DEV)
+    vd = torch.tensor([vd0 if given else float("nan")], dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(fa.fa_kv_cache_write_fp8_workspace_size(T, Hkv, Dqk, Dv), 4), dtype=torch.uint8, device=DEV)
+    fa.fa_kv_cache_write_fp8(k.to(DEV), v.to(DEV), slots.to(DEV), kc, vc, kd, vd, compute_scale=not given,
+                             workspace=ws)
+    torch.cuda.synchronize()
+    assert np.float32(kd.item()) == np.float32(kd_r) and np.float32(vd.item()) == np.float32(vd_r)
+    assert np.array_equal(kc.cpu().numpy(), kc_r), (kc.cpu().numpy() != kc_r).sum()
+    assert np.array_equal(vc.cpu().numpy(), vc_r), (vc.cpu().numpy() != vc_r).sum()
+
+
+def test_kv_cache_write_then_decode():
+    """A cache filled by the writer serves the decode path: same result as
+    the oracle attention over the oracle-written cache."""
+    lk = [100, 1000, 37]
+    B, Hq, Hkv, ps = 3, 16, 2, 64
+    d = synth.make_paged([1] * B, lk, Hq, Hkv, 192, 128, page_size=ps, seed=251, extra_pages=4)
+    T = sum(lk)
+    k, v = _kv_rows(T, Hkv, 192, 128, seed=3)
+    bt = d["block_table"]
+    slots = torch.cat([bt[b, torch.arange(lk[b]) // ps].long() * ps + torch.arange(lk[b]) % ps for b in range(B)])
+    kc = torch.full_like(d["k_cache"], 0x7F).to(DEV)
+    vc = torch.full_like(d["v_cache"], 0x7F).to(DEV)
+    kd = torch.empty(1, dtype=torch.float32, device=DEV)
+    vd = torch.empty(1, dtype=torch.float32, device=DEV)
+    ws = torch.empty(fa.fa_kv_cache_write_fp8_workspace_size(T, Hkv, 192, 128), dtype=torch.uint8, device=DEV)
+    fa.fa_kv_cache_write_fp8(k.to(DEV), v.to(DEV), slots.to(DEV), kc, vc, kd, vd, workspace=ws)
+    e = dict(d, k_cache=kc, v_cache=vc, k_descale=kd, v_descale=vd)
+    o, lse = _paged_run(e, dict(causal=True), 128)
+    kc_r, vc_r, kd_r, vd_r = oracle.kv_cache_write(k.float().numpy(), v.float().numpy(), slots.numpy(),
+                                                   torch.full_like(d["k_cache"], 0x7F).numpy(),
+                                                   torch.full_like(d["v_cache"], 0x7F).numpy(), ps)
+    o_ref, l_ref = oracle.attention_paged(f64(d["q"]), kc_r, vc_r, d["cu_q"], d["seqlen_k"], d["block_table"],
+                                          dict(causal=True), float(kd_r), float(vd_r))
+    compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_FP8, what="written cache")
+
+
 # ----------------------------------------------------------------------------- decode
 @pytest.mark.parametrize("Hq,Hkv,Dqk,sq", [(16, 2, 192, 1), (8, 8, 128, 1), (16, 2, 192, 4), (64, 8, 192, 1)])
 def test_decode_small(Hq, Hkv, Dqk, sq):
