@@ -36,6 +36,7 @@ constexpr int64_t kI32 = (int64_t)1 << 31;
 constexpr int kBM = 128;           // prefill query rows per workgroup
 constexpr int kMaskBQ = 128;       // block-mask query tiles: multiples of a workgroup's rows
 constexpr int kBN = 64;            // prefill keys per tile
+constexpr int kKvLdsBytes = 24576;  // KV-cache writer: LDS for 16 tokens' codes per workgroup
 constexpr int kDecodeRows = 32;    // decode rows (query x q-head-in-group) per wavefront
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -535,7 +536,9 @@ int fa_kv_cache_write_fp8(const void* k, const void* v, const int64_t* slot_mapp
   if (page_size < (vec ? 16 : 1) || page_size > 1024 || (page_size & (page_size - 1)))
     return fail(FA_ERR_UNSUPPORTED, "page_size must be a power of two in [%d, 1024], got %lld", vec ? 16 : 1,
                 (long long)page_size);
-  if (T >= kI32 || Hkv >= kI32 || d_qk > 65536 || d_v > 65536) return fail(FA_ERR_LIMIT, "sizes exceed the limits");
+  if (T >= kI32 || Hkv >= kI32) return fail(FA_ERR_LIMIT, "T and Hkv must stay below 2^31");
+  if (d_qk + d_v > kKvLdsBytes / 16)
+    return fail(FA_ERR_UNSUPPORTED, "d_qk + d_v must be at most %d", kKvLdsBytes / 16);
   if (T == 0) return FA_OK;
   if (!k || !v || !slot_mapping || !k_descale || !v_descale)
     return fail(FA_ERR_INVALID, "k, v, slot_mapping and the descales must be non-NULL");
@@ -581,9 +584,8 @@ int fa_kv_cache_write_fp8(const void* k, const void* v, const int64_t* slot_mapp
   w.d_v = (int)d_v;
   w.num_pages = num_pages;
   w.page_shift = shift;
-  const int64_t items = T * Hkv * ((d_qk + d_v) / 16);
-  const int blocks = (int)std::min<int64_t>((items + 255) / 256, 8192);
-  hipError_t e = fa::kv_write_dispatch(w, vec, blocks, st);
+  w.heads_per_pass = (int)std::min<int64_t>(Hkv, kKvLdsBytes / (16 * (d_qk + d_v)));
+  hipError_t e = fa::kv_write_dispatch(w, vec, st);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "cache write launch failed: %s", hipGetErrorString(e));
   return FA_OK;
 }

@@ -121,10 +121,11 @@ struct KvWriteArgs {
   int d_qk, d_v;
   int64_t num_pages;
   int page_shift;
+  int heads_per_pass;          // kv-heads per workgroup (16 tokens of them fit in LDS)
 };
 
 hipError_t kv_amax_dispatch(const KvAmaxArgs& a, hipStream_t stream);
-hipError_t kv_write_dispatch(const KvWriteArgs& a, bool vec, int blocks, hipStream_t stream);
+hipError_t kv_write_dispatch(const KvWriteArgs& a, bool vec, hipStream_t stream);
 
 hipError_t prefill_dispatch(const PrefillArgs& a, int dqk, int dv, bool fp8, bool paged, bool vec, int mods,
                             int n_bh, int n_qtiles, hipStream_t stream, bool* supported);

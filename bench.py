@@ -16,7 +16,8 @@ before timing starts.
   python bench.py --config N --traffic-from FETCH_CSV WRITE_CSV
 
 --config selects another workload for investigation (1 dense D64, 3 paged
-FP8 prefill, 4 paged FP8 decode, 5 flex); the default line is config 2.
+FP8 prefill, 4 paged FP8 decode, 5 flex, 6 FP8 KV-cache write of the decode
+cache); the default line is config 2.
 --layout vec runs configs 3 and 4 on the vectorised 5-D page format
 (fa_fwd_paged_vec) instead of head-major pages; --q-dtype fp8 gives them
 E4M3 queries with a per-tensor descale (fa_fwd_paged_ex); --dv 192 runs them
@@ -40,13 +41,15 @@ METRIC = "attention fwd TFLOP/s + fraction of MFMA peak; paged-decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 COPY_BYTES = 256 << 20        # calibration copy for the HBM byte counters
-DOMINANT = {"prefill": "fa_prefill_kernel", "decode": "fa_decode_kernel"}
+DOMINANT = {"prefill": "fa_prefill_kernel", "decode": "fa_decode_kernel", "kvwrite": "fa_kv_write_kernel"}
 KERNEL_SOURCES = {
     "prefill": ["attention_fa_fwd_03_amd/csrc/fa_prefill.hip", "attention_fa_fwd_03_amd/csrc/fa_prefill_common.h",
                 "attention_fa_fwd_03_amd/csrc/fa_device.h",
                 "attention_fa_fwd_03_amd/csrc/fa_kernels.h"],
     "decode": ["attention_fa_fwd_03_amd/csrc/fa_decode.hip", "attention_fa_fwd_03_amd/csrc/fa_device.h",
                "attention_fa_fwd_03_amd/csrc/fa_kernels.h"],
+    "kvwrite": ["attention_fa_fwd_03_amd/csrc/fa_kvcache.hip", "attention_fa_fwd_03_amd/csrc/fa_device.h",
+                "attention_fa_fwd_03_amd/csrc/fa_kernels.h"],
 }
 
 
@@ -255,6 +258,35 @@ def build_workload(cfg: int, flex: str, torch, synth, fa, page_size: int = 64, l
         name = f"flex {flex} B2 H16 S8192 D128 bf16"
         return name, run, dict(flops=flops, bytes=byts, kind="prefill", bound=bound), \
             {"B": B, "H": H, "S": S, "D": D, "mod": flex}, None
+    if cfg == 6:
+        # every token of the decode cache (64 sequences, contexts U[1024, 32768],
+        # 8 kv-heads, 192/128) quantised from bf16 with per-tensor amax
+        # descales and written into pages of page_size (shuffled)
+        lk = synth.make_decode_lengths(synth.seed_for(4))
+        T, Hkv, ps = sum(lk), 8, page_size
+        g = torch.Generator(device=dev).manual_seed(synth.seed_for(6))
+        k = torch.randn((T, Hkv, 192), generator=g, device=dev).to(torch.bfloat16)
+        v = torch.randn((T, Hkv, dv), generator=g, device=dev).to(torch.bfloat16)
+        P = (T + ps - 1) // ps
+        slots = torch.randperm(P, generator=g, device=dev).repeat_interleave(ps)[:T] * ps + \
+            torch.arange(T, device=dev) % ps
+        if layout == "vec":
+            kc = torch.empty((P, Hkv, 12, ps, 16), dtype=torch.uint8, device=dev)
+            vc = torch.empty((P, Hkv, ps // 16, dv, 16), dtype=torch.uint8, device=dev)
+        else:
+            kc = torch.empty((P, Hkv, ps, 192), dtype=torch.uint8, device=dev)
+            vc = torch.empty((P, Hkv, ps, dv), dtype=torch.uint8, device=dev)
+        kd = torch.empty(1, dtype=torch.float32, device=dev)
+        vd = torch.empty(1, dtype=torch.float32, device=dev)
+        ws = torch.empty(fa.fa_kv_cache_write_fp8_workspace_size(T, Hkv, 192, dv), dtype=torch.uint8, device=dev)
+        run = lambda: fa.fa_kv_cache_write_fp8(k, v, slots, kc, vc, kd, vd, workspace=ws)
+        # the per-tensor maximum must see every row before any code is
+        # written: two reads of the bf16 rows, one write of the codes
+        byts = 2 * T * Hkv * (192 + dv) * 2 + T * Hkv * (192 + dv) + T * 8
+        name = f"FP8 KV-cache write {T} tokens Hkv8 D192/{dv} page{ps} amax descales" + \
+            (" vectorised" if layout == "vec" else "")
+        return name, run, dict(flops=0, bytes=byts, kind="kvwrite", bound="hbm"), \
+            {"T": T, "Hkv": Hkv, "d_qk": 192, "d_v": dv, "page_size": ps, "layout": layout}, None
     raise SystemExit(f"unknown config {cfg}")
 
 
@@ -299,6 +331,8 @@ def main():
     key = f"config{args.config}" + (f"_{args.flex}" if args.config == 5 else "")
     if args.config == 4 and args.page_size != 64:
         key += f"_ps{args.page_size}"
+    if args.config == 6:
+        key += f"_ps{args.page_size}" + ("_vec" if args.layout == "vec" else "") + (f"_dv{args.dv}" if args.dv != 128 else "")
     if args.config in (3, 4) and args.layout == "vec":
         key += "_vec"
     if args.config in (3, 4) and args.q_dtype == "fp8":
@@ -306,7 +340,7 @@ def main():
     if args.config in (3, 4) and args.dv != 128:
         key += f"_dv{args.dv}"
     if args.traffic_from:
-        kind = "decode" if args.config == 4 else "prefill"
+        kind = {4: "decode", 6: "kvwrite"}.get(args.config, "prefill")
         print(json.dumps({key: traffic_from_counters(args.traffic_from[0], args.traffic_from[1], key, kind)}))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -394,13 +428,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("fp8-qkv/bf16" if args.q_dtype == "fp8" else "fp8-kv/bf16") if args.config in (3, 4) else "bf16",
+        "dtype": ("fp8-qkv/bf16" if args.q_dtype == "fp8" else "fp8-kv/bf16") if args.config in (3, 4)
+        else ("bf16->fp8" if args.config == 6 else "bf16"),
         "data": "synthetic",
         "config": {"workload": name, **cfg_extra},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
-    if work["bound"] == "hbm":
+    if work["bound"] == "hbm" and work["flops"]:
         line["config"]["tflops"] = round(tflops, 3)
     print(json.dumps(line))
 
