@@ -18,6 +18,8 @@ beyond optional row chunking that does not change any result):
   * FP8 caches  OCP E4M3 (e4m3fn) bytes decoded bit-field by bit-field, times
                 the per-tensor descale
   * split-KV    merging per-split (O_s, LSE_s) partials by their LSE weights
+  * backward    dV = P^T dO, dS = P (dO V^T - Delta), dQ = scale dS K, dK = scale dS^T Q
+                (oracle.backward)
   * KV write    E4M3 encoding (ties to even, saturating) of x / descale with the
                 per-tensor descale amax/448, placed by a slot mapping into
                 head-major or vectorised pages (oracle.kvcache)
@@ -48,6 +50,7 @@ the score mods, which the pages name but print no values for.
 """
 from .e4m3 import decode_e4m3, encode_e4m3  # noqa: F401
 from .kvcache import amax_descale, quantize_rows, kv_cache_write  # noqa: F401
+from .backward import attend_bwd, attention_bwd_dense, attention_bwd_varlen  # noqa: F401
 from .attention import visible, attend, lse_merge  # noqa: F401
 from .layouts import (  # noqa: F401
     attention_dense,

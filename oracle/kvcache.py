@@ -17,7 +17,8 @@ Readings (the pages give the scale rule, not the arithmetic order):
     the conversion ties-to-even and saturating at 448 (encode_e4m3);
   * token t goes to page slot_mapping[t] // page_size, slot
     slot_mapping[t] % page_size; a negative entry skips the token, as does
-    one past the cache.
+    one past the cache; with no rows at all nothing is written, descales
+    included.
 """
 from __future__ import annotations
 
@@ -53,6 +54,8 @@ def kv_cache_write(k, v, slot_mapping, k_cache, v_cache, page_size, layout="head
     v = np.asarray(v, dtype=np.float32)
     slot_mapping = np.asarray(slot_mapping, dtype=np.int64)
     kc, vc = np.array(k_cache, dtype=np.uint8, copy=True), np.array(v_cache, dtype=np.uint8, copy=True)
+    if k.shape[0] == 0:                   # nothing to write: caches and descales untouched
+        return kc, vc, k_descale, v_descale
     kd = amax_descale(k) if k_descale is None else np.float32(k_descale)
     vd = amax_descale(v) if v_descale is None else np.float32(v_descale)
     kq, vq = quantize_rows(k, kd), quantize_rows(v, vd)

@@ -533,3 +533,71 @@ def test_kv_cache_write_given_descale():
     assert kd == np.float32(0.5) and np.all(kc[0, 0, 3] == 0x40)     # 2.0
     assert np.all(vc[0, 0, 3] == 0xD0)                               # -8.0
     assert np.all(kc[0, 0, :3] == 0)
+
+
+# ----------------------------------------------------------------------------- backward
+def _loss(q, k, v, do, mods):
+    o, _ = oracle.attention_dense(q, k, v, mods)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("sq,skv,mods", [(5, 7, dict(causal=True)), (7, 5, dict(causal=True)),
+                                         (6, 6, dict()), (6, 9, dict(window=(2, 1))), (8, 3, dict(causal=True))])
+def test_backward_matches_finite_differences(sq, skv, mods):
+    """Central differences of sum(dO * O) from the forward oracle, at every
+    coordinate of q, k and v (tiny shapes, GQA 4/2 so dK and dV sum over a
+    group; rows without a visible key included)."""
+    g = np.random.default_rng(sq * 10 + skv)
+    q = g.standard_normal((1, sq, 4, 3))
+    k = g.standard_normal((1, skv, 2, 3))
+    v = g.standard_normal((1, skv, 2, 2))
+    do = g.standard_normal((1, sq, 4, 2))
+    dq, dk, dv = oracle.attention_bwd_dense(q, k, v, do, mods)
+    h = 1e-6
+    for x, dx in ((q, dq), (k, dk), (v, dv)):
+        for idx in np.ndindex(x.shape):
+            x0 = x[idx]
+            x[idx] = x0 + h
+            lp = _loss(q, k, v, do, mods)
+            x[idx] = x0 - h
+            lm = _loss(q, k, v, do, mods)
+            x[idx] = x0
+            assert abs((lp - lm) / (2 * h) - dx[idx]) < 1e-7, (idx, (lp - lm) / (2 * h), dx[idx])
+
+
+def test_backward_matches_torch_autograd_fp64():
+    """torch autograd through a plain fp64 softmax attention (library case),
+    causal with more keys than queries (no empty rows), varlen driver."""
+    g = torch.Generator().manual_seed(9)
+    lq, lk = [5, 9], [8, 9]
+    cu_q, cu_k = np.cumsum([0] + lq), np.cumsum([0] + lk)
+    q = torch.randn(sum(lq), 2, 8, generator=g, dtype=torch.float64, requires_grad=True)
+    k = torch.randn(sum(lk), 1, 8, generator=g, dtype=torch.float64, requires_grad=True)
+    v = torch.randn(sum(lk), 1, 4, generator=g, dtype=torch.float64, requires_grad=True)
+    do = torch.randn(sum(lq), 2, 4, generator=g, dtype=torch.float64)
+    outs = []
+    for b in range(2):
+        qb, kb, vb = q[cu_q[b]:cu_q[b + 1]], k[cu_k[b]:cu_k[b + 1]], v[cu_k[b]:cu_k[b + 1]]
+        s = torch.einsum("ihd,jd->hij", qb, kb[:, 0]) / math.sqrt(8)
+        i = torch.arange(lq[b])[:, None] + lk[b] - lq[b]
+        s = s.masked_fill(torch.arange(lk[b])[None, :] > i, float("-inf"))
+        outs.append(torch.einsum("hij,jd->ihd", torch.softmax(s, dim=-1), vb[:, 0]))
+    (torch.cat(outs) * do).sum().backward()
+    dq, dk, dv = oracle.attention_bwd_varlen(q.detach().numpy(), k.detach().numpy(), v.detach().numpy(),
+                                             do.numpy(), cu_q, cu_k, dict(causal=True))
+    assert np.allclose(dq, q.grad.numpy(), atol=1e-12)
+    assert np.allclose(dk, k.grad.numpy(), atol=1e-12)
+    assert np.allclose(dv, v.grad.numpy(), atol=1e-12)
+
+
+def test_backward_delta_is_rowsum_do_o():
+    """Delta_i = sum_j P_ij dP_ij equals dO_i . O_i (the form the kernels use)."""
+    g = np.random.default_rng(2)
+    q, k, v, do = g.standard_normal((6, 4)), g.standard_normal((9, 4)), g.standard_normal((9, 3)), \
+        g.standard_normal((6, 3))
+    vis = oatt.visible(6, 9, causal=True)
+    o, _ = oatt.attend(q, k, v, 0.5, vis)
+    s = np.where(vis, 0.5 * q @ k.T, -np.inf)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    assert np.allclose((p * (do @ v.T)).sum(axis=1), (do * o).sum(axis=1), atol=1e-12)
