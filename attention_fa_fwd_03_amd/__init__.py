@@ -23,6 +23,9 @@ from .binding import (  # noqa: F401
     FA_PAGES_VECTORIZED,
     fa_fwd_paged_workspace_size,
     fa_kv_cache_write_fp8,
+    fa_bwd_dense,
+    fa_bwd_varlen,
+    fa_bwd_workspace_size,
     fa_kv_cache_write_fp8_workspace_size,
     FA_SCALE_GIVEN,
     FA_SCALE_AMAX,

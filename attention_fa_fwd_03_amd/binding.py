@@ -74,6 +74,12 @@ lib.fa_kv_cache_write_fp8.argtypes = ([_vp] * 3 + [_i64] * 4 + [_vp, _vp, _i64, 
 lib.fa_kv_cache_write_fp8.restype = ctypes.c_int
 lib.fa_kv_cache_write_fp8_workspace_size.argtypes = [_i64] * 4
 lib.fa_kv_cache_write_fp8_workspace_size.restype = _sz
+lib.fa_bwd_dense.argtypes = [_vp] * 9 + [_i64] * 7 + [ctypes.POINTER(_FaMods), _vp, _sz, _vp]
+lib.fa_bwd_dense.restype = ctypes.c_int
+lib.fa_bwd_varlen.argtypes = [_vp] * 11 + [_i64] * 9 + [ctypes.POINTER(_FaMods), _vp, _sz, _vp]
+lib.fa_bwd_varlen.restype = ctypes.c_int
+lib.fa_bwd_workspace_size.argtypes = [_i64, _i64]
+lib.fa_bwd_workspace_size.restype = _sz
 lib.fa_fwd_paged_workspace_size.argtypes = [_i64] * 9 + [ctypes.c_int]
 lib.fa_fwd_paged_workspace_size.restype = _sz
 lib.fa_last_error.argtypes = []
@@ -315,3 +321,51 @@ def fa_kv_cache_write_fp8(k, v, slot_mapping, k_cache, v_cache, k_descale, v_des
                                      k_descale.data_ptr(), v_descale.data_ptr(),
                                      FA_SCALE_AMAX if compute_scale else FA_SCALE_GIVEN, ws_ptr or None, ws_bytes,
                                      _stream(stream, k.device)))
+
+
+def fa_bwd_workspace_size(total_q, Hq) -> int:
+    return int(lib.fa_bwd_workspace_size(total_q, Hq))
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    _need(workspace, "workspace")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def fa_bwd_dense(q, k, v, o, dout, lse, dq, dk, dv, mods=None, workspace=None, stream=None):
+    """dQ, dK, dV of the dense forward (see include/fa.h): q/o/dout/dq
+    [B,Sq,Hq,D], k/v/dk/dv [B,Skv,Hkv,D] bf16, lse [B,Hq,Sq] fp32."""
+    B, Sq, Hq, Dqk = q.shape
+    _, Skv, Hkv, Dv = v.shape
+    for t, n, shp in ((q, "q", None), (k, "k", (B, Skv, Hkv, Dqk)), (v, "v", None), (o, "o", (B, Sq, Hq, Dv)),
+                      (dout, "dout", (B, Sq, Hq, Dv)), (dq, "dq", tuple(q.shape)), (dk, "dk", tuple(k.shape)),
+                      (dv, "dv", tuple(v.shape))):
+        _need(t, n, torch.bfloat16, shp)
+    _need(lse, "lse", torch.float32, (B, Hq, Sq))
+    ws, wsb = _ws(workspace)
+    _check(lib.fa_bwd_dense(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Sq, Skv, Hq, Hkv, Dqk, Dv, _mods(mods),
+                            ws, wsb, _stream(stream, q.device)))
+
+
+def fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                  mods=None, workspace=None, stream=None):
+    """dQ, dK, dV of the varlen forward: q/o/dout/dq [Tq,Hq,D], k/v/dk/dv
+    [Tk,Hkv,D] bf16, lse [Hq,Tq] fp32."""
+    Tq, Hq, Dqk = q.shape
+    Tk, Hkv, Dv = v.shape
+    B = cu_seqlens_q.shape[0] - 1
+    for t, n, shp in ((q, "q", None), (k, "k", (Tk, Hkv, Dqk)), (v, "v", None), (o, "o", (Tq, Hq, Dv)),
+                      (dout, "dout", (Tq, Hq, Dv)), (dq, "dq", tuple(q.shape)), (dk, "dk", tuple(k.shape)),
+                      (dv, "dv", tuple(v.shape))):
+        _need(t, n, torch.bfloat16, shp)
+    _need(lse, "lse", torch.float32, (Hq, Tq))
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, (B + 1,))
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, (B + 1,))
+    ws, wsb = _ws(workspace)
+    _check(lib.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens_q.data_ptr(),
+                             cu_seqlens_k.data_ptr(), B, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, Dqk,
+                             Dv, _mods(mods), ws, wsb, _stream(stream, q.device)))

@@ -590,4 +590,113 @@ int fa_kv_cache_write_fp8(const void* k, const void* v, const int64_t* slot_mapp
   return FA_OK;
 }
 
+size_t fa_bwd_workspace_size(int64_t total_q, int64_t Hq) {
+  if (total_q <= 0 || Hq <= 0) return 0;
+  return (size_t)(total_q * Hq) * sizeof(float);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared checks and launch of the two backward entry points (cu_q null: dense).
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv, const int32_t* cu_q, const int32_t* cu_k, int64_t B, int64_t Sq,
+             int64_t Skv, int64_t total_q, int64_t total_k, int64_t max_sq, int64_t max_sk, int64_t Hq, int64_t Hkv,
+             int64_t d_qk, int64_t d_v, const fa_mods* mods, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  int rc = check_common(B, Hq, Hkv, d_qk, d_v);
+  if (rc) return rc;
+  if (total_q < 0 || total_k < 0 || max_sq < 0 || max_sk < 0) return fail(FA_ERR_INVALID, "token counts must be >= 0");
+  if (max_sq > total_q || max_sk > total_k) return fail(FA_ERR_INVALID, "max_seqlen exceeds the packed token count");
+  if (total_q >= kI32 || total_k >= kI32) return fail(FA_ERR_LIMIT, "token counts must stay below 2^31");
+  if (B * Hq >= kI32 || B * Hkv >= 65536 * 16384) return fail(FA_ERR_LIMIT, "B*H exceeds the grid limit");
+  if (max_sq / 128 >= 65535 || max_sk / 128 >= 65535) return fail(FA_ERR_LIMIT, "sequence length exceeds the grid limit");
+  Mods m;
+  if ((rc = read_mods(mods, d_qk, max_sq, max_sk, &m))) return rc;
+  if (m.flags & (FA_ALIBI | FA_SOFTCAP | FA_BLOCK_MASK))
+    return fail(FA_ERR_UNSUPPORTED, "the backward supports FA_CAUSAL and FA_WINDOW only");
+  if (d_qk != d_v || (d_qk != 64 && d_qk != 128))
+    return fail(FA_ERR_UNSUPPORTED, "backward head dims (%lld, %lld) not built; built: (64,64), (128,128)",
+                (long long)d_qk, (long long)d_v);
+  if (B == 0 || (total_q == 0 && total_k == 0)) return FA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || (cu_q && !cu_k))
+    return fail(FA_ERR_INVALID, "tensor pointers must be non-NULL");
+  const size_t need = fa_bwd_workspace_size(total_q, Hq);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(FA_ERR_WORKSPACE, "the backward needs a workspace of %zu bytes (got %zu)", need, workspace_bytes);
+  const size_t nq = (size_t)(total_q * Hq * d_qk) * 2, nk = (size_t)(total_k * Hkv * d_qk) * 2;
+  const size_t nv = (size_t)(total_k * Hkv * d_v) * 2, no = (size_t)(total_q * Hq * d_v) * 2;
+  const size_t nl = (size_t)(total_q * Hq) * 4;
+  const void* ins[] = {q, k, v, o, dout, lse};
+  const size_t in_n[] = {nq, nk, nv, no, no, nl};
+  void* outs[] = {dq, dk, dv, workspace};
+  const size_t out_n[] = {nq, nk, nv, need};
+  for (int x = 0; x < 4; ++x) {
+    for (int y = 0; y < 6; ++y)
+      if (overlaps(outs[x], out_n[x], ins[y], in_n[y])) return fail(FA_ERR_INVALID, "outputs must not overlap inputs");
+    for (int y = x + 1; y < 4; ++y)
+      if (overlaps(outs[x], out_n[x], outs[y], out_n[y])) return fail(FA_ERR_INVALID, "outputs must not overlap");
+  }
+  fa::BwdArgs a{};
+  a.q = (const __bf16*)q;
+  a.k = (const __bf16*)k;
+  a.v = (const __bf16*)v;
+  a.o = (const __bf16*)o;
+  a.dout = (const __bf16*)dout;
+  a.lse = lse;
+  a.delta = (float*)workspace;
+  a.dq = (__bf16*)dq;
+  a.dk = (__bf16*)dk;
+  a.dv = (__bf16*)dv;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.q_st = Hq * d_qk; a.q_sh = d_qk;
+  a.k_st = Hkv * d_qk; a.k_sh = d_qk;
+  a.v_st = Hkv * d_v; a.v_sh = d_v;
+  a.o_st = Hq * d_v; a.o_sh = d_v;
+  a.lse_tq = total_q;
+  a.total_rows = total_q;
+  a.Sq = (int)Sq; a.Skv = (int)Skv;
+  a.B = (int)B; a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.group = (int)(Hq / Hkv);
+  a.qk_scale = m.scale;
+  a.causal = (m.flags & FA_CAUSAL) ? 1 : 0;
+  a.win_left = (m.flags & FA_WINDOW) ? clamp_i32(m.wl) : -1;
+  a.win_right = (m.flags & FA_WINDOW) ? clamp_i32(m.wr) : -1;
+  bool supported = false;
+  hipError_t e = fa::bwd_dispatch(a, (int)d_qk, (int)max_sq, (int)max_sk, (hipStream_t)stream, &supported);
+  if (!supported) return fail(FA_ERR_UNSUPPORTED, "no backward kernel for d=%lld", (long long)d_qk);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_dense(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, int64_t B, int64_t Sq, int64_t Skv, int64_t Hq, int64_t Hkv,
+                 int64_t d_qk, int64_t d_v, const fa_mods* mods, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  g_err.clear();
+  if (B < 0 || Sq < 0 || Skv < 0) return fail(FA_ERR_INVALID, "sizes must be >= 0");
+  if (Sq >= kI32 || Skv >= kI32 || B * Sq >= kI32 || B * Skv >= kI32)
+    return fail(FA_ERR_LIMIT, "token counts must stay below 2^31");
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, nullptr, nullptr, B, Sq, Skv, B * Sq, B * Skv, Sq, Skv, Hq, Hkv,
+                  d_qk, d_v, mods, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                  int64_t B, int64_t total_q, int64_t total_k, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                  int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v, const fa_mods* mods,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!cu_seqlens_q || !cu_seqlens_k) {
+    if (B > 0 && (total_q > 0 || total_k > 0)) return fail(FA_ERR_INVALID, "cu_seqlens must be non-NULL");
+  }
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, B, 0, 0, total_q, total_k,
+                  max_seqlen_q, max_seqlen_k, Hq, Hkv, d_qk, d_v, mods, workspace, workspace_bytes, stream);
+}
+
 }  // extern "C"

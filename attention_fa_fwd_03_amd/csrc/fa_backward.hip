@@ -1,0 +1,478 @@
+// Attention backward pass (dQ, dK, dV) for gfx950, recomputing the
+// probabilities from the forward's saved LSE.
+//
+// Method (SM90 FlashAttention page, backward commit; LSE page, Summary): a
+// preprocess computes Delta_i = dO_i . O_i per row and head; with
+// P = exp(scale q.k - LSE) the gradients are
+//   dV = P^T dO,  dS = P * (dO V^T - Delta),  dK = scale dS^T Q,  dQ = scale dS K.
+// The page's kernel walks key tiles, loops over query tiles and adds dQ
+// with atomics; here dK/dV and dQ are two kernels that each recompute S and
+// dP, so every output is written once by one wavefront and summed in fp32
+// in a fixed order (deterministic, no atomics, no pre-cleared memory).
+//
+// Products are v_mfma_f32_32x32x16_bf16, oriented as in the forward kernel
+// so that each accumulator feeds the next product without moving data
+// between lanes:
+//   dK/dV kernel (a wavefront owns 32 keys, K and V^T fragments in
+//   registers; 64-row Q / dO tiles staged in LDS):
+//     S  [rows x keys] = Q K^T        A = Q rows from LDS, B = K in registers
+//     dP [rows x keys] = dO V^T       A = dO rows from LDS, B = V in registers
+//     dV^T [d x keys] += dO^T P       A = dO read transposed, B = P in registers
+//     dK^T [d x keys] += Q^T dS       A = Q read transposed,  B = dS in registers
+//   dQ kernel (a wavefront owns 32 query rows, Q and dO fragments in
+//   registers; 64-key K / V tiles staged in LDS):
+//     S^T [keys x rows] = K Q^T,  dP^T = V dO^T,  dQ^T [d x rows] += K^T dS^T
+// The B operand taken from a 32x32 accumulator enumerates its 16 rows (or
+// keys) per step with bits 2 and 3 swapped, and the transposed reads fetch
+// rows in that same order (as in the forward's P.V).
+//
+// Rows with no visible key have LSE = -inf: their P is 0 (the log2-domain
+// LSE is replaced by +inf), so they contribute nothing.  Masking is by
+// select, never by multiply.
+#include "fa_device.h"
+#include "fa_kernels.h"
+#include "fa_prefill_common.h"
+
+namespace fa {
+
+constexpr int kBwWaves = 4;
+constexpr int kBwThreads = 64 * kBwWaves;
+constexpr int kBwTile = 64;        // rows of a staged Q/dO tile, keys of a staged K/V tile
+constexpr int kBwKeys = 32 * kBwWaves;   // keys per dK/dV workgroup
+constexpr int kBwRowsQ = 32 * kBwWaves;  // query rows per dQ workgroup
+
+struct BwSeq {
+  int64_t qstart, kstart;
+  int sq, skv;
+};
+
+__device__ __forceinline__ BwSeq bw_seq(const BwdArgs& a, int b) {
+  BwSeq s;
+  if (a.cu_q) {
+    s.qstart = a.cu_q[b];
+    s.sq = a.cu_q[b + 1] - a.cu_q[b];
+    s.kstart = a.cu_k[b];
+    s.skv = a.cu_k[b + 1] - a.cu_k[b];
+  } else {
+    s.qstart = (int64_t)b * a.Sq;
+    s.sq = a.Sq;
+    s.kstart = (int64_t)b * a.Skv;
+    s.skv = a.Skv;
+  }
+  return s;
+}
+
+// index of (sequence b, head h, row i) in the LSE / Delta layout
+__device__ __forceinline__ int64_t bw_lse_index(const BwdArgs& a, int b, int h, int64_t qstart, int i) {
+  if (a.cu_q) return (int64_t)h * a.lse_tq + qstart + i;
+  return ((int64_t)b * a.Hq + h) * a.Sq + i;
+}
+
+// 64 rows x D bf16 of a packed tensor -> swizzled LDS tile, one 1 KB
+// global_load_lds per wavefront instruction (lane l fills 16 bytes at
+// 16 l of its KB: tile row r, stored chunk pos = source chunk pos ^ swz(r)).
+// Rows at or past nrows re-read the last row (their results are masked).
+template <int D>
+struct RowStager {
+  static constexpr int kRow = D * 2;
+  static constexpr int kPerWave = kBwTile * kRow / 1024 / kBwWaves;
+  static_assert(kPerWave >= 1, "tile too small");
+  int row[kPerWave], col[kPerWave];   // tile row and source element column of each piece
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int byte = (wave * kPerWave + i) * 1024 + lane * 16;
+      row[i] = byte / kRow;
+      col[i] = ((((byte % kRow) >> 4) ^ swz<kRow>(row[i])) << 3);
+    }
+  }
+  __device__ __forceinline__ void issue(const bf16* base, int64_t st, int r0, int nrows, char FA_LDS* tile,
+                                        int wave) const {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int r = min(r0 + row[i], nrows - 1);
+      global_to_lds16(base + (int64_t)r * st + col[i], tile + (wave * kPerWave + i) * 1024);
+    }
+  }
+};
+
+// A fragment of O^T-style products read transposed from a swizzled tile of
+// 64 rows: rows {16u + swap23 order} x 32 columns [32 dblk, +32).
+template <int kRow>
+__device__ __forceinline__ bf16x8 tr_fragment(const char FA_LDS* tile, int u, int dblk, int lane) {
+  const int grp = lane >> 4, i16 = lane & 15;
+  const int r1 = u * 16 + (grp >> 1) * 4 + (i16 >> 2);
+  const int r2 = r1 + 8;
+  const int dcol = dblk * 32 + (grp & 1) * 16 + 4 * (i16 & 3);
+  const int chunk = dcol >> 3, half = (dcol >> 2) & 1;
+  const bf16x4 lo4 = lds_read_tr16(tile + r1 * kRow + ((chunk ^ swz<kRow>(r1)) << 4) + half * 8);
+  const bf16x4 hi4 = lds_read_tr16(tile + r2 * kRow + ((chunk ^ swz<kRow>(r2)) << 4) + half * 8);
+  bf16x8 f;
+  f[0] = lo4[0]; f[1] = lo4[1]; f[2] = lo4[2]; f[3] = lo4[3];
+  f[4] = hi4[0]; f[5] = hi4[1]; f[6] = hi4[2]; f[7] = hi4[3];
+  return f;
+}
+
+// natural-log LSE -> log2 domain, with rows that see no key sent to +inf
+__device__ __forceinline__ float lse_log2(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
+
+// ---------------------------------------------------------------- Delta
+// One wavefront per (row, head): Delta = dO . O in fp32.
+template <int D>
+__global__ __launch_bounds__(kBwThreads) void fa_bwd_delta_kernel(const BwdArgs a) {
+  constexpr int kPer = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * kBwWaves + (threadIdx.x >> 6);
+  if (item >= a.total_rows * a.Hq) return;
+  const int64_t t = item / a.Hq;
+  const int h = (int)(item - t * a.Hq);
+  const bf16* op = a.o + t * a.o_st + (int64_t)h * a.o_sh + lane * kPer;
+  const bf16* dp = a.dout + t * a.o_st + (int64_t)h * a.o_sh + lane * kPer;
+  float acc = 0.0f;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) acc += (float)op[e] * (float)dp[e];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+  if (lane == 0) {
+    int64_t li;
+    if (a.cu_q) li = (int64_t)h * a.lse_tq + t;
+    else li = ((t / a.Sq) * a.Hq + h) * a.Sq + t % a.Sq;
+    a.delta[li] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+// Workgroup = (sequence, kv-head, 128 keys); wavefront w owns keys
+// [k0 + 32 w, +32).  Steps walk the q-heads of the group and, per head, the
+// 64-row query tiles that can see any of the workgroup's keys; the Q / dO
+// tiles (and their LSE / Delta rows) of the next step load while the
+// current one is computed.
+template <int D>
+__global__ __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu(1)))
+void fa_bwd_dkdv_kernel(const BwdArgs a) {
+  constexpr int kRow = D * 2;
+  constexpr int kTileB = kBwTile * kRow;
+  constexpr int kStage = 2 * kTileB + 2 * kBwTile * 4;
+  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage];
+  char FA_LDS* lds = (char FA_LDS*)(lds_raw);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int bg = blockIdx.x;
+  if (bg >= a.B * a.Hkv) return;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const BwSeq sv = bw_seq(a, b);
+  const int k0 = blockIdx.y * kBwKeys;
+  if (k0 >= sv.skv) return;
+  const int key = k0 + wave * 32 + (lane & 31);
+  const bool kvalid = key < sv.skv;
+  const int delta_al = sv.skv - sv.sq;
+
+  // K and V fragments of this lane's key (B operands): d = 16 s + 8 (lane/32) + e
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const int64_t kr = sv.kstart + min(key, sv.skv - 1);
+    const bf16* kp = a.k + kr * a.k_st + (int64_t)g * a.k_sh + (lane >> 5) * 8;
+    const bf16* vp = a.v + kr * a.v_st + (int64_t)g * a.v_sh + (lane >> 5) * 8;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      kf[s] = kvalid ? *reinterpret_cast<const bf16x8*>(kp + 16 * s) : bf16x8{};
+      vf[s] = kvalid ? *reinterpret_cast<const bf16x8*>(vp + 16 * s) : bf16x8{};
+    }
+  }
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) dk[d] = dv[d] = f32x16{};
+
+  // query rows that see any key of [k0, j1]
+  const int j1 = min(k0 + kBwKeys, sv.skv) - 1;
+  int r_lo = 0, r_hi = sv.sq - 1;
+  if (a.causal) r_lo = max(r_lo, k0 - delta_al);
+  if (a.win_right >= 0) r_lo = max(r_lo, k0 - delta_al - a.win_right);
+  if (a.win_left >= 0) r_hi = min(r_hi, j1 + a.win_left - delta_al);
+  const int qb0 = r_lo >= 0 ? r_lo / kBwTile : 0;
+  const int nqb = r_lo <= r_hi ? r_hi / kBwTile - qb0 + 1 : 0;
+  const int nsteps = nqb * a.group;
+  const float C = a.qk_scale * kLog2e;
+
+  RowStager<D> st;
+  st.init(wave, lane);
+  auto stage_ptr = [&](int i) { return lds + i * kStage; };
+  float ld_lse = 0.0f, ld_delta = 0.0f;
+  // loads of step n into stage buffer sb: Q and dO by DMA, LSE / Delta to registers
+  auto issue = [&](int n, int sb) {
+    const int h = g * a.group + n / nqb;
+    const int r0 = (qb0 + n % nqb) * kBwTile;
+    char FA_LDS* sp = stage_ptr(sb);
+    st.issue(a.q + sv.qstart * a.q_st + (int64_t)h * a.q_sh, a.q_st, r0, sv.sq, sp, wave);
+    st.issue(a.dout + sv.qstart * a.o_st + (int64_t)h * a.o_sh, a.o_st, r0, sv.sq, sp + kTileB, wave);
+    if (tid < kBwTile) {
+      const int r = min(r0 + tid, sv.sq - 1);
+      const int64_t li = bw_lse_index(a, b, h, sv.qstart, r);
+      ld_lse = lse_log2(a.lse[li]);
+      ld_delta = a.delta[li];
+    }
+  };
+  auto publish = [&](int sb) {
+    if (tid < kBwTile) {
+      float FA_LDS* lp = reinterpret_cast<float FA_LDS*>(stage_ptr(sb) + 2 * kTileB);
+      lp[tid] = ld_lse;
+      lp[kBwTile + tid] = ld_delta;
+    }
+  };
+
+  if (nsteps > 0) {
+    issue(0, 0);
+    FA_WAIT_VMCNT(0);
+    publish(0);
+  }
+  for (int n = 0; n < nsteps; ++n) {
+    const int sb = n & 1;
+    __syncthreads();   // step n visible; everyone is done with the other buffer
+    if (n + 1 < nsteps) issue(n + 1, sb ^ 1);
+    const char FA_LDS* qt = stage_ptr(sb);
+    const char FA_LDS* dt = qt + kTileB;
+    const float FA_LDS* lse2 = reinterpret_cast<const float FA_LDS*>(qt + 2 * kTileB);
+    const float FA_LDS* dl = lse2 + kBwTile;
+    const int r0 = (qb0 + n % nqb) * kBwTile;
+
+    // S and dP for rows [32 rb, +32) of the tile
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int stp = 0; stp < D / 16; ++stp) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int r = rb * 32 + (lane & 31);
+        const int off = r * kRow + (((2 * stp + (lane >> 5)) ^ swz<kRow>(r)) << 4);
+        s[rb] = mfma32(lds_read_b128(qt + off), kf[stp], s[rb]);
+        dp[rb] = mfma32(lds_read_b128(dt + off), vf[stp], dp[rb]);
+      }
+    }
+    // P and dS (register i of row block rb: row 32 rb + 8 (i/4) + 4 (lane/32) + i%4)
+    bf16x8 pf[4], dsf[4];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int rr = rb * 32 + q4 * 8 + (lane >> 5) * 4;
+        const f32x4 l4 = *reinterpret_cast<const f32x4 FA_LDS*>(lse2 + rr);
+        const f32x4 d4 = *reinterpret_cast<const f32x4 FA_LDS*>(dl + rr);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = q4 * 4 + e;
+          const int qi = r0 + rr + e;
+          const int ip = qi + delta_al;
+          bool vis = kvalid && qi < sv.sq;
+          if (a.causal) vis = vis && key <= ip;
+          if (a.win_right >= 0) vis = vis && key <= ip + a.win_right;
+          if (a.win_left >= 0) vis = vis && key >= ip - a.win_left;
+          const float p = vis ? exp2_hw(fmaf(s[rb][i], C, -l4[e])) : 0.0f;
+          const float ds = p * (dp[rb][i] - d4[e]);
+          pf[rb * 2 + (i >> 3)][i & 7] = (bf16)p;
+          dsf[rb * 2 + (i >> 3)][i & 7] = (bf16)ds;
+        }
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 64 rows
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int d = 0; d < D / 32; ++d) {
+        dv[d] = mfma32(tr_fragment<kRow>(dt, u, d, lane), pf[u], dv[d]);
+        dk[d] = mfma32(tr_fragment<kRow>(qt, u, d, lane), dsf[u], dk[d]);
+      }
+    }
+    if (n + 1 < nsteps) {
+      FA_WAIT_VMCNT(0);
+      publish(sb ^ 1);
+    }
+  }
+
+  // dK^T / dV^T register i of block d: dim 32 d + 8 (i/4) + 4 (lane/32) + i%4
+  if (kvalid) {
+    const int64_t kr = sv.kstart + key;
+    bf16* kp = a.dk + kr * a.k_st + (int64_t)g * a.k_sh + (lane >> 5) * 4;
+    bf16* vp = a.dv + kr * a.v_st + (int64_t)g * a.v_sh + (lane >> 5) * 4;
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d) {
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        bf16x4 wk, wv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wk[e] = (bf16)(dk[d][gi * 4 + e] * a.qk_scale);
+          wv[e] = (bf16)dv[d][gi * 4 + e];
+        }
+        *reinterpret_cast<bf16x4*>(kp + d * 32 + gi * 8) = wk;
+        *reinterpret_cast<bf16x4*>(vp + d * 32 + gi * 8) = wv;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+// Workgroup = (sequence, q-head, 128 query rows), as the forward kernel;
+// 64-key K / V tiles stream through two LDS stages.
+template <int D>
+__global__ __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu(1)))
+void fa_bwd_dq_kernel(const BwdArgs a) {
+  constexpr int kRow = D * 2;
+  constexpr int kTileB = kBwTile * kRow;
+  constexpr int kStage = 2 * kTileB;
+  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage];
+  char FA_LDS* lds = (char FA_LDS*)(lds_raw);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int bh = blockIdx.x;
+  if (bh >= a.B * a.Hq) return;
+  const int b = bh / a.Hq, h = bh % a.Hq, g = h / a.group;
+  const BwSeq sv = bw_seq(a, b);
+  const int q0 = blockIdx.y * kBwRowsQ;
+  if (q0 >= sv.sq) return;
+  const int q1 = min(q0 + kBwRowsQ, sv.sq);
+  const int delta_al = sv.skv - sv.sq;
+  const int qrow = q0 + wave * 32 + (lane & 31);
+  const bool qvalid = qrow < sv.sq;
+  const int ip = qrow + delta_al;
+
+  // Q and dO fragments of this lane's row (B operands)
+  bf16x8 qf[D / 16], of[D / 16];
+  {
+    const int64_t t = sv.qstart + (qvalid ? qrow : 0);
+    const bf16* qp = a.q + t * a.q_st + (int64_t)h * a.q_sh + (lane >> 5) * 8;
+    const bf16* op = a.dout + t * a.o_st + (int64_t)h * a.o_sh + (lane >> 5) * 8;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      qf[s] = qvalid ? *reinterpret_cast<const bf16x8*>(qp + 16 * s) : bf16x8{};
+      of[s] = qvalid ? *reinterpret_cast<const bf16x8*>(op + 16 * s) : bf16x8{};
+    }
+  }
+  float lse2 = INFINITY, dlt = 0.0f;
+  if (qvalid) {
+    const int64_t li = bw_lse_index(a, b, h, sv.qstart, qrow);
+    lse2 = lse_log2(a.lse[li]);
+    dlt = a.delta[li];
+  }
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) dq[d] = f32x16{};
+
+  // key tiles that any row of the workgroup sees
+  auto row_hi = [&](int i) {
+    int hi = sv.skv - 1;
+    if (a.causal) hi = min(hi, i + delta_al);
+    if (a.win_right >= 0) hi = min(hi, i + delta_al + a.win_right);
+    return hi;
+  };
+  auto row_lo = [&](int i) {
+    int lo = 0;
+    if (a.win_left >= 0) lo = max(lo, i + delta_al - a.win_left);
+    return lo;
+  };
+  const int lo_min = row_lo(q0), hi_max = row_hi(q1 - 1);
+  const int t_begin = lo_min / kBwTile;
+  const int t_end = hi_max >= lo_min ? hi_max / kBwTile : t_begin - 1;
+  const int my_lo = row_lo(qrow), my_hi = row_hi(qrow);
+  const float C = a.qk_scale * kLog2e;
+
+  RowStager<D> st;
+  st.init(wave, lane);
+  auto stage_ptr = [&](int i) { return lds + i * kStage; };
+  const bf16* kbase = a.k + sv.kstart * a.k_st + (int64_t)g * a.k_sh;
+  const bf16* vbase = a.v + sv.kstart * a.v_st + (int64_t)g * a.v_sh;
+  auto issue = [&](int t, int sb) {
+    st.issue(kbase, a.k_st, t * kBwTile, sv.skv, stage_ptr(sb), wave);
+    st.issue(vbase, a.v_st, t * kBwTile, sv.skv, stage_ptr(sb) + kTileB, wave);
+  };
+  if (t_begin <= t_end) {
+    issue(t_begin, 0);
+    FA_WAIT_VMCNT(0);
+  }
+  for (int t = t_begin; t <= t_end; ++t) {
+    const int sb = (t - t_begin) & 1;
+    __syncthreads();
+    if (t + 1 <= t_end) issue(t + 1, sb ^ 1);
+    const char FA_LDS* kt = stage_ptr(sb);
+    const char FA_LDS* vt = kt + kTileB;
+    const int k0 = t * kBwTile;
+
+    // S^T and dP^T for keys [32 kb, +32) of the tile
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int stp = 0; stp < D / 16; ++stp) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int r = kb * 32 + (lane & 31);
+        const int off = r * kRow + (((2 * stp + (lane >> 5)) ^ swz<kRow>(r)) << 4);
+        s[kb] = mfma32(lds_read_b128(kt + off), qf[stp], s[kb]);
+        dp[kb] = mfma32(lds_read_b128(vt + off), of[stp], dp[kb]);
+      }
+    }
+    // dS^T (register i of key block kb: key 32 kb + 8 (i/4) + 4 (lane/32) + i%4)
+    bf16x8 dsf[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = k0 + kb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+        const bool vis = qvalid && j >= my_lo && j <= my_hi;
+        const float p = vis ? exp2_hw(fmaf(s[kb][i], C, -lse2)) : 0.0f;
+        dsf[kb * 2 + (i >> 3)][i & 7] = (bf16)(p * (dp[kb][i] - dlt));
+      }
+    }
+    // dQ^T += K^T dS^T over the tile's 64 keys
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int d = 0; d < D / 32; ++d) dq[d] = mfma32(tr_fragment<kRow>(kt, u, d, lane), dsf[u], dq[d]);
+    }
+    if (t + 1 <= t_end) FA_WAIT_VMCNT(0);
+  }
+
+  if (qvalid) {
+    bf16* qp = a.dq + (sv.qstart + qrow) * a.q_st + (int64_t)h * a.q_sh + (lane >> 5) * 4;
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d) {
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(dq[d][gi * 4 + e] * a.qk_scale);
+        *reinterpret_cast<bf16x4*>(qp + d * 32 + gi * 8) = w;
+      }
+    }
+  }
+}
+
+template <int D>
+static hipError_t launch_bwd(const BwdArgs& a, int max_sq, int max_skv, hipStream_t stream) {
+  const int64_t rows = a.total_rows * a.Hq;
+  if (rows > 0) {
+    hipLaunchKernelGGL(fa_bwd_delta_kernel<D>, dim3((unsigned)((rows + kBwWaves - 1) / kBwWaves)), dim3(kBwThreads),
+                       0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (max_skv > 0) {
+    hipLaunchKernelGGL(fa_bwd_dkdv_kernel<D>, dim3(a.B * a.Hkv, (max_skv + kBwKeys - 1) / kBwKeys),
+                       dim3(kBwThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (max_sq > 0) {
+    hipLaunchKernelGGL(fa_bwd_dq_kernel<D>, dim3(a.B * a.Hq, (max_sq + kBwRowsQ - 1) / kBwRowsQ),
+                       dim3(kBwThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t bwd_dispatch(const BwdArgs& a, int d, int max_sq, int max_skv, hipStream_t stream, bool* supported) {
+  *supported = true;
+  if (d == 64) return launch_bwd<64>(a, max_sq, max_skv, stream);
+  if (d == 128) return launch_bwd<128>(a, max_sq, max_skv, stream);
+  *supported = false;
+  return hipSuccess;
+}
+
+}  // namespace fa

@@ -98,6 +98,35 @@ struct CombineArgs {
   int n_workers, slot_rows;
 };
 
+// Backward pass (fa_backward.hip).  Rows of Q, O, dO, dQ: token t, head h at
+// t*q_st + h*q_sh (O and dO with o_st / o_sh); K, V, dK, dV rows with
+// k_st / k_sh (v_st / v_sh).  Dense batches are packed rows with sequence b
+// starting at b*Sq (b*Skv); LSE and Delta share the forward's LSE layout.
+struct BwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* o;
+  const __bf16* dout;
+  const float* lse;
+  float* delta;
+  __bf16* dq;
+  __bf16* dk;
+  __bf16* dv;
+  const int32_t* cu_q;         // null: dense
+  const int32_t* cu_k;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh;
+  int64_t lse_tq;              // packed layouts: LSE is [Hq, lse_tq]
+  int64_t total_rows;          // query rows over all sequences
+  int Sq, Skv;                 // dense lengths
+  int B, Hq, Hkv, group;
+  float qk_scale;
+  int causal;
+  int win_left, win_right;     // < 0: unbounded
+};
+
+hipError_t bwd_dispatch(const BwdArgs& a, int d, int max_sq, int max_skv, hipStream_t stream, bool* supported);
+
 // FP8 KV-cache write (fa_kvcache.hip).
 struct KvAmaxArgs {
   const __bf16* k;

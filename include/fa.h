@@ -201,6 +201,36 @@ size_t fa_fwd_paged_workspace_size(int64_t B, int64_t total_q, int64_t max_seqle
                                    int64_t max_seqlen_k, int64_t Hq, int64_t Hkv, int64_t d_qk,
                                    int64_t d_v, int64_t page_size, fa_dtype kv_dtype);
 
+/*
+ * Backward pass of the dense / varlen forward: dQ, dK, dV from Q, K, V, the
+ * forward's O and LSE and the upstream gradient dO (method: "SM90 TMA +
+ * mma.sync FlashAttention, forward + backward (causal, varlen, LSE)",
+ * backward commit — a Delta = rowsum(dO * O) preprocess, then dQ/dK/dV
+ * recomputing P from the saved LSE).  Layouts are the forward's: dense Q,
+ * O, dO, dQ [B, Sq, Hq, d], K, V, dK, dV [B, Skv, Hkv, d], LSE [B, Hq, Sq];
+ * varlen rows packed by cu_seqlens_q / cu_seqlens_k, LSE [Hq, total_q].
+ * All tensors bf16 except LSE (fp32).  GQA: dK / dV of a kv-head sum over
+ * its q-heads.  Built: d_qk = d_v in {64, 128}.  Mods: FA_CAUSAL and
+ * FA_WINDOW (and softmax_scale) — the masks the forward used must be passed
+ * again.  Rows with no visible key contribute nothing; every element of dQ,
+ * dK and dV is written (zeros where no gradient flows).  Needs a device
+ * workspace of fa_bwd_workspace_size(...) bytes (Delta, fp32), else
+ * FA_ERR_WORKSPACE; outputs must not overlap the inputs or each other.
+ * Deterministic: every output element is summed in a fixed order.
+ */
+int fa_bwd_dense(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, int64_t B, int64_t Sq, int64_t Skv, int64_t Hq, int64_t Hkv,
+                 int64_t d_qk, int64_t d_v, const fa_mods* mods, void* workspace, size_t workspace_bytes,
+                 void* stream);
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                  int64_t B, int64_t total_q, int64_t total_k, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                  int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v, const fa_mods* mods,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of the backward entry points (total_q = B * Sq for dense). */
+size_t fa_bwd_workspace_size(int64_t total_q, int64_t Hq);
+
 /* fa_kv_cache_write_fp8 scale_mode */
 #define FA_SCALE_GIVEN 0  /* quantise with the descales already in *k_descale / *v_descale */
 #define FA_SCALE_AMAX 1   /* first set *k_descale = max(max|k| / 448, 2^-126), same for v */

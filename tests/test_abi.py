@@ -227,3 +227,38 @@ def test_kv_cache_write_empty_and_workspace_query():
     assert fa.fa_kv_cache_write_fp8_workspace_size(0, 8, 192, 128) == 0
     n = fa.fa_kv_cache_write_fp8_workspace_size(1000, 8, 192, 128)
     assert 0 < n < 1 << 16 and n % 4 == 0
+
+
+def _bwd(**kw):
+    fa = _lib()
+    a = dict(B=1, Sq=16, Skv=16, Hq=2, Hkv=2, dqk=64, dv=64, mods=None, ws=FAKE * 30, wsb=1 << 20)
+    a.update(kw)
+    ptrs = [FAKE * (i + 1) for i in range(9)]
+    rc = fa.lib.fa_bwd_dense(*ptrs, a["B"], a["Sq"], a["Skv"], a["Hq"], a["Hkv"], a["dqk"], a["dv"], a["mods"],
+                             a["ws"], a["wsb"], None)
+    return rc, fa.fa_last_error()
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(dqk=192, dv=128), -2, "not built"),
+    (dict(dqk=128, dv=64), -2, "not built"),
+    (dict(ws=0), -4, "workspace"),
+    (dict(wsb=8), -4, "workspace"),
+    (dict(Hq=3, Hkv=2), -1, "multiple"),
+    (dict(Sq=-1), -1, ">= 0"),
+])
+def test_bwd_rejects(kw, code, frag):
+    rc, msg = _bwd(**kw)
+    assert rc == code and frag in msg, (rc, msg)
+
+
+def test_bwd_rejects_score_mods_and_overlap():
+    fa = _lib()
+    m = fa.Mods(softcap=20.0).to_c()
+    rc, msg = _bwd(mods=ctypes.byref(m))
+    assert rc == -2 and "FA_CAUSAL" in msg
+    ptrs = [FAKE * (i + 1) for i in range(9)]
+    ptrs[6] = ptrs[0]                      # dq aliases q
+    rc = fa.lib.fa_bwd_dense(*ptrs, 1, 16, 16, 2, 2, 64, 64, None, FAKE * 30, 1 << 20, None)
+    assert rc == -1 and "overlap" in fa.fa_last_error()
+    assert fa.fa_bwd_workspace_size(0, 4) == 0 and fa.fa_bwd_workspace_size(10, 4) == 160

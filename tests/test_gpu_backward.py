@@ -1,0 +1,112 @@
+"""Backward pass (dQ, dK, dV) through the C ABI against the fp64 oracle.
+
+The forward runs on the GPU first (its O and LSE are the backward's inputs);
+the oracle differentiates the same bf16 Q, K, V with the same dO.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.helpers import f64
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import attention_fa_fwd_03_amd as fa
+
+DEV = "cuda"
+# max |gpu - ref| <= TOL_GRAD * max |ref| + TOL_GRAD_ABS: P and dS enter
+# their products in bf16 (relative 2^-9 each) and Delta comes from the bf16
+# O, so an element carries a few 1e-3 of the largest term of its sum; the
+# absolute part covers sums that cancel exactly (one visible key gives
+# dS = dP - Delta = 0, which the GPU reaches only to fp32 rounding of O(1) terms)
+TOL_GRAD = 2e-2
+TOL_GRAD_ABS = 1e-3
+
+
+def _check_grad(g, ref, what):
+    g = f64(g)
+    assert not np.isnan(g).any(), f"{what}: NaN"
+    scale = float(np.abs(ref).max())
+    err = float(np.abs(g - ref).max())
+    assert err <= TOL_GRAD * scale + TOL_GRAD_ABS, f"{what}: max err {err:.3e} vs max |ref| {scale:.3e}"
+
+
+def _dense_fb(B, Sq, Skv, Hq, Hkv, D, mods_kw, seed):
+    d = synth.make_dense(B, Sq, Skv, Hq, Hkv, D, D, seed=seed)
+    q, k, v = (d[x].to(DEV) for x in ("q", "k", "v"))
+    do = synth.randn_bf16((B, Sq, Hq, D), seed + 5)
+    o = torch.empty((B, Sq, Hq, D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=DEV)
+    fa.fa_fwd_dense(q, k, v, o, lse, fa.Mods(**mods_kw))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(fa.fa_bwd_workspace_size(B * Sq, Hq), 4), dtype=torch.uint8, device=DEV)
+    fa.fa_bwd_dense(q, k, v, o, do.to(DEV), lse, dq, dk, dv, fa.Mods(**mods_kw), workspace=ws)
+    torch.cuda.synchronize()
+    return d, do, (dq, dk, dv)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Sq,Skv", [(128, 128), (200, 333), (333, 200), (1, 77), (70, 1)])
+def test_bwd_dense_matches_oracle(D, causal, Sq, Skv):
+    mods_kw = dict(causal=causal)
+    d, do, grads = _dense_fb(1, Sq, Skv, 2, 2, D, mods_kw, seed=301 + Sq + D)
+    ref = oracle.attention_bwd_dense(f64(d["q"]), f64(d["k"]), f64(d["v"]), f64(do), mods_kw)
+    for g, r, n in zip(grads, ref, ("dq", "dk", "dv")):
+        _check_grad(g, r, f"{n} D{D} causal={causal} {Sq}x{Skv}")
+
+
+@pytest.mark.parametrize("mods_kw", [dict(causal=True), dict(window=(40, 5)), dict(causal=True, window=(100, 0))])
+def test_bwd_varlen_gqa_matches_oracle(mods_kw):
+    """Ragged sequences (one empty, one key-starved), GQA 8/2, D 128."""
+    lq, lk = [300, 0, 129, 64, 5], [300, 40, 129, 1, 77]
+    d = synth.make_varlen(lq, lk, 8, 2, 128, 128, seed=331)
+    q, k, v = (d[x].to(DEV) for x in ("q", "k", "v"))
+    cu_q, cu_k = d["cu_q"].to(DEV), d["cu_k"].to(DEV)
+    Tq, Tk = q.shape[0], k.shape[0]
+    do = synth.randn_bf16((Tq, 8, 128), 337)
+    o = torch.empty((Tq, 8, 128), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((8, Tq), dtype=torch.float32, device=DEV)
+    fa.fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, max(lq), max(lk), fa.Mods(**mods_kw))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_size(Tq, 8), dtype=torch.uint8, device=DEV)
+    fa.fa_bwd_varlen(q, k, v, o, do.to(DEV), lse, dq, dk, dv, cu_q, cu_k, max(lq), max(lk), fa.Mods(**mods_kw),
+                     workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.attention_bwd_varlen(f64(d["q"]), f64(d["k"]), f64(d["v"]), f64(do), d["cu_q"].numpy(),
+                                      d["cu_k"].numpy(), mods_kw)
+    for g, r, n in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
+        _check_grad(g, r, f"varlen {n} {mods_kw}")
+    # keys of the sequence without queries get exactly zero gradients
+    assert torch.count_nonzero(dk[300:340]) == 0 and torch.count_nonzero(dv[300:340]) == 0
+
+
+def test_bwd_is_deterministic():
+    d, do, g1 = _dense_fb(2, 257, 300, 4, 2, 128, dict(causal=True), seed=351)
+    _, _, g2 = _dense_fb(2, 257, 300, 4, 2, 128, dict(causal=True), seed=351)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_bwd_medium_varlen():
+    """Sequences of 700-1000 tokens, 4 heads, D 128, causal."""
+    lq = lk = [700, 1000, 300]
+    d = synth.make_varlen(lq, lk, 4, 4, 128, 128, seed=361)
+    q, k, v = (d[x].to(DEV) for x in ("q", "k", "v"))
+    cu = d["cu_q"].to(DEV)
+    Tq = q.shape[0]
+    do = synth.randn_bf16((Tq, 4, 128), 367)
+    o = torch.empty_like(q)
+    lse = torch.empty((4, Tq), dtype=torch.float32, device=DEV)
+    fa.fa_fwd_varlen(q, k, v, o, lse, cu, cu, 1000, 1000, fa.Mods(causal=True))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_size(Tq, 4), dtype=torch.uint8, device=DEV)
+    fa.fa_bwd_varlen(q, k, v, o, do.to(DEV), lse, dq, dk, dv, cu, cu, 1000, 1000, fa.Mods(causal=True), workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.attention_bwd_varlen(f64(d["q"]), f64(d["k"]), f64(d["v"]), f64(do), d["cu_q"].numpy(),
+                                      d["cu_q"].numpy(), dict(causal=True))
+    for g, r, n in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
+        _check_grad(g, r, f"medium {n}")
