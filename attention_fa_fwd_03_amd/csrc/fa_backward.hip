@@ -147,8 +147,10 @@ __global__ __launch_bounds__(kBwThreads) void fa_bwd_delta_kernel(const BwdArgs 
 // 64-row query tiles that can see any of the workgroup's keys; the Q / dO
 // tiles (and their LSE / Delta rows) of the next step load while the
 // current one is computed.
+// (at D = 128 the K / V fragments and dK / dV accumulators alone take 192
+// registers: one wavefront per SIMD, the rest in accumulation registers)
 template <int D>
-__global__ __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu(D > 64 ? 1 : 2)))
 void fa_bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int kRow = D * 2;
   constexpr int kTileB = kBwTile * kRow;
@@ -236,22 +238,21 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
     const float FA_LDS* dl = lse2 + kBwTile;
     const int r0 = (qb0 + n % nqb) * kBwTile;
 
-    // S and dP for rows [32 rb, +32) of the tile
-    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int stp = 0; stp < D / 16; ++stp) {
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int r = rb * 32 + (lane & 31);
-        const int off = r * kRow + (((2 * stp + (lane >> 5)) ^ swz<kRow>(r)) << 4);
-        s[rb] = mfma32(lds_read_b128(qt + off), kf[stp], s[rb]);
-        dp[rb] = mfma32(lds_read_b128(dt + off), vf[stp], dp[rb]);
-      }
-    }
-    // P and dS (register i of row block rb: row 32 rb + 8 (i/4) + 4 (lane/32) + i%4)
-    bf16x8 pf[4], dsf[4];
+    // the tile's two 32-row halves one after the other (keeps the S / dP
+    // accumulators of one half live at a time)
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
+      // S and dP for rows [32 rb, +32)
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int stp = 0; stp < D / 16; ++stp) {
+        const int r = rb * 32 + (lane & 31);
+        const int off = r * kRow + (((2 * stp + (lane >> 5)) ^ swz<kRow>(r)) << 4);
+        s = mfma32(lds_read_b128(qt + off), kf[stp], s);
+        dp = mfma32(lds_read_b128(dt + off), vf[stp], dp);
+      }
+      // P and dS (register i: row 32 rb + 8 (i/4) + 4 (lane/32) + i%4)
+      bf16x8 pf[2], dsf[2];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int rr = rb * 32 + q4 * 8 + (lane >> 5) * 4;
@@ -266,20 +267,19 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
           if (a.causal) vis = vis && key <= ip;
           if (a.win_right >= 0) vis = vis && key <= ip + a.win_right;
           if (a.win_left >= 0) vis = vis && key >= ip - a.win_left;
-          const float p = vis ? exp2_hw(fmaf(s[rb][i], C, -l4[e])) : 0.0f;
-          const float ds = p * (dp[rb][i] - d4[e]);
-          pf[rb * 2 + (i >> 3)][i & 7] = (bf16)p;
-          dsf[rb * 2 + (i >> 3)][i & 7] = (bf16)ds;
+          const float p = vis ? exp2_hw(fmaf(s[i], C, -l4[e])) : 0.0f;
+          pf[i >> 3][i & 7] = (bf16)p;
+          dsf[i >> 3][i & 7] = (bf16)(p * (dp[i] - d4[e]));
         }
       }
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 64 rows
+      // dV^T += dO^T P and dK^T += Q^T dS over these 32 rows
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+      for (int uu = 0; uu < 2; ++uu) {
 #pragma unroll
-      for (int d = 0; d < D / 32; ++d) {
-        dv[d] = mfma32(tr_fragment<kRow>(dt, u, d, lane), pf[u], dv[d]);
-        dk[d] = mfma32(tr_fragment<kRow>(qt, u, d, lane), dsf[u], dk[d]);
+        for (int d = 0; d < D / 32; ++d) {
+          dv[d] = mfma32(tr_fragment<kRow>(dt, rb * 2 + uu, d, lane), pf[uu], dv[d]);
+          dk[d] = mfma32(tr_fragment<kRow>(qt, rb * 2 + uu, d, lane), dsf[uu], dk[d]);
+        }
       }
     }
     if (n + 1 < nsteps) {
@@ -314,7 +314,7 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
 // Workgroup = (sequence, q-head, 128 query rows), as the forward kernel;
 // 64-key K / V tiles stream through two LDS stages.
 template <int D>
-__global__ __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_bwd_dq_kernel(const BwdArgs a) {
   constexpr int kRow = D * 2;
   constexpr int kTileB = kBwTile * kRow;

@@ -17,7 +17,7 @@ before timing starts.
 
 --config selects another workload for investigation (1 dense D64, 3 paged
 FP8 prefill, 4 paged FP8 decode, 5 flex, 6 FP8 KV-cache write of the decode
-cache); the default line is config 2.
+cache, 7 backward pass of config 2's batch); the default line is config 2.
 --layout vec runs configs 3 and 4 on the vectorised 5-D page format
 (fa_fwd_paged_vec) instead of head-major pages; --q-dtype fp8 gives them
 E4M3 queries with a per-tensor descale (fa_fwd_paged_ex); --dv 192 runs them
@@ -41,7 +41,8 @@ METRIC = "attention fwd TFLOP/s + fraction of MFMA peak; paged-decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 COPY_BYTES = 256 << 20        # calibration copy for the HBM byte counters
-DOMINANT = {"prefill": "fa_prefill_kernel", "decode": "fa_decode_kernel", "kvwrite": "fa_kv_write_kernel"}
+DOMINANT = {"prefill": "fa_prefill_kernel", "decode": "fa_decode_kernel", "kvwrite": "fa_kv_write_kernel",
+            "backward": "fa_bwd_dkdv_kernel"}
 KERNEL_SOURCES = {
     "prefill": ["attention_fa_fwd_03_amd/csrc/fa_prefill.hip", "attention_fa_fwd_03_amd/csrc/fa_prefill_common.h",
                 "attention_fa_fwd_03_amd/csrc/fa_device.h",
@@ -50,6 +51,8 @@ KERNEL_SOURCES = {
                "attention_fa_fwd_03_amd/csrc/fa_kernels.h"],
     "kvwrite": ["attention_fa_fwd_03_amd/csrc/fa_kvcache.hip", "attention_fa_fwd_03_amd/csrc/fa_device.h",
                 "attention_fa_fwd_03_amd/csrc/fa_kernels.h"],
+    "backward": ["attention_fa_fwd_03_amd/csrc/fa_backward.hip", "attention_fa_fwd_03_amd/csrc/fa_prefill_common.h",
+                 "attention_fa_fwd_03_amd/csrc/fa_device.h", "attention_fa_fwd_03_amd/csrc/fa_kernels.h"],
 }
 
 
@@ -258,6 +261,27 @@ def build_workload(cfg: int, flex: str, torch, synth, fa, page_size: int = 64, l
         name = f"flex {flex} B2 H16 S8192 D128 bf16"
         return name, run, dict(flops=flops, bytes=byts, kind="prefill", bound=bound), \
             {"B": B, "H": H, "S": S, "D": D, "mod": flex}, None
+    if cfg == 7:
+        # backward of the default batch: the forward runs once beforehand for
+        # O and LSE; a step is one fa_bwd_varlen call (Delta, dK/dV, dQ)
+        lens = synth.varlen_lengths(synth.seed_for(2))
+        d = synth.make_varlen(lens, lens, 16, 16, 128, 128, seed=synth.seed_for(2), device=dev)
+        T = sum(lens)
+        o = torch.empty(T, 16, 128, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(16, T, dtype=torch.float32, device=dev)
+        mods = fa.Mods(causal=True)
+        fa.fa_fwd_varlen(d["q"], d["k"], d["v"], o, lse, d["cu_q"], d["cu_k"], max(lens), max(lens), mods)
+        dout = synth.randn_bf16((T, 16, 128), synth.seed_for(7), device=dev)
+        dq, dk, dvv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+        ws = torch.empty(fa.fa_bwd_workspace_size(T, 16), dtype=torch.uint8, device=dev)
+        # algorithmic: the five products of the backward (S, dP, dV, dK, dQ),
+        # 2.5 times the forward's two, over the visible pairs
+        flops = sum(16 * L * (L + 1) // 2 * 5 * 2 * 128 for L in lens)
+        run = lambda: fa.fa_bwd_varlen(d["q"], d["k"], d["v"], o, dout, lse, dq, dk, dvv, d["cu_q"], d["cu_k"],
+                                       max(lens), max(lens), mods, workspace=ws)
+        name = "varlen causal backward H16 D128 bf16, 8 seqs U[0,4096]"
+        return name, run, dict(flops=flops, kind="backward", bound="mfma"), \
+            {"seqlens": lens, "total_tokens": T, "H": 16, "D": 128, "causal": True}, None
     if cfg == 6:
         # every token of the decode cache (64 sequences, contexts U[1024, 32768],
         # 8 kv-heads, 192/128) quantised from bf16 with per-tensor amax
@@ -340,7 +364,7 @@ def main():
     if args.config in (3, 4) and args.dv != 128:
         key += f"_dv{args.dv}"
     if args.traffic_from:
-        kind = {4: "decode", 6: "kvwrite"}.get(args.config, "prefill")
+        kind = {4: "decode", 6: "kvwrite", 7: "backward"}.get(args.config, "prefill")
         print(json.dumps({key: traffic_from_counters(args.traffic_from[0], args.traffic_from[1], key, kind)}))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
