@@ -147,11 +147,14 @@ __global__ __launch_bounds__(kBwThreads) void fa_bwd_delta_kernel(const BwdArgs 
 // 64-row query tiles that can see any of the workgroup's keys; the Q / dO
 // tiles (and their LSE / Delta rows) of the next step load while the
 // current one is computed.
-// (at D = 128 the K / V fragments and dK / dV accumulators alone take 192
-// registers: one wavefront per SIMD, the rest in accumulation registers)
-template <int D>
-__global__ __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu(D > 64 ? 1 : 2)))
+// MODE 0 computes both; at D = 128 the K / V fragments and both
+// accumulators alone take 192 registers (one wavefront per SIMD), so there
+// MODE 1 (dV: S and dV^T += dO^T P) and MODE 2 (dK: S, dP and dK^T += Q^T dS)
+// run as two kernels of half the registers, two wavefronts per SIMD each.
+template <int D, int MODE>
+__global__ __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu((D > 64 && MODE == 0) ? 1 : 2)))
 void fa_bwd_dkdv_kernel(const BwdArgs a) {
+  constexpr bool DOV = MODE != 2, DOK = MODE != 1;
   constexpr int kRow = D * 2;
   constexpr int kTileB = kBwTile * kRow;
   constexpr int kStage = 2 * kTileB + 2 * kBwTile * 4;
@@ -179,7 +182,7 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       kf[s] = kvalid ? *reinterpret_cast<const bf16x8*>(kp + 16 * s) : bf16x8{};
-      vf[s] = kvalid ? *reinterpret_cast<const bf16x8*>(vp + 16 * s) : bf16x8{};
+      vf[s] = (DOK && kvalid) ? *reinterpret_cast<const bf16x8*>(vp + 16 * s) : bf16x8{};
     }
   }
   f32x16 dk[D / 32], dv[D / 32];
@@ -238,6 +241,12 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
     const float FA_LDS* dl = lse2 + kBwTile;
     const int r0 = (qb0 + n % nqb) * kBwTile;
 
+    // every row of the tile sees every key of this wavefront: no per-score mask
+    const int kw0 = k0 + wave * 32, kw1 = kw0 + 31;
+    bool full = kw1 < sv.skv && r0 + kBwTile <= sv.sq;
+    if (a.causal) full = full && kw1 <= r0 + delta_al;
+    if (a.win_right >= 0) full = full && kw1 <= r0 + delta_al + a.win_right;
+    if (a.win_left >= 0) full = full && kw0 >= r0 + kBwTile - 1 + delta_al - a.win_left;
     // the tile's two 32-row halves one after the other (keeps the S / dP
     // accumulators of one half live at a time)
 #pragma unroll
@@ -249,7 +258,7 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
         const int r = rb * 32 + (lane & 31);
         const int off = r * kRow + (((2 * stp + (lane >> 5)) ^ swz<kRow>(r)) << 4);
         s = mfma32(lds_read_b128(qt + off), kf[stp], s);
-        dp = mfma32(lds_read_b128(dt + off), vf[stp], dp);
+        if (DOK) dp = mfma32(lds_read_b128(dt + off), vf[stp], dp);
       }
       // P and dS (register i: row 32 rb + 8 (i/4) + 4 (lane/32) + i%4)
       bf16x8 pf[2], dsf[2];
@@ -261,15 +270,18 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = q4 * 4 + e;
-          const int qi = r0 + rr + e;
-          const int ip = qi + delta_al;
-          bool vis = kvalid && qi < sv.sq;
-          if (a.causal) vis = vis && key <= ip;
-          if (a.win_right >= 0) vis = vis && key <= ip + a.win_right;
-          if (a.win_left >= 0) vis = vis && key >= ip - a.win_left;
-          const float p = vis ? exp2_hw(fmaf(s[i], C, -l4[e])) : 0.0f;
-          pf[i >> 3][i & 7] = (bf16)p;
-          dsf[i >> 3][i & 7] = (bf16)(p * (dp[i] - d4[e]));
+          float p = exp2_hw(fmaf(s[i], C, -l4[e]));
+          if (!full) {
+            const int qi = r0 + rr + e;
+            const int ip = qi + delta_al;
+            bool vis = kvalid && qi < sv.sq;
+            if (a.causal) vis = vis && key <= ip;
+            if (a.win_right >= 0) vis = vis && key <= ip + a.win_right;
+            if (a.win_left >= 0) vis = vis && key >= ip - a.win_left;
+            p = vis ? p : 0.0f;
+          }
+          if (DOV) pf[i >> 3][i & 7] = (bf16)p;
+          if (DOK) dsf[i >> 3][i & 7] = (bf16)(p * (dp[i] - d4[e]));
         }
       }
       // dV^T += dO^T P and dK^T += Q^T dS over these 32 rows
@@ -277,8 +289,8 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
       for (int uu = 0; uu < 2; ++uu) {
 #pragma unroll
         for (int d = 0; d < D / 32; ++d) {
-          dv[d] = mfma32(tr_fragment<kRow>(dt, rb * 2 + uu, d, lane), pf[uu], dv[d]);
-          dk[d] = mfma32(tr_fragment<kRow>(qt, rb * 2 + uu, d, lane), dsf[uu], dk[d]);
+          if (DOV) dv[d] = mfma32(tr_fragment<kRow>(dt, rb * 2 + uu, d, lane), pf[uu], dv[d]);
+          if (DOK) dk[d] = mfma32(tr_fragment<kRow>(qt, rb * 2 + uu, d, lane), dsf[uu], dk[d]);
         }
       }
     }
@@ -303,8 +315,8 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
           wk[e] = (bf16)(dk[d][gi * 4 + e] * a.qk_scale);
           wv[e] = (bf16)dv[d][gi * 4 + e];
         }
-        *reinterpret_cast<bf16x4*>(kp + d * 32 + gi * 8) = wk;
-        *reinterpret_cast<bf16x4*>(vp + d * 32 + gi * 8) = wv;
+        if (DOK) *reinterpret_cast<bf16x4*>(kp + d * 32 + gi * 8) = wk;
+        if (DOV) *reinterpret_cast<bf16x4*>(vp + d * 32 + gi * 8) = wv;
       }
     }
   }
@@ -374,6 +386,10 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
   const int t_begin = lo_min / kBwTile;
   const int t_end = hi_max >= lo_min ? hi_max / kBwTile : t_begin - 1;
   const int my_lo = row_lo(qrow), my_hi = row_hi(qrow);
+  // this wavefront's rows [wq0, wq1]: the intersection of their key ranges
+  const int wq0 = q0 + wave * 32, wq1 = wq0 + 31;
+  const bool wave_rows_full = wq1 < sv.sq;
+  const int wave_lo_max = row_lo(wq1), wave_hi_min = row_hi(wq0);
   const float C = a.qk_scale * kLog2e;
 
   RowStager<D> st;
@@ -409,15 +425,19 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
         dp[kb] = mfma32(lds_read_b128(vt + off), of[stp], dp[kb]);
       }
     }
-    // dS^T (register i of key block kb: key 32 kb + 8 (i/4) + 4 (lane/32) + i%4)
+    // dS^T (register i of key block kb: key 32 kb + 8 (i/4) + 4 (lane/32) + i%4);
+    // tiles inside every row's key range of this wavefront skip the mask
+    const bool full = wave_rows_full && k0 >= wave_lo_max && k0 + kBwTile - 1 <= wave_hi_min;
     bf16x8 dsf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int j = k0 + kb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-        const bool vis = qvalid && j >= my_lo && j <= my_hi;
-        const float p = vis ? exp2_hw(fmaf(s[kb][i], C, -lse2)) : 0.0f;
+        float p = exp2_hw(fmaf(s[kb][i], C, -lse2));
+        if (!full) {
+          const int j = k0 + kb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+          p = (qvalid && j >= my_lo && j <= my_hi) ? p : 0.0f;
+        }
         dsf[kb * 2 + (i >> 3)][i & 7] = (bf16)(p * (dp[kb][i] - dlt));
       }
     }
@@ -455,8 +475,15 @@ static hipError_t launch_bwd(const BwdArgs& a, int max_sq, int max_skv, hipStrea
     if (e != hipSuccess) return e;
   }
   if (max_skv > 0) {
-    hipLaunchKernelGGL(fa_bwd_dkdv_kernel<D>, dim3(a.B * a.Hkv, (max_skv + kBwKeys - 1) / kBwKeys),
-                       dim3(kBwThreads), 0, stream, a);
+    const dim3 grid(a.B * a.Hkv, (max_skv + kBwKeys - 1) / kBwKeys);
+    if (D > 64) {
+      hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, 1>), grid, dim3(kBwThreads), 0, stream, a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, 2>), grid, dim3(kBwThreads), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, 0>), grid, dim3(kBwThreads), 0, stream, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
