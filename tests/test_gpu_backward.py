@@ -110,3 +110,35 @@ def test_bwd_medium_varlen():
                                       d["cu_q"].numpy(), dict(causal=True))
     for g, r, n in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
         _check_grad(g, r, f"medium {n}")
+
+
+def test_bwd_full_size_sampled():
+    """The default batch's backward (8 sequences up to 3605 tokens, H16,
+    D128, causal) in the launch configuration the benchmark times; checked
+    on the longest sequence for two heads: dQ on sampled rows, dK and dV on
+    sampled keys, against the oracle over that (sequence, head)."""
+    lens = synth.varlen_lengths(synth.seed_for(2))
+    d = synth.make_varlen(lens, lens, 16, 16, 128, 128, seed=synth.seed_for(2))
+    q, k, v = (d[x].to(DEV) for x in ("q", "k", "v"))
+    cu = d["cu_q"].to(DEV)
+    T = q.shape[0]
+    do = synth.randn_bf16((T, 16, 128), synth.seed_for(7))
+    o = torch.empty_like(q)
+    lse = torch.empty((16, T), dtype=torch.float32, device=DEV)
+    mods = fa.Mods(causal=True)
+    fa.fa_fwd_varlen(q, k, v, o, lse, cu, cu, max(lens), max(lens), mods)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_size(T, 16), dtype=torch.uint8, device=DEV)
+    fa.fa_bwd_varlen(q, k, v, o, do.to(DEV), lse, dq, dk, dv, cu, cu, max(lens), max(lens), mods, workspace=ws)
+    torch.cuda.synchronize()
+    b = int(np.argmax(lens))
+    s0, L = int(d["cu_q"][b]), lens[b]
+    rng = np.random.default_rng(5)
+    rows = sorted({0, 1, L - 1, *rng.integers(0, L, 6).tolist()})
+    for h in (0, 11):
+        vis = oracle.visible(L, L, causal=True)
+        gq, gk, gv = oracle.attend_bwd(f64(d["q"][s0:s0 + L, h]), f64(d["k"][s0:s0 + L, h]),
+                                       f64(d["v"][s0:s0 + L, h]), f64(do[s0:s0 + L, h]), 128 ** -0.5, vis)
+        _check_grad(dq[s0:s0 + L, h][rows], gq[rows], f"full dq h{h}")
+        _check_grad(dk[s0:s0 + L, h][rows], gk[rows], f"full dk h{h}")
+        _check_grad(dv[s0:s0 + L, h][rows], gv[rows], f"full dv h{h}")

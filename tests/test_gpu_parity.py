@@ -583,21 +583,36 @@ def test_decode_requires_workspace():
     assert e.value.code == -4
 
 
-def test_decode_full_size_sampled():
-    """64 sequences, contexts uniform in [1024, 32768], GQA 64/8, D 192/128,
-    pages of 64 with a shuffled block table; 6 sequences checked in full."""
+@pytest.mark.parametrize("variant", ["head_major", "vec", "vec_q8", "v192_q8"])
+def test_decode_full_size_sampled(variant):
+    """64 sequences, contexts uniform in [1024, 32768], GQA 64/8, D 192/128
+    (192/192 for v192), pages of 64 with a shuffled block table, in the
+    launch configuration the benchmark times; 6 sequences checked in full,
+    the oracle reading the same page format and query type."""
     lk = synth.make_decode_lengths(synth.seed_for(4))
     lq = [1] * 64
-    d = synth.make_paged(lq, lk, 64, 8, 192, 128, page_size=64, seed=synth.seed_for(4), device=DEV)
-    o, lse = _paged_run(d, dict(causal=True), 128)
+    Dv = 192 if variant.startswith("v192") else 128
+    q8 = variant.endswith("q8")
+    vec = variant != "head_major"
+    d = synth.make_paged(lq, lk, 64, 8, 192, Dv, page_size=64, seed=synth.seed_for(4), device=DEV,
+                         q_dtype="fp8" if q8 else "bf16")
+    if q8:
+        o, lse = _paged_q8_run(d, dict(causal=True), Dv, vec=vec)
+    elif vec:
+        o, lse = _paged_vec_run(d, dict(causal=True), Dv)
+    else:
+        o, lse = _paged_run(d, dict(causal=True), Dv)
+    e = synth.to_vectorized(d) if vec else d
     bsel = [0, 5, 17, 33, 50, 63]
     picks = [(b, h, 0) for b in bsel for h in range(64)]
-    o_ref, l_ref = oracle.paged_rows(f64(d["q"]), f64(d["k_cache"]), f64(d["v_cache"]), d["cu_q"].cpu(),
+    o_ref, l_ref = oracle.paged_rows(f64(d["q"]), f64(e["k_cache"]), f64(e["v_cache"]), d["cu_q"].cpu(),
                                      d["seqlen_k"].cpu(), d["block_table"].cpu(), picks, dict(causal=True),
-                                     float(d["k_descale"]), float(d["v_descale"]))
+                                     float(d["k_descale"]), float(d["v_descale"]),
+                                     layout="vectorized" if vec else "head_major",
+                                     q_descale=float(d["q_descale"]) if q8 else None)
     og = torch.stack([o[b, h] for b, h, _ in picks])
     lg = torch.stack([lse[h, b] for b, h, _ in picks])
-    compare(og, lg, o_ref, l_ref, TOL_O_FP8, what="decode full")
+    compare(og, lg, o_ref, l_ref, TOL_O_FP8, what=f"decode full {variant}")
 
 
 # ----------------------------------------------------------------------------- flex
