@@ -51,15 +51,18 @@
 // seqlen_k are clamped for the load and removed by select before the softmax.
 //
 // Vectorised pages (the 5-D layout of the paged FP8 PR review: K page
-// [Hkv, D/16, page, 16], V page [Hkv, page/16, Dv, 16]) take the same LDS
-// K tile and a different V tile.  A K load instruction covers two 16-byte
-// columns c of the tile's 32 keys (lanes 0-31 column 2i, lanes 32-63 column
-// 2i+1; each half is 512 contiguous bytes) and is stored to the key-row
-// layout above.  A V load covers 64 head dims of one 16-key block (1 KB
-// contiguous): these are already V^T rows, so the tile is kept as V^T
-// [Dv][32 keys] with each row's keys in the order the P^T operand enumerates
-// them, and the A fragments are plain 8-byte reads.  Value bytes past the
-// sequence's end share a 16-byte load with live ones and are cleared.
+// [Hkv, D/16, page, 16], V page [Hkv, page/16, Dv, 16]) keep the cache's
+// order in LDS.  A K load instruction covers two 16-byte columns c of the
+// tile's 32 keys (lanes 0-31 column 2i, lanes 32-63 column 2i+1; each half
+// is 512 contiguous bytes) and lands in a column-major K tile.  A V load
+// covers 64 head dims of one 16-key block (1 KB contiguous): these are
+// already V^T rows, so the tile is kept as V^T [Dv][32 keys] with each row's
+// keys in the order the P^T operand enumerates them, and the A fragments
+// are plain 8-byte reads.  Every 16-byte LDS store of these tiles is
+// contiguous per 16 lanes: measured on the hardware, a 16-byte store whose
+// 16-lane groups do not each write one contiguous 256 bytes takes twice the
+// cycles, whatever its bank pattern.  Value bytes past the sequence's end
+// share a 16-byte load with live ones and are cleared.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -216,10 +219,10 @@ void fa_decode_kernel(const DecodeArgs a) {
   int kst[T::kKLoads], vst[T::kVLoads];
 #pragma unroll
   for (int i = 0; i < T::kKLoads; ++i) {
-    const int off = i * 1024 + lane * 16;
-    const int row = VEC ? (lane & 31) : off / DQK;
-    const int c = VEC ? 2 * i + (lane >> 5) : (off % DQK) >> 4;
-    kst[i] = row * DQK + ((c ^ dec_kswz(row)) << 4);
+    const int off = i * 1024 + lane * 16, row = off / DQK;
+    // vectorised pages: column-major tile (column c of key r at 512 c + 16 r),
+    // so each load's store is contiguous
+    kst[i] = VEC ? off : row * DQK + ((((off % DQK) >> 4) ^ dec_kswz(row)) << 4);
   }
 #pragma unroll
   for (int n = 0; n < T::kVLoads; ++n) {
@@ -233,16 +236,17 @@ void fa_decode_kernel(const DecodeArgs a) {
   const int vsw = dec_vswz<DV>(vrow);
   // V^T tile (vectorised pages): row d is 32 bytes, byte 8 kgrp + e holds key
   // (e / 4) * 16 + 4 kgrp + e % 4, so the lanes of key group kgrp read their
-  // 8 bytes of row 16 blk + lane%16 at 8-byte unit kgrp.  Rows 8-15 of every
-  // 16 swap unit pairs (0,1) <-> (2,3): the 16 rows x 2 units of a half
-  // wavefront then cover the 64 banks once.
-  const char FA_LDS* vtrd = vlds + (lane & 15) * 32 + ((kgrp ^ (((lane >> 3) & 1) << 1)) << 3);
-  const int vtst = lane * 32;                         // row d = lane (and 64 + lane, ...)
-  const int vtsw = ((lane >> 3) & 1) << 4;            // 16-byte half swap of rows 8-15
+  // 8 bytes of row 16 blk + lane%16 at 8-byte unit kgrp.  The two 16-byte
+  // halves of the rows are stored apart (half h of row d at h Dv 16 + 16 d):
+  // a 16-lane group of a 16-byte store then writes one contiguous 256 bytes
+  // (any other pattern measured twice the cycles), and a half wavefront's
+  // reads cover the 64 banks once.
+  const char FA_LDS* vtrd = vlds + (kgrp >> 1) * (DV * 16) + (lane & 15) * 16 + (kgrp & 1) * 8;
+  const int vtst = lane * 16;                         // row d = lane (and 64 + lane, ...)
   // K fragment reads: row kh*16 + lane%16 (the swizzle of r and r+16 agree),
   // chunk 2 st + kgrp/2, half kgrp%2
-  const int krow = lane & 15, kx = dec_kswz(krow);
-  const char FA_LDS* krd = klds + krow * DQK + (kgrp & 1) * 8;
+  const int krow = lane & 15, kx = VEC ? 0 : dec_kswz(krow);
+  const char FA_LDS* krd = klds + (VEC ? krow * 16 : krow * DQK) + (kgrp & 1) * 8;
   const float kdesc = *a.k_descale, vdesc = *a.v_descale;
   // bf16 Q enters scaled by 16 (split below); E4M3 Q enters as it is, with its descale
   const float C = Q8 ? a.qk_scale * kLog2e * kdesc * *a.q_descale : a.qk_scale * kLog2e * kdesc * (1.0f / 16.0f);
@@ -422,9 +426,9 @@ void fa_decode_kernel(const DecodeArgs a) {
 #pragma unroll
         for (int hr = 0; hr < kVPerBlk; ++hr) {
           const i32x4 b0 = vb[hr], b1 = vb[kVPerBlk + hr];
-          char FA_LDS* row = vlds + vtst + hr * 64 * 32;
-          *reinterpret_cast<i32x4 FA_LDS*>(row + vtsw) = i32x4{b0[0], b1[0], b0[1], b1[1]};
-          *reinterpret_cast<i32x4 FA_LDS*>(row + (16 ^ vtsw)) = i32x4{b0[2], b1[2], b0[3], b1[3]};
+          char FA_LDS* row = vlds + vtst + hr * 64 * 16;
+          *reinterpret_cast<i32x4 FA_LDS*>(row) = i32x4{b0[0], b1[0], b0[1], b1[1]};
+          *reinterpret_cast<i32x4 FA_LDS*>(row + DV * 16) = i32x4{b0[2], b1[2], b0[3], b1[3]};
         }
       } else {
 #pragma unroll
@@ -438,6 +442,7 @@ void fa_decode_kernel(const DecodeArgs a) {
       auto kread = [&](int n) {
         const int kh = n / kSteps, st = n % kSteps;
         const int c = (2 * st + (kgrp >> 1)) ^ kx;
+        if (VEC) return *reinterpret_cast<const i32x2 FA_LDS*>(krd + kh * 16 * 16 + c * 512);
         return *reinterpret_cast<const i32x2 FA_LDS*>(krd + kh * 16 * DQK + c * 16);
       };
       f32x4 sacc[NRB][2];
@@ -499,7 +504,7 @@ void fa_decode_kernel(const DecodeArgs a) {
 
       // ---- O^T += V^T P^T ----  (same two-ahead chunking)
       auto vread = [&](int d) {
-        if (VEC) return *reinterpret_cast<const i32x2 FA_LDS*>(vtrd + d * 16 * 32);
+        if (VEC) return *reinterpret_cast<const i32x2 FA_LDS*>(vtrd + d * 16 * 16);
         return lds_read_tr8(vrd + ((d ^ vsw) << 4));
       };
       i32x2 vraw[kDB];
