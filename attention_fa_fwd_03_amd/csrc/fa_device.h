@@ -29,6 +29,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 #define FA_LDS __attribute__((address_space(3)))
 #define FA_GLOBAL __attribute__((address_space(1)))
@@ -109,6 +110,35 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(i32x2 w) {
   r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
   r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
   return r;
+}
+
+// Eight bf16 values x -> E4M3 parts (hi, lo) of 16 x, with 16 x ~= hi + lo:
+// the two 3-bit mantissas carry x to about 2^-8 relative, the factor 16 keeps
+// N(0,1)-scale values clear of the E4M3 subnormal range, and each part times
+// an E4M3 operand is exact in an FP8 product.
+__device__ __forceinline__ void split_e4m3(bf16x8 x, i32x2& hi, i32x2& lo) {
+  float f[8], r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = 16.0f * (float)x[e];
+  int h0 = 0, h1 = 0, l0 = 0, l1 = 0;
+  h0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], h0, false);
+  h0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], h0, true);
+  h1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], h1, false);
+  h1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], h1, true);
+  r[0] = f[0] - __builtin_amdgcn_cvt_f32_fp8(h0, 0);
+  r[1] = f[1] - __builtin_amdgcn_cvt_f32_fp8(h0, 1);
+  r[2] = f[2] - __builtin_amdgcn_cvt_f32_fp8(h0, 2);
+  r[3] = f[3] - __builtin_amdgcn_cvt_f32_fp8(h0, 3);
+  r[4] = f[4] - __builtin_amdgcn_cvt_f32_fp8(h1, 0);
+  r[5] = f[5] - __builtin_amdgcn_cvt_f32_fp8(h1, 1);
+  r[6] = f[6] - __builtin_amdgcn_cvt_f32_fp8(h1, 2);
+  r[7] = f[7] - __builtin_amdgcn_cvt_f32_fp8(h1, 3);
+  l0 = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], l0, false);
+  l0 = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], l0, true);
+  l1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[4], r[5], l1, false);
+  l1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[6], r[7], l1, true);
+  hi = i32x2{h0, h1};
+  lo = i32x2{l0, l1};
 }
 
 // 16 OCP E4M3 bytes -> 16 bf16 (exact).

@@ -36,17 +36,23 @@
 // in a loaded tile skips its math for that tile; tiles wholly inside a
 // wavefront's range skip the per-score mask.
 //
-// K/V staging: bf16 K/V go global -> LDS with global_load_lds_dwordx4 (no
-// registers), one or two tiles ahead; FP8 E4M3 K/V are loaded to registers one
-// tile ahead (two LDS stages), converted
-// exactly to bf16 and written to LDS.  LDS rows are 16-byte-chunk XOR
-// swizzled so that both the K reads and the transposed V reads are
-// bank-conflict free.  Whole tiles take a fast addressing path (per-lane
+// FP8 E4M3 caches keep K as bytes: S^T = K Q^T runs on the FP8 product
+// v_mfma_scale_f32_32x32x64_f8f6f4 (64 dims a step, unit scales) against E4M3
+// queries as given, or against bf16 queries split into two E4M3 parts of
+// 16 q (hi + lo, about 2^-8 relative; each part times a K byte is exact), so
+// the K descale (and the query descale or 1/16) folds into the logit constant.
+//
+// K/V staging: bf16 K/V and FP8 K go global -> LDS with
+// global_load_lds_dwordx4 (no registers), one or two tiles ahead; FP8 V is
+// loaded to registers one tile ahead (two LDS stages), converted exactly to
+// bf16 and written to LDS.  LDS rows are 16-byte-chunk XOR swizzled so that
+// both the K reads and the transposed V reads are bank-conflict free.  Whole tiles take a fast addressing path (per-lane
 // 32-bit offsets from one scalar tile base); the sequence tail and pages
 // smaller than a tile take a clamped per-row path.
 #include "fa_device.h"
 #include "fa_kernels.h"
 #include "fa_prefill_common.h"
+
 
 namespace fa {
 
@@ -60,7 +66,7 @@ constexpr float kLazyTau = 8.0f;
 
 template <int DQK, int DV, bool FP8>
 struct PrefillTraits {
-  static constexpr int kRowK = DQK * 2;            // bytes per bf16 K row in LDS
+  static constexpr int kRowK = FP8 ? DQK : DQK * 2; // bytes per K row in LDS (FP8 K stays E4M3)
   static constexpr int kRowV = DV * 2;
   static constexpr int kTileK = BN * kRowK;
   static constexpr int kTileV = BN * kRowV;
@@ -68,10 +74,6 @@ struct PrefillTraits {
   // two workgroups per CU: at most 80 KB of LDS each
   static constexpr int kStages = FP8 ? 2 : ((3 * (BN * DQK * 2 + BN * DV * 2) <= 81920) ? 3 : 2);
   static constexpr int kLds = kStages * kStage;
-  static constexpr int kKItems = BN * DQK / 16;    // 16-byte source items per K tile (fp8)
-  static constexpr int kVItems = BN * DV / 16;
-  static constexpr int kKPer = (kKItems + NTHREADS - 1) / NTHREADS;
-  static constexpr int kVPer = (kVItems + NTHREADS - 1) / NTHREADS;
 };
 
 // bf16 tile of D columns: global -> LDS with one 1 KB global_load_lds per
@@ -116,8 +118,9 @@ struct Bf16Stager {
   }
 };
 
-// FP8 tile of D columns: 16-byte items loaded to registers one tile ahead,
-// converted exactly to bf16 and written to the swizzled LDS rows.
+// FP8 V tile of D columns (head-major pages): 16-byte items loaded to
+// registers one tile ahead, converted exactly to bf16 and written to the
+// swizzled LDS rows.
 template <int D, bool PAGED>
 struct Fp8Stager {
   static constexpr int kPerRow = D / 16;
@@ -168,55 +171,53 @@ struct Fp8Stager {
 // V page [Hkv, page/16, Dv, 16]).  The (page, kv-head) block starts at
 // page*pg + g*sh; page_shift >= 4.
 
-// K: item idx is 16-byte column f = idx / 64 of tile row r = idx % 64, so one
-// wavefront's load covers 64 keys of one column: 1 KB contiguous when the
-// tile sits in one page.  Stored to the same swizzled key rows as above.
-template <int D>
-struct Fp8VecK {
-  static constexpr int kItems = BN * D / 16;
-  static constexpr int kPer = (kItems + NTHREADS - 1) / NTHREADS;
-  static constexpr int kRow = D * 2;
-  static_assert(kItems % NTHREADS == 0, "whole K items per thread");
-  i32x4 w[kPer];
-  int off[kPer];
-  __device__ __forceinline__ void init(int page_shift, int tid) {
+// FP8 K tile of D bytes per key, staged by LDS DMA as E4M3 bytes (no
+// registers, no conversion): instruction n covers LDS bytes [1024 n, +1024),
+// lane l fills 16 bytes at 16 l: tile row r, stored chunk pos = source
+// chunk pos ^ swz8(r).  Head-major pages read the chunk from the key's row;
+// vectorised pages from column pos ^ swz8(r) of the page.  Whole tiles
+// inside one page take one scalar page lookup, other tiles a per-row one
+// (rows past the sequence re-read its last key).
+template <int D, bool VEC>
+struct Fp8KDma {
+  static constexpr int kPerWave = BN * D / 1024 / NWAVES;
+  static_assert(kPerWave >= 1 && (BN * D) % (1024 * NWAVES) == 0, "whole 1 KB pieces per wavefront");
+  int off[kPerWave];   // byte offset of this lane's source chunk from the tile's first key
+  __device__ __forceinline__ static void place(int i, int wave, int lane, int& row, int& col) {
+    const int byte = (wave * kPerWave + i) * 1024 + lane * 16;
+    row = byte / D;
+    col = ((byte % D) >> 4) ^ swz8<D>(row);
+  }
+  __device__ __forceinline__ void init(int page_shift, int wave, int lane) {
 #pragma unroll
-    for (int it = 0; it < kPer; ++it) {
-      const int idx = it * NTHREADS + tid;
-      off[it] = ((idx / BN) << (page_shift + 4)) + (idx % BN) * 16;
+    for (int i = 0; i < kPerWave; ++i) {
+      int row, col;
+      place(i, wave, lane, row, col);
+      off[i] = VEC ? (col << (page_shift + 4)) + row * 16 : row * D + col * 16;
     }
   }
-  __device__ __forceinline__ void load(const PrefillArgs& a, const SeqView& sv, const uint8_t* base, int k0,
-                                       bool fast, int tid) {
+  __device__ __forceinline__ void issue(const PrefillArgs& a, const SeqView& sv, const uint8_t* base, int k0,
+                                        bool fast, char FA_LDS* tile, int wave, int lane) const {
     const int pmask = (1 << a.page_shift) - 1;
     if (fast) {
       int page = load_uniform_i32(a.block_table, (int64_t)sv.b * a.max_pages + (k0 >> a.page_shift));
       page = min(max(page, 0), a.num_pages - 1);
-      const uint8_t* tb = base + (int64_t)page * a.k_pg + (int64_t)sv.g * a.k_sh + (k0 & pmask) * 16;
+      const uint8_t* tb = base + (int64_t)page * a.k_pg + (int64_t)sv.g * a.k_sh + (k0 & pmask) * (VEC ? 16 : D);
 #pragma unroll
-      for (int it = 0; it < kPer; ++it) w[it] = *reinterpret_cast<const i32x4*>(tb + off[it]);
+      for (int i = 0; i < kPerWave; ++i) global_to_lds16(tb + off[i], tile + (wave * kPerWave + i) * 1024);
     } else {
 #pragma unroll
-      for (int it = 0; it < kPer; ++it) {
-        const int idx = it * NTHREADS + tid;
-        const int j = min(k0 + idx % BN, sv.skv - 1);
+      for (int i = 0; i < kPerWave; ++i) {
+        int row, col;
+        place(i, wave, lane, row, col);
+        const int j = min(k0 + row, sv.skv - 1);
         int page = a.block_table[(int64_t)sv.b * a.max_pages + (j >> a.page_shift)];
         page = min(max(page, 0), a.num_pages - 1);
-        w[it] = *reinterpret_cast<const i32x4*>(base + (int64_t)page * a.k_pg + (int64_t)sv.g * a.k_sh +
-                                                ((idx / BN) << (a.page_shift + 4)) + (j & pmask) * 16);
+        const uint8_t* pb = base + (int64_t)page * a.k_pg + (int64_t)sv.g * a.k_sh;
+        const uint8_t* src = VEC ? pb + ((int64_t)col << (a.page_shift + 4)) + (j & pmask) * 16
+                                 : pb + (int64_t)(j & pmask) * D + col * 16;
+        global_to_lds16(src, tile + (wave * kPerWave + i) * 1024);
       }
-    }
-  }
-  __device__ __forceinline__ void store(char FA_LDS* tile, int tid) const {
-#pragma unroll
-    for (int it = 0; it < kPer; ++it) {
-      const int idx = it * NTHREADS + tid;
-      const int r = idx % BN, f = idx / BN;
-      bf16x8 lo, hi;
-      fp8x16_to_bf16(w[it], lo, hi);
-      char FA_LDS* rowp = tile + r * kRow;
-      *reinterpret_cast<bf16x8 FA_LDS*>(rowp + (((2 * f) ^ swz<kRow>(r)) << 4)) = lo;
-      *reinterpret_cast<bf16x8 FA_LDS*>(rowp + (((2 * f + 1) ^ swz<kRow>(r)) << 4)) = hi;
     }
   }
 };
@@ -278,6 +279,17 @@ struct Fp8VecV {
   }
 };
 
+// C[32 x 32] += A B^T over 64 E4M3 products per output: lane m + 32 h holds
+// bytes 32 h .. 32 h + 31 of row m of A (and of column n of B), unit scales.
+// The accumulator layout is that of the bf16 32x32 product.
+__device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ i32x8 cat8(i32x4 x, i32x4 y) {
+  return i32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+}
+
 // Active-tile bits of the block-mask rows that a workgroup spans (one per
 // 128-query half), 64 mask key-blocks at a time: one vector load and a ballot
 // per row and 64 blocks; the per-tile tests are scalar.  tile_bits(t) has bit
@@ -315,10 +327,11 @@ struct MaskBits {
   }
 };
 
-template <int DQK, int DV, bool FP8, bool PAGED, bool VEC, int MODS>
+template <int DQK, int DV, bool FP8, bool PAGED, bool VEC, bool Q8, int MODS>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_prefill_kernel(const PrefillArgs a) {
   static_assert(!VEC || (FP8 && PAGED), "vectorised pages hold FP8 K/V");
+  static_assert(!Q8 || FP8, "E4M3 queries go with an FP8 cache");
   using T = PrefillTraits<DQK, DV, FP8>;
   __shared__ __attribute__((aligned(1024))) char lds_raw[T::kLds];
   char FA_LDS* lds = (char FA_LDS*)(lds_raw);
@@ -379,23 +392,45 @@ void fa_prefill_kernel(const PrefillArgs a) {
   if (hi_max < lo_min) t_end = t_begin - 1;
 
   // ---- per-lane query row and its Q fragments (B operand of S^T = K Q^T) ----
+  // bf16 K: eight dims per lane and 16-dim step.  FP8 K (E4M3 products, 64
+  // dims a step, 32 per lane): E4M3 queries as they are; bf16 queries as two
+  // E4M3 parts of 16 q (hi + lo), each multiplied exactly.
   const int qrow = q0 + wave * 32 + (lane & 31);
   const bool qvalid = qrow < sv.sq;
-  bf16x8 qf[DQK / 16];
-  const int64_t qoff = (sv.qstart + (qvalid ? qrow : 0)) * a.q_st + (int64_t)sv.h * a.q_sh + (lane >> 5) * 8;
-  if (FP8 && a.q_descale) {
-    // E4M3 queries: converted exactly, the descale folded into the logit constant
-    const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.q) + qoff;
+  constexpr int kQf = FP8 ? 1 : DQK / 16;
+  constexpr int kQ8 = FP8 ? DQK / 64 : 1;
+  bf16x8 qf[kQf];
+  i32x8 qhi[kQ8], qlo[kQ8];
+  const int64_t qrow_off = (sv.qstart + (qvalid ? qrow : 0)) * a.q_st + (int64_t)sv.h * a.q_sh;
+  if (FP8) {
+    if (Q8) {
+      const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.q) + qrow_off + (lane >> 5) * 32;
 #pragma unroll
-    for (int s = 0; s < DQK / 16; ++s) {
-      i32x2 v = *reinterpret_cast<const i32x2*>(qp + s * 16);
-      if (!qvalid) v = i32x2{};
-      qf[s] = fp8x8_to_bf16(v);
+      for (int s = 0; s < kQ8; ++s) {
+        i32x8 v = cat8(*reinterpret_cast<const i32x4*>(qp + s * 64), *reinterpret_cast<const i32x4*>(qp + s * 64 + 16));
+        if (!qvalid) v = i32x8{};
+        qhi[s] = v;
+        qlo[s] = i32x8{};
+      }
+    } else {
+      const bf16* qp = reinterpret_cast<const bf16*>(a.q) + qrow_off + (lane >> 5) * 32;
+#pragma unroll
+      for (int s = 0; s < kQ8; ++s) {
+        i32x2 h[4], l[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + s * 64 + u * 8);
+          if (!qvalid) v = bf16x8{};
+          split_e4m3(v, h[u], l[u]);
+        }
+        qhi[s] = i32x8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+        qlo[s] = i32x8{l[0][0], l[0][1], l[1][0], l[1][1], l[2][0], l[2][1], l[3][0], l[3][1]};
+      }
     }
   } else {
-    const bf16* qp = reinterpret_cast<const bf16*>(a.q) + qoff;
+    const bf16* qp = reinterpret_cast<const bf16*>(a.q) + qrow_off + (lane >> 5) * 8;
 #pragma unroll
-    for (int s = 0; s < DQK / 16; ++s) {
+    for (int s = 0; s < kQf; ++s) {
       bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + s * 16);
       if (!qvalid) v = bf16x8{};
       qf[s] = v;
@@ -415,7 +450,8 @@ void fa_prefill_kernel(const PrefillArgs a) {
   if (FP8) {
     kdesc = *a.k_descale;
     vdesc = *a.v_descale;
-    if (a.q_descale) kdesc *= *a.q_descale;       // both descales scale every logit
+    if (Q8) kdesc *= *a.q_descale;       // both descales scale every logit
+    else kdesc *= 0.0625f;               // the split carries 16 q
   }
   // C: multiplier from the raw MFMA dot product to log2-domain scaled logits
   const float C = ANYMOD ? 1.0f : a.qk_scale * kLog2e * kdesc;
@@ -447,45 +483,38 @@ void fa_prefill_kernel(const PrefillArgs a) {
 
   Bf16Stager<DQK, PAGED> kdma;
   Bf16Stager<DV, PAGED> vdma;
-  Fp8Stager<DQK, PAGED> k8;
+  Fp8KDma<DQK, VEC> k8;
   Fp8Stager<DV, PAGED> v8;
-  Fp8VecK<DQK> kv8;
   Fp8VecV<DV> vv8;
   constexpr int kDmaPerTile = Bf16Stager<DQK, PAGED>::kPerWave + Bf16Stager<DV, PAGED>::kPerWave;
-  if (VEC) {
-    kv8.init(a.page_shift, tid);
-  } else if (FP8) {
-    k8.init(a.k_st, tid);
-    v8.init(a.v_st, tid);
+  if (FP8) {
+    k8.init(a.page_shift, wave, lane);
+    if (!VEC) v8.init(a.v_st, tid);
   } else {
     kdma.init(a.k_st, wave, lane);
     vdma.init(a.v_st, wave, lane);
   }
   auto stage_ptr = [&](int i) { return lds + i * T::kStage; };
-  // bf16: DMA straight into the stage.  FP8: load into registers only.
+  // bf16: K and V by DMA straight into the stage.  FP8: K (E4M3 bytes) by
+  // DMA into the stage, V into registers (converted when stored).
   auto issue = [&](int t, char FA_LDS* st) {
     const int k0 = t * BN;
     const bool fast = fast_tile(k0);
-    if (VEC) {
-      kv8.load(a, sv, reinterpret_cast<const uint8_t*>(a.k), k0, fast, tid);
-      vv8.load(a, sv, reinterpret_cast<const uint8_t*>(a.v), k0, fast, tid);
-    } else if (FP8) {
-      k8.load(a, sv, reinterpret_cast<const uint8_t*>(a.k), a.k_st, a.k_sh, kpg, k0, fast, tid);
-      v8.load(a, sv, reinterpret_cast<const uint8_t*>(a.v), a.v_st, a.v_sh, vpg, k0, fast, tid);
+    if (FP8) {
+      k8.issue(a, sv, reinterpret_cast<const uint8_t*>(a.k), k0, fast, st, wave, lane);
+      if (VEC) vv8.load(a, sv, reinterpret_cast<const uint8_t*>(a.v), k0, fast, tid);
+      else v8.load(a, sv, reinterpret_cast<const uint8_t*>(a.v), a.v_st, a.v_sh, vpg, k0, fast, tid);
     } else {
       kdma.issue(a, sv, reinterpret_cast<const bf16*>(a.k), a.k_st, a.k_sh, kpg, st, k0, fast, wave, lane);
       vdma.issue(a, sv, reinterpret_cast<const bf16*>(a.v), a.v_st, a.v_sh, vpg, st + T::kTileK, k0, fast, wave,
                  lane);
     }
   };
+  // FP8: V registers -> bf16 in the stage, then wait for the K DMA
   auto fp8_store = [&](char FA_LDS* st) {
-    if (VEC) {
-      kv8.store(st, tid);
-      vv8.store(st + T::kTileK, tid);
-    } else {
-      k8.store(st, tid);
-      v8.store(st + T::kTileK, tid);
-    }
+    if (VEC) vv8.store(st + T::kTileK, tid);
+    else v8.store(st + T::kTileK, tid);
+    FA_WAIT_VMCNT(0);
   };
 
   // Tile pipeline: t (computed now, stage sc), t1 and t2 (the next two
@@ -512,7 +541,7 @@ void fa_prefill_kernel(const PrefillArgs a) {
   while (t <= t_end) {
     __syncthreads();   // tile t visible to all; everyone is done with the stage reused below
     if (FP8) {
-      if (t1 <= t_end) issue(t1, nullptr);
+      if (t1 <= t_end) issue(t1, stage_ptr(sc ^ 1));
     } else if (T::kStages == 2) {
       if (t1 <= t_end) issue(t1, stage_ptr(sc ^ 1));
     } else if (t2 <= t_end) {
@@ -528,7 +557,44 @@ void fa_prefill_kernel(const PrefillArgs a) {
       // two independent accumulation chains (key blocks 0 and 1); the K
       // fragments of step s+1 are read while the products of step s run
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
-      {
+      if constexpr (FP8) {
+        // K rows as E4M3: lane holds dims 64 s + 32 (lane/32) + [0, 32) of
+        // key row lane%32 of each block, two 16-byte chunks
+        const int r = lane & 31;                       // swz8(r) == swz8(r + 32)
+        const char FA_LDS* rowp = cur + r * T::kRowK;
+        const int sw = swz8<DQK>(r);
+        const int c0 = 2 * (lane >> 5);
+        auto kread = [&](int s, int kb) {
+          const char FA_LDS* p = rowp + kb * 32 * T::kRowK;
+          return cat8(*reinterpret_cast<const i32x4 FA_LDS*>(p + (((4 * s + c0) ^ sw) << 4)),
+                      *reinterpret_cast<const i32x4 FA_LDS*>(p + (((4 * s + c0 + 1) ^ sw) << 4)));
+        };
+        // two K fragments live: the next step's fragment for a block is read
+        // once that block's last product of this step has been issued
+        constexpr int S = DQK / 64;
+        i32x8 ka = kread(0, 0), kb = kread(0, 1);
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          sacc[0] = mfma32_fp8(ka, qhi[s], sacc[0]);
+          sacc[1] = mfma32_fp8(kb, qhi[s], sacc[1]);
+          if (!Q8) {
+            sacc[0] = mfma32_fp8(ka, qlo[s], sacc[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (s + 1 < S) ka = kread(s + 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            sacc[1] = mfma32_fp8(kb, qlo[s], sacc[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (s + 1 < S) kb = kread(s + 1, 1);
+          } else {
+            __builtin_amdgcn_sched_barrier(0);
+            if (s + 1 < S) {
+              ka = kread(s + 1, 0);
+              kb = kread(s + 1, 1);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
         const int r = lane & 31;                       // swz(r) == swz(r + 32)
         const char FA_LDS* rowp = cur + r * T::kRowK;
         const int sw = swz<T::kRowK>(r);
@@ -697,7 +763,10 @@ void fa_prefill_kernel(const PrefillArgs a) {
 template <int DQK, int DV, bool FP8, bool PAGED, bool VEC, int MODS>
 static hipError_t launch_prefill(const PrefillArgs& a, int n_bh, int n_qtiles, hipStream_t stream) {
   dim3 grid((n_bh + 7) / 8 * 8, n_qtiles);
-  hipLaunchKernelGGL((fa_prefill_kernel<DQK, DV, FP8, PAGED, VEC, MODS>), grid, dim3(NTHREADS), 0, stream, a);
+  if (FP8 && a.q_descale)
+    hipLaunchKernelGGL((fa_prefill_kernel<DQK, DV, FP8, PAGED, VEC, FP8, MODS>), grid, dim3(NTHREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fa_prefill_kernel<DQK, DV, FP8, PAGED, VEC, false, MODS>), grid, dim3(NTHREADS), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -27,6 +27,18 @@ __device__ __forceinline__ int swz(int r) {
   return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
+// FP8 K tile rows of D bytes (kept as E4M3 bytes): chunk c of row r at
+// c ^ swz8<D>(r).  192-byte rows start 48 banks apart, so rows four apart
+// share banks: the map (inside the aligned group of four chunks) sends them
+// elsewhere; 128-byte rows alternate bank halves and the map runs over the
+// whole row.  Either way the 16 rows that 16 lanes read at one chunk fall in
+// 16 different 16-byte bank slots.
+template <int D>
+__device__ __forceinline__ int swz8(int r) {
+  if (D == 128) return (r >> 1) & 7;
+  return (r >> 2) & 3;
+}
+
 // Element offset of key row j in the slow path (tail tiles, pages smaller
 // than a tile): clamped row, per-row page lookup.
 __device__ __forceinline__ int64_t key_row_offset(const PrefillArgs& a, const SeqView& sv, int j,
