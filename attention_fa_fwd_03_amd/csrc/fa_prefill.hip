@@ -64,15 +64,18 @@ constexpr int kMaskRows = 128;          // block-mask query tiles are multiples 
 constexpr int kHalves = BM / kMaskRows; // mask rows one workgroup can span
 constexpr float kLazyTau = 8.0f;
 
-template <int DQK, int DV, bool FP8>
+// VREG: FP8 V goes through registers (converted to bf16 when stored);
+// otherwise FP8 V stays E4M3 in LDS and is converted when read.
+template <int DQK, int DV, bool FP8, bool VREG>
 struct PrefillTraits {
-  static constexpr int kRowK = FP8 ? DQK : DQK * 2; // bytes per K row in LDS (FP8 K stays E4M3)
-  static constexpr int kRowV = DV * 2;
+  static constexpr int kRowK = FP8 ? DQK : DQK * 2;           // bytes per K row in LDS (FP8 K stays E4M3)
+  static constexpr int kRowV = (FP8 && !VREG) ? DV : DV * 2;  // bytes per V row (or V^T block row) in LDS
   static constexpr int kTileK = BN * kRowK;
   static constexpr int kTileV = BN * kRowV;
   static constexpr int kStage = kTileK + kTileV;
-  // two workgroups per CU: at most 80 KB of LDS each
-  static constexpr int kStages = FP8 ? 2 : ((3 * (BN * DQK * 2 + BN * DV * 2) <= 81920) ? 3 : 2);
+  // two workgroups per CU: at most 80 KB of LDS each; V in registers waits
+  // one tile there, so two stages
+  static constexpr int kStages = (!VREG && 3 * kStage <= 81920) ? 3 : 2;
   static constexpr int kLds = kStages * kStage;
 };
 
@@ -279,6 +282,57 @@ struct Fp8VecV {
   }
 };
 
+// FP8 V tile of head-major pages, staged by LDS DMA as E4M3 bytes: tile
+// rows of D bytes (key-major), chunk c of row r at c ^ swzv8<D>(r), read with
+// the transposing byte read.  Whole tiles inside one page take one scalar
+// page lookup, other tiles a per-row one (rows past the sequence re-read its
+// last key, whose p is 0).
+template <int D>
+struct Fp8VDma {
+  static constexpr int kPerWave = BN * D / 1024 / NWAVES;
+  static_assert(kPerWave >= 1 && (BN * D) % (1024 * NWAVES) == 0, "whole 1 KB pieces per wavefront");
+  int off[kPerWave];   // byte offset of this lane's source chunk from the tile's first key
+  __device__ __forceinline__ static void place(int i, int wave, int lane, int& row, int& col) {
+    const int byte = (wave * kPerWave + i) * 1024 + lane * 16;
+    row = byte / D;
+    col = ((byte % D) >> 4) ^ swzv8<D>(row);
+  }
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      int row, col;
+      place(i, wave, lane, row, col);
+      off[i] = row * D + col * 16;
+    }
+  }
+  __device__ __forceinline__ void issue(const PrefillArgs& a, const SeqView& sv, const uint8_t* base, int k0,
+                                        bool fast, char FA_LDS* tile, int wave, int lane) const {
+    const int pmask = (1 << a.page_shift) - 1;
+    if (fast) {
+      int page = load_uniform_i32(a.block_table, (int64_t)sv.b * a.max_pages + (k0 >> a.page_shift));
+      page = min(max(page, 0), a.num_pages - 1);
+      const uint8_t* tb = base + (int64_t)page * a.v_pg + (int64_t)sv.g * a.v_sh + (k0 & pmask) * D;
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i) global_to_lds16(tb + off[i], tile + (wave * kPerWave + i) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i) {
+        int row, col;
+        place(i, wave, lane, row, col);
+        const int j = min(k0 + row, sv.skv - 1);
+        int page = a.block_table[(int64_t)sv.b * a.max_pages + (j >> a.page_shift)];
+        page = min(max(page, 0), a.num_pages - 1);
+        global_to_lds16(base + (int64_t)page * a.v_pg + (int64_t)sv.g * a.v_sh + (int64_t)(j & pmask) * D + col * 16,
+                        tile + (wave * kPerWave + i) * 1024);
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ i32x2 lds_read_tr8(const char FA_LDS* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 FA_LDS*)(p));
+}
+
 // C[32 x 32] += A B^T over 64 E4M3 products per output: lane m + 32 h holds
 // bytes 32 h .. 32 h + 31 of row m of A (and of column n of B), unit scales.
 // The accumulator layout is that of the bf16 32x32 product.
@@ -332,7 +386,10 @@ __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_prefill_kernel(const PrefillArgs a) {
   static_assert(!VEC || (FP8 && PAGED), "vectorised pages hold FP8 K/V");
   static_assert(!Q8 || FP8, "E4M3 queries go with an FP8 cache");
-  using T = PrefillTraits<DQK, DV, FP8>;
+  // FP8 V through registers for vectorised pages and for E4M3 queries at
+  // D_v = 128; E4M3 in LDS otherwise (the faster of the two, measured)
+  constexpr bool VREG = FP8 && (VEC || (Q8 && DV <= 128));
+  using T = PrefillTraits<DQK, DV, FP8, VREG>;
   __shared__ __attribute__((aligned(1024))) char lds_raw[T::kLds];
   char FA_LDS* lds = (char FA_LDS*)(lds_raw);
 
@@ -484,51 +541,57 @@ void fa_prefill_kernel(const PrefillArgs a) {
   Bf16Stager<DQK, PAGED> kdma;
   Bf16Stager<DV, PAGED> vdma;
   Fp8KDma<DQK, VEC> k8;
-  Fp8Stager<DV, PAGED> v8;
+  Fp8VDma<DV> v8d;
+  Fp8Stager<DV, PAGED> v8r;
   Fp8VecV<DV> vv8;
-  constexpr int kDmaPerTile = Bf16Stager<DQK, PAGED>::kPerWave + Bf16Stager<DV, PAGED>::kPerWave;
+  constexpr int kDmaPerTile = FP8 ? Fp8KDma<DQK, VEC>::kPerWave + (VREG ? 0 : Fp8VDma<DV>::kPerWave)
+                                  : Bf16Stager<DQK, PAGED>::kPerWave + Bf16Stager<DV, PAGED>::kPerWave;
   if (FP8) {
     k8.init(a.page_shift, wave, lane);
-    if (!VEC) v8.init(a.v_st, tid);
+    if (!VREG) v8d.init(wave, lane);
+    else if (!VEC) v8r.init(a.v_st, tid);
   } else {
     kdma.init(a.k_st, wave, lane);
     vdma.init(a.v_st, wave, lane);
   }
   auto stage_ptr = [&](int i) { return lds + i * T::kStage; };
-  // bf16: K and V by DMA straight into the stage.  FP8: K (E4M3 bytes) by
-  // DMA into the stage, V into registers (converted when stored).
+  // K (and V unless VREG) by DMA straight into the stage, FP8 as E4M3
+  // bytes; VREG: V into registers, converted when stored (fp8_store)
   auto issue = [&](int t, char FA_LDS* st) {
     const int k0 = t * BN;
     const bool fast = fast_tile(k0);
     if (FP8) {
       k8.issue(a, sv, reinterpret_cast<const uint8_t*>(a.k), k0, fast, st, wave, lane);
-      if (VEC) vv8.load(a, sv, reinterpret_cast<const uint8_t*>(a.v), k0, fast, tid);
-      else v8.load(a, sv, reinterpret_cast<const uint8_t*>(a.v), a.v_st, a.v_sh, vpg, k0, fast, tid);
+      if (!VREG) v8d.issue(a, sv, reinterpret_cast<const uint8_t*>(a.v), k0, fast, st + T::kTileK, wave, lane);
+      else if (VEC) vv8.load(a, sv, reinterpret_cast<const uint8_t*>(a.v), k0, fast, tid);
+      else v8r.load(a, sv, reinterpret_cast<const uint8_t*>(a.v), a.v_st, a.v_sh, vpg, k0, fast, tid);
     } else {
       kdma.issue(a, sv, reinterpret_cast<const bf16*>(a.k), a.k_st, a.k_sh, kpg, st, k0, fast, wave, lane);
       vdma.issue(a, sv, reinterpret_cast<const bf16*>(a.v), a.v_st, a.v_sh, vpg, st + T::kTileK, k0, fast, wave,
                  lane);
     }
   };
-  // FP8: V registers -> bf16 in the stage, then wait for the K DMA
+
+  // VREG: the registers -> bf16 in the stage, then wait for the K copies
   auto fp8_store = [&](char FA_LDS* st) {
     if (VEC) vv8.store(st + T::kTileK, tid);
-    else v8.store(st + T::kTileK, tid);
+    else v8r.store(st + T::kTileK, tid);
     FA_WAIT_VMCNT(0);
   };
 
   // Tile pipeline: t (computed now, stage sc), t1 and t2 (the next two
-  // active tiles).  bf16 keeps t and t1 (and after the issue below t2) in
-  // flight in the stage ring; FP8 keeps t1 in registers.
+  // active tiles).  A three-stage ring keeps t and t1 (and after the issue
+  // below t2) in flight; a two-stage ring t and t1; VREG keeps t1's V in
+  // registers.
   unsigned hb, hb1, hb2;
   int t = next_tile(t_begin, hb);
   int t1 = t <= t_end ? next_tile(t + 1, hb1) : t_end + 1;
-  int t2 = (!FP8 && t1 <= t_end) ? next_tile(t1 + 1, hb2) : t_end + 1;
-  if (FP8) hb2 = 0;
+  int t2 = (!VREG && t1 <= t_end) ? next_tile(t1 + 1, hb2) : t_end + 1;
+  if (VREG) hb2 = 0;
   int sc = 0;
   if (t <= t_end) {
     issue(t, stage_ptr(0));
-    if (FP8) {
+    if (VREG) {
       fp8_store(stage_ptr(0));
     } else if (T::kStages == 3 && t1 <= t_end) {
       issue(t1, stage_ptr(1));
@@ -540,10 +603,8 @@ void fa_prefill_kernel(const PrefillArgs a) {
 
   while (t <= t_end) {
     __syncthreads();   // tile t visible to all; everyone is done with the stage reused below
-    if (FP8) {
-      if (t1 <= t_end) issue(t1, stage_ptr(sc ^ 1));
-    } else if (T::kStages == 2) {
-      if (t1 <= t_end) issue(t1, stage_ptr(sc ^ 1));
+    if (T::kStages == 2) {
+      if (t1 <= t_end) issue(t1, stage_ptr(sc ^ 1));   // VREG: K copies and V registers
     } else if (t2 <= t_end) {
       const int s2 = sc + 2 < T::kStages ? sc + 2 : sc + 2 - T::kStages;
       issue(t2, stage_ptr(s2));
@@ -677,7 +738,27 @@ void fa_prefill_kernel(const PrefillArgs a) {
       }
 
       // ---------------- O^T += V^T P^T ----------------
-      if (VEC) {
+      // A = V^T: lane m + 32 h takes d = 32 blk + m and, of the 16 keys of
+      // step u, keys 4h..4h+3 and 8+4h..8+4h+3 (the order of P^T)
+      if constexpr (FP8 && !VREG) {
+        // E4M3 key-major rows: lanes 2t+q of a 16-lane group read half q of
+        // row t of the group's eight keys; the transposing read gives lane i
+        // byte column i of those rows, converted exactly to bf16
+        const char FA_LDS* vt = cur + T::kTileK;
+        const int h = lane >> 5;
+        const int i16 = lane & 15, t8 = i16 >> 1, q = i16 & 1;
+        const int key = (t8 < 4 ? t8 : 4 + t8) + 4 * h;   // key within the 16-key step
+        const int cg = (lane >> 4) & 1;                    // 16-dim half of the 32-dim block
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = u * 16 + key;
+          const char FA_LDS* rp = vt + r * DV + q * 8;
+          const int sw = swzv8<DV>(r);
+#pragma unroll
+          for (int d = 0; d < DV / 32; ++d)
+            oacc[d] = mfma32(fp8x8_to_bf16(lds_read_tr8(rp + (((2 * d + cg) ^ sw) << 4))), pf[u], oacc[d]);
+        }
+      } else if constexpr (VEC) {
         // V^T tile: row d = 32 blk + lane%32, chunk 2u + lane/32
         const char FA_LDS* vt = cur + T::kTileK + (lane & 31) * (BN * 2);
         const int sw = ((lane & 31) >> 1) & 7;
@@ -710,10 +791,10 @@ void fa_prefill_kernel(const PrefillArgs a) {
       }
     }
 
-    // publish the next tile: FP8 converts its registers into the other
-    // stage; bf16 waits for its own DMA of t1 (t2 may stay in flight)
+    // publish the next tile: wait for this wavefront's copies of t1 (t2 may
+    // stay in flight)
     const int s1 = sc + 1 < T::kStages ? sc + 1 : 0;
-    if (FP8) {
+    if (VREG) {
       if (t1 <= t_end) fp8_store(stage_ptr(s1));
     } else if (T::kStages == 3 && t2 <= t_end) {
       FA_WAIT_VMCNT(kDmaPerTile);
@@ -723,7 +804,7 @@ void fa_prefill_kernel(const PrefillArgs a) {
     sc = s1;
     t = t1;
     hb = hb1;
-    if (FP8) {
+    if (VREG) {
       t1 = t1 <= t_end ? next_tile(t1 + 1, hb1) : t_end + 1;
     } else {
       t1 = t2;

@@ -39,6 +39,20 @@ __device__ __forceinline__ int swz8(int r) {
   return (r >> 2) & 3;
 }
 
+// FP8 V tile rows of D bytes (key-major E4M3): chunk c of row r at
+// c ^ swzv8<D>(r).  A transposing byte read of half a wavefront takes the
+// keys {0-3, 8-11} of a 16-key step (the other half: +4) at two adjacent
+// chunks.  128-byte rows alternate bank halves: the map gives the four rows
+// of each parity four different even chunk offsets, so the 16 pieces fill
+// all 64 banks.  192-byte rows repeat their bank offset every four rows:
+// the map moves rows 8..11 (and 12..15) to the other chunk pair of their
+// aligned group of four.
+template <int D>
+__device__ __forceinline__ int swzv8(int r) {
+  if (D == 128) return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2);
+  return ((r >> 3) & 1) << 1;
+}
+
 // Element offset of key row j in the slow path (tail tiles, pages smaller
 // than a tile): clamped row, per-row page lookup.
 __device__ __forceinline__ int64_t key_row_offset(const PrefillArgs& a, const SeqView& sv, int j,
