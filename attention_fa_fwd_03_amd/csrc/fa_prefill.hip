@@ -42,11 +42,14 @@
 // 16 q (hi + lo, about 2^-8 relative; each part times a K byte is exact), so
 // the K descale (and the query descale or 1/16) folds into the logit constant.
 //
-// K/V staging: bf16 K/V and FP8 K go global -> LDS with
-// global_load_lds_dwordx4 (no registers), one or two tiles ahead; FP8 V is
-// loaded to registers one tile ahead (two LDS stages), converted exactly to
+// K/V staging: bf16 K/V, FP8 K and the FP8 V of head-major pages go
+// global -> LDS with global_load_lds_dwordx4 (no registers), one or two
+// tiles ahead; FP8 V stays E4M3 there and its P.V fragments come from the
+// transposing byte read (ds_read_b64_tr_b8), converted exactly to bf16.  For
+// vectorised pages, and for E4M3 queries at D_v = 128, FP8 V is loaded to
+// registers one tile ahead instead (two LDS stages), converted exactly to
 // bf16 and written to LDS.  LDS rows are 16-byte-chunk XOR swizzled so that
-// both the K reads and the transposed V reads are bank-conflict free.  Whole tiles take a fast addressing path (per-lane
+// the K reads and the transposed V reads are bank-conflict free.  Whole tiles take a fast addressing path (per-lane
 // 32-bit offsets from one scalar tile base); the sequence tail and pages
 // smaller than a tile take a clamped per-row path.
 #include "fa_device.h"
