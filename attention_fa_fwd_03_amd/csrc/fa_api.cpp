@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 
 #include "fa.h"
@@ -96,6 +97,15 @@ int read_mods(const fa_mods* m, int64_t d_qk, int64_t max_sq, int64_t max_sk, Mo
   if (!std::isfinite(r.scale)) return fail(FA_ERR_INVALID, "softmax_scale must be finite");
   *out = r;
   return FA_OK;
+}
+
+// The kernels move tensors 16 bytes at a time (vector loads, LDS DMA):
+// tensor bases must be 16-byte aligned, and every row then is (head dims are
+// multiples of 8 elements); fp32 and int32 arrays 4-byte, int64 8-byte.
+bool misaligned(uintptr_t align, std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p && (reinterpret_cast<uintptr_t>(p) % align) != 0) return true;
+  return false;
 }
 
 int clamp_i32(int64_t w) {
@@ -234,6 +244,8 @@ int fa_fwd_dense(const void* q, const void* k, const void* v, void* o, float* ls
   if (B == 0 || Sq == 0) return FA_OK;
   if (!q || !o || !lse) return fail(FA_ERR_INVALID, "q, o and lse must be non-NULL");
   if (Skv > 0 && (!k || !v)) return fail(FA_ERR_INVALID, "k and v must be non-NULL");
+  if (misaligned(16, {q, k, v, o}) || misaligned(4, {lse}))
+    return fail(FA_ERR_INVALID, "q, k, v and o must be 16-byte aligned, lse 4-byte aligned");
   const size_t nq = (size_t)(B * Sq * Hq * d_qk) * 2, no = (size_t)(B * Sq * Hq * d_v) * 2;
   const size_t nk = (size_t)(B * Skv * Hkv * d_qk) * 2, nv = (size_t)(B * Skv * Hkv * d_v) * 2;
   const size_t nl = (size_t)(B * Hq * Sq) * 4;
@@ -278,6 +290,8 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   if (B == 0 || total_q == 0) return FA_OK;
   if (!q || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return fail(FA_ERR_INVALID, "q, o, lse and cu_seqlens must be non-NULL");
   if (total_k > 0 && (!k || !v)) return fail(FA_ERR_INVALID, "k and v must be non-NULL");
+  if (misaligned(16, {q, k, v, o}) || misaligned(4, {lse, cu_seqlens_q, cu_seqlens_k}))
+    return fail(FA_ERR_INVALID, "q, k, v and o must be 16-byte aligned, lse and cu_seqlens 4-byte aligned");
   const size_t nq = (size_t)(total_q * Hq * d_qk) * 2, no = (size_t)(total_q * Hq * d_v) * 2;
   const size_t nk = (size_t)(total_k * Hkv * d_qk) * 2, nv = (size_t)(total_k * Hkv * d_v) * 2;
   const size_t nl = (size_t)(Hq * total_q) * 4;
@@ -366,6 +380,9 @@ int paged_impl(const fa_paged_opts* opts, const void* q, const void* k_cache, co
   if (num_pages > 0 && (!k_cache || !v_cache)) return fail(FA_ERR_INVALID, "caches must be non-NULL");
   if (max_seqlen_k > 0 && num_pages == 0) return fail(FA_ERR_INVALID, "num_pages is 0 but max_seqlen_k > 0");
   if (fp8 && (!k_descale || !v_descale)) return fail(FA_ERR_INVALID, "FP8 caches need k_descale and v_descale");
+  if (misaligned(16, {q, k_cache, v_cache, o, workspace}) ||
+      misaligned(4, {lse, cu_seqlens_q, seqlen_k, block_table, k_descale, v_descale}))
+    return fail(FA_ERR_INVALID, "q, the caches, o and workspace must be 16-byte aligned, the other arrays 4-byte aligned");
   const size_t es = fp8 ? 1 : 2;
   const size_t nq = (size_t)(total_q * Hq * d_qk) * (q8 ? 1 : 2), no = (size_t)(total_q * Hq * d_v) * 2;
   const size_t nk = (size_t)num_pages * Hkv * page_size * d_qk * es, nv = (size_t)num_pages * Hkv * page_size * d_v * es;
@@ -543,6 +560,10 @@ int fa_kv_cache_write_fp8(const void* k, const void* v, const int64_t* slot_mapp
   if (!k || !v || !slot_mapping || !k_descale || !v_descale)
     return fail(FA_ERR_INVALID, "k, v, slot_mapping and the descales must be non-NULL");
   if (num_pages > 0 && (!k_cache || !v_cache)) return fail(FA_ERR_INVALID, "caches must be non-NULL");
+  if (misaligned(16, {k, v, k_cache, v_cache, workspace}) || misaligned(8, {slot_mapping}) ||
+      misaligned(4, {k_descale, v_descale}))
+    return fail(FA_ERR_INVALID, "k, v, the caches and workspace must be 16-byte aligned, slot_mapping 8-byte, "
+                "the descales 4-byte");
   const size_t nk = (size_t)(T * Hkv * d_qk) * 2, nv = (size_t)(T * Hkv * d_v) * 2;
   const size_t ck = (size_t)num_pages * Hkv * page_size * d_qk, cv = (size_t)num_pages * Hkv * page_size * d_v;
   if (overlaps(k_cache, ck, v_cache, cv) || overlaps(k_cache, ck, k, nk) || overlaps(k_cache, ck, v, nv) ||
@@ -622,6 +643,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   if (B == 0 || (total_q == 0 && total_k == 0)) return FA_OK;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || (cu_q && !cu_k))
     return fail(FA_ERR_INVALID, "tensor pointers must be non-NULL");
+  if (misaligned(16, {q, k, v, o, dout, dq, dk, dv, workspace}) || misaligned(4, {lse, cu_q, cu_k}))
+    return fail(FA_ERR_INVALID, "tensors and workspace must be 16-byte aligned, lse and cu_seqlens 4-byte aligned");
   const size_t need = fa_bwd_workspace_size(total_q, Hq);
   if (need && (!workspace || workspace_bytes < need))
     return fail(FA_ERR_WORKSPACE, "the backward needs a workspace of %zu bytes (got %zu)", need, workspace_bytes);

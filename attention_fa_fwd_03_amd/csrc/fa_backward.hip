@@ -117,23 +117,33 @@ __device__ __forceinline__ bf16x8 tr_fragment(const char FA_LDS* tile, int u, in
 __device__ __forceinline__ float lse_log2(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
 
 // ---------------------------------------------------------------- Delta
-// One wavefront per (row, head): Delta = dO . O in fp32.
+// Delta = dO . O in fp32 per (row, head): D / 8 lanes per (row, head), one
+// 16-byte piece of O and of dO each, summed over the lanes of the row.
+template <int D>
+struct DeltaShape {
+  static constexpr int kLanes = D / 8;                 // lanes per (row, head)
+  static constexpr int kRows = 64 / kLanes;            // (row, head) items per wavefront
+};
+
 template <int D>
 __global__ __launch_bounds__(kBwThreads) void fa_bwd_delta_kernel(const BwdArgs a) {
-  constexpr int kPer = D / 64;
+  using S = DeltaShape<D>;
   const int lane = threadIdx.x & 63;
-  const int64_t item = (int64_t)blockIdx.x * kBwWaves + (threadIdx.x >> 6);
-  if (item >= a.total_rows * a.Hq) return;
-  const int64_t t = item / a.Hq;
-  const int h = (int)(item - t * a.Hq);
-  const bf16* op = a.o + t * a.o_st + (int64_t)h * a.o_sh + lane * kPer;
-  const bf16* dp = a.dout + t * a.o_st + (int64_t)h * a.o_sh + lane * kPer;
+  const int64_t item = ((int64_t)blockIdx.x * kBwWaves + (threadIdx.x >> 6)) * S::kRows + lane / S::kLanes;
+  const int piece = lane % S::kLanes;
+  const bool ok = item < a.total_rows * a.Hq;
+  const int64_t t = ok ? item / a.Hq : 0;
+  const int h = ok ? (int)(item - t * a.Hq) : 0;
   float acc = 0.0f;
+  if (ok) {
+    const bf16x8 o = *reinterpret_cast<const bf16x8*>(a.o + t * a.o_st + (int64_t)h * a.o_sh + piece * 8);
+    const bf16x8 g = *reinterpret_cast<const bf16x8*>(a.dout + t * a.o_st + (int64_t)h * a.o_sh + piece * 8);
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) acc += (float)op[e] * (float)dp[e];
+    for (int e = 0; e < 8; ++e) acc += (float)o[e] * (float)g[e];
+  }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-  if (lane == 0) {
+  for (int off = S::kLanes / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (ok && piece == 0) {
     int64_t li;
     if (a.cu_q) li = (int64_t)h * a.lse_tq + t;
     else li = ((t / a.Sq) * a.Hq + h) * a.Sq + t % a.Sq;
@@ -469,8 +479,9 @@ template <int D>
 static hipError_t launch_bwd(const BwdArgs& a, int max_sq, int max_skv, hipStream_t stream) {
   const int64_t rows = a.total_rows * a.Hq;
   if (rows > 0) {
-    hipLaunchKernelGGL(fa_bwd_delta_kernel<D>, dim3((unsigned)((rows + kBwWaves - 1) / kBwWaves)), dim3(kBwThreads),
-                       0, stream, a);
+    const int64_t per_wg = (int64_t)kBwWaves * DeltaShape<D>::kRows;
+    hipLaunchKernelGGL(fa_bwd_delta_kernel<D>, dim3((unsigned)((rows + per_wg - 1) / per_wg)), dim3(kBwThreads), 0,
+                       stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -25,6 +25,9 @@
  *    never allocates, frees or keeps them.  Tensors are contiguous in the
  *    layouts stated per function; bf16 means IEEE bfloat16, FP8 means OCP
  *    E4M3 (e4m3fn, max 448, 0x7F/0xFF NaN).
+ *  - Tensor and workspace pointers must be 16-byte aligned (the kernels
+ *    move 16 bytes at a time), fp32 and int32 arrays 4-byte aligned and the
+ *    int64 slot mapping 8-byte aligned; otherwise FA_ERR_INVALID.
  *  - Sizes are int64_t host values.  Token counts, page counts and every
  *    flattened tensor extent must stay below 2^31 elements (FA_ERR_LIMIT);
  *    byte offsets inside the kernels are 64-bit.
@@ -53,7 +56,7 @@ extern "C" {
 #endif
 
 #define FA_OK 0
-#define FA_ERR_INVALID (-1)     /* null / aliasing pointers, inconsistent sizes */
+#define FA_ERR_INVALID (-1)     /* null / aliasing / misaligned pointers, inconsistent sizes */
 #define FA_ERR_UNSUPPORTED (-2) /* head-dim pair, dtype, page size or mod combination not built */
 #define FA_ERR_LIMIT (-3)       /* a count or flattened extent >= 2^31 */
 #define FA_ERR_WORKSPACE (-4)   /* workspace missing or too small */

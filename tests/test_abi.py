@@ -76,6 +76,12 @@ def test_dense_rejects(kw, code, frag):
     assert rc == code and frag in msg, (rc, msg)
 
 
+@pytest.mark.parametrize("kw", [dict(q=FAKE + 8), dict(v=FAKE * 3 + 4), dict(o=FAKE * 4 + 2), dict(lse=FAKE * 5 + 2)])
+def test_dense_rejects_misaligned_pointers(kw):
+    rc, msg = _dense(**kw)
+    assert rc == -1 and "aligned" in msg, (rc, msg)
+
+
 def test_dense_rejects_lse_overlapping_o():
     rc, msg = _dense(o=FAKE * 4, lse=FAKE * 4 + 8)
     assert rc == -1 and "overlap" in msg
@@ -139,6 +145,12 @@ def _paged(vec=False, opts=None, **kw):
 def test_paged_rejects(kw, code, frag):
     rc, msg = _paged(**kw)
     assert rc == code and frag in msg, (rc, msg)
+
+
+@pytest.mark.parametrize("kw", [dict(kc=FAKE * 2 + 8), dict(bt=FAKE * 8 + 2), dict(ws=FAKE * 64 + 4)])
+def test_paged_rejects_misaligned_pointers(kw):
+    rc, msg = _paged(**kw)
+    assert rc == -1 and "aligned" in msg, (rc, msg)
 
 
 @pytest.mark.parametrize("kw,code,frag", [
@@ -221,6 +233,12 @@ def test_kv_cache_write_rejects(kw, code, frag):
     assert rc == code and frag in msg, (rc, msg)
 
 
+@pytest.mark.parametrize("kw", [dict(k=FAKE + 8), dict(sm=FAKE * 3 + 4), dict(vc=FAKE * 40 + 1)])
+def test_kv_cache_write_rejects_misaligned_pointers(kw):
+    rc, msg = _kvw(**kw)
+    assert rc == -1 and "aligned" in msg, (rc, msg)
+
+
 def test_kv_cache_write_empty_and_workspace_query():
     fa = _lib()
     assert _kvw(T=0, k=0, v=0, sm=0, ws=0)[0] == 0
@@ -250,6 +268,14 @@ def _bwd(**kw):
 def test_bwd_rejects(kw, code, frag):
     rc, msg = _bwd(**kw)
     assert rc == code and frag in msg, (rc, msg)
+
+
+def test_bwd_rejects_misaligned_pointers():
+    fa = _lib()
+    ptrs = [FAKE * (i + 1) for i in range(9)]
+    ptrs[6] += 8    # dq
+    rc = fa.lib.fa_bwd_dense(*ptrs, 1, 16, 16, 2, 2, 64, 64, None, FAKE * 30, 1 << 20, None)
+    assert rc == -1 and "aligned" in fa.fa_last_error()
 
 
 def test_bwd_rejects_score_mods_and_overlap():
