@@ -5,9 +5,10 @@
 // 80 KB, so two workgroups share each CU and each SIMD runs one wavefront of
 // each: their barriers are independent, so one workgroup's vector and scalar
 // stretches overlap the other's matrix work.  The key axis is walked in tiles
-// of 64 keys staged in LDS (bf16 at D <= 64: a ring of three stages, two
-// tiles in flight; at D = 128: two stages, the next tile loads while the
-// current one is computed).  Per tile and wavefront:
+// of 64 keys staged in LDS (a ring of three stages, two tiles in flight, when
+// three fit in 80 KB: bf16 at D <= 64 and the FP8 caches; otherwise two
+// stages, the next tile loading while the current one is computed).  Per
+// tile and wavefront:
 //
 //   S^T[64 x 32]  = K_tile . Q^T          v_mfma_f32_32x32x16_bf16, A = K from LDS,
 //                                          B = Q fragments kept in registers
