@@ -297,16 +297,19 @@ def _paged_vec_run(d, mods_kw, Dv):
     return o, lse
 
 
+@pytest.mark.parametrize("decode", [False, True])
 @pytest.mark.parametrize("vec", [False, True])
 @pytest.mark.parametrize("dv", [128, 192])
-def test_paged_fp8_peaked_queries_pair_k_with_v(vec, dv):
-    """Paged FP8 prefill with each query equal to 1.5 x the dequantised K row
-    of one visible key: the softmax concentrates on that key, so any K/V row
-    pairing mistake in the E4M3 staging or the transposed byte reads shows as
-    a large O error (random queries spread P too thinly to expose it)."""
+def test_paged_fp8_peaked_queries_pair_k_with_v(vec, dv, decode):
+    """Paged FP8 prefill (or single-query decode) with each query equal to
+    1.5 x the dequantised K row of one visible key: the softmax concentrates
+    on that key, so any K/V row pairing mistake in the E4M3 staging or the
+    transposed byte reads shows as a large O error (random queries spread P
+    too thinly to expose it)."""
     L = [200, 77]
-    Hq, Hkv = 4, 2
-    d = synth.make_paged(L, L, Hq, Hkv, 192, dv, page_size=16 if vec else 64, seed=97)
+    lq = [1, 1] if decode else L
+    Hq, Hkv = (16, 2) if decode else (4, 2)
+    d = synth.make_paged(lq, L, Hq, Hkv, 192, dv, page_size=16 if vec else 64, seed=97)
     gen = torch.Generator().manual_seed(5)
     q = d["q"].clone()
     cu = d["cu_q"].tolist()
@@ -314,15 +317,17 @@ def test_paged_fp8_peaked_queries_pair_k_with_v(vec, dv):
     for b, n in enumerate(L):
         rows = [oracle.gather_paged(f64(d["k_cache"]), d["block_table"][b].numpy(), n, g, float(d["k_descale"]))
                 for g in range(Hkv)]
-        for i in range(n):
-            j = int(torch.randint(0, i + 1, (1,), generator=gen))     # a key row i sees (causal)
+        for i in range(lq[b]):
+            ip = i + n - lq[b]                                         # aligned position (bottom-right)
+            j = int(torch.randint(0, ip + 1, (1,), generator=gen))    # a key row i sees (causal)
             picks.append((b, i, j))
             for h in range(Hq):
                 q[cu[b] + i, h] = synth.peaked_queries(torch.from_numpy(rows[h // (Hq // Hkv)][j]), 1.5)
     d["q"] = q
     o, lse = (_paged_vec_run(d, dict(causal=True), dv) if vec else _paged_run(d, dict(causal=True), dv))
     o_ref, l_ref = _paged_ref(d, dict(causal=True))
-    compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_FP8, what=f"peaked vec={vec} dv={dv}")
+    compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, TOL_O_FP8,
+            what=f"peaked vec={vec} dv={dv} decode={decode}")
     # the peak dominates: O of head 0 is close to the picked V row
     worst = 0.0
     for b, n in enumerate(L):
