@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_prefill.hip", "fa_decode.hip", "fa_kvcache.hip", "fa_backward.hip", "fa_api.cpp"]
+SOURCES = ["fa_prefill.hip", "fa_prefill_bf16.hip", "fa_decode.hip", "fa_kvcache.hip", "fa_backward.hip", "fa_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

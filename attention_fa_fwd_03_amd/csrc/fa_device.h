@@ -100,6 +100,19 @@ __device__ __forceinline__ void global_to_lds16(const void* gsrc, char FA_LDS* l
   __builtin_amdgcn_global_load_lds((const FA_GLOBAL void*)(gsrc), (FA_LDS void*)(lds_base), 16, 0, 0);
 }
 
+// Buffer descriptor over [base, base + 2^31): raw (unstrided) 32-bit
+// offsets; loads past the end return zeros.  The third word is the gfx9
+// default (32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+
+// 16 bytes at byte offset voff of the descriptor's range straight into LDS
+// (base + 16*lane).
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rs, unsigned voff, char FA_LDS* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)(lds_base), 16, voff, 0, 0, 0);
+}
+
 // 8 OCP E4M3 bytes -> 8 bf16 (exact).
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(i32x2 w) {
   bf16x8 r;

@@ -158,6 +158,8 @@ hipError_t kv_write_dispatch(const KvWriteArgs& a, bool vec, hipStream_t stream)
 
 hipError_t prefill_dispatch(const PrefillArgs& a, int dqk, int dv, bool fp8, bool paged, bool vec, int mods,
                             int n_bh, int n_qtiles, hipStream_t stream, bool* supported);
+hipError_t prefill_bf16_dispatch(const PrefillArgs& a, int d, bool paged, int mods, int n_bh, int n_qtiles,
+                                 hipStream_t stream, bool* supported);
 hipError_t decode_dispatch(const DecodePlanArgs& plan, const DecodeArgs& a, int dqk, int dv, bool fp8, bool vec,
                            bool q8, hipStream_t stream, bool* supported);
 hipError_t combine_dispatch(const CombineArgs& a, int dv, hipStream_t stream, bool* supported);

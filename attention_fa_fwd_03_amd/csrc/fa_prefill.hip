@@ -60,14 +60,6 @@
 
 namespace fa {
 
-constexpr int NWAVES = 4;
-constexpr int BM = 32 * NWAVES;
-constexpr int BN = 64;
-constexpr int NTHREADS = 64 * NWAVES;
-constexpr int kMaskRows = 128;          // block-mask query tiles are multiples of this
-constexpr int kHalves = BM / kMaskRows; // mask rows one workgroup can span
-constexpr float kLazyTau = 8.0f;
-
 // VREG: FP8 V goes through registers (converted to bf16 when stored);
 // otherwise FP8 V stays E4M3 in LDS and is converted when read.
 template <int DQK, int DV, bool FP8, bool VREG>
@@ -81,48 +73,6 @@ struct PrefillTraits {
   // one tile there, so two stages
   static constexpr int kStages = (!VREG && 3 * kStage <= 81920) ? 3 : 2;
   static constexpr int kLds = kStages * kStage;
-};
-
-// bf16 tile of D columns: global -> LDS with one 1 KB global_load_lds per
-// wave instruction.  Instruction n covers LDS bytes [n*1024, n*1024+1024);
-// lane l fills 16 bytes at n*1024 + 16*l, i.e. tile row r, stored chunk pos,
-// which holds source chunk pos ^ swz(r).
-template <int D, bool PAGED>
-struct Bf16Stager {
-  static constexpr int kRow = D * 2;
-  static constexpr int kPerWave = BN * kRow / 1024 / NWAVES;
-  static_assert(kPerWave >= 1, "a bf16 tile must give every wavefront a 1 KB piece");
-  int off[kPerWave];   // element offset of this lane's 16 bytes from tile row 0
-  __device__ __forceinline__ static void place(int i, int wave, int lane, int& row, int& chunk) {
-    const int byte = (wave * kPerWave + i) * 1024 + lane * 16;
-    row = byte / kRow;
-    chunk = ((byte % kRow) >> 4) ^ swz<kRow>(row);
-  }
-  __device__ __forceinline__ void init(int64_t st, int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < kPerWave; ++i) {
-      int row, chunk;
-      place(i, wave, lane, row, chunk);
-      off[i] = row * (int)st + chunk * 8;
-    }
-  }
-  __device__ __forceinline__ void issue(const PrefillArgs& a, const SeqView& sv, const bf16* base, int64_t st,
-                                        int64_t sh, int64_t pg, char FA_LDS* tile, int k0, bool fast, int wave,
-                                        int lane) {
-    if (fast) {
-      const bf16* tb = base + tile_base(a, sv, k0, st, sh, pg, PAGED);
-#pragma unroll
-      for (int i = 0; i < kPerWave; ++i) global_to_lds16(tb + off[i], tile + (wave * kPerWave + i) * 1024);
-    } else {
-#pragma unroll
-      for (int i = 0; i < kPerWave; ++i) {
-        int row, chunk;
-        place(i, wave, lane, row, chunk);
-        global_to_lds16(base + key_row_offset(a, sv, k0 + row, st, sh, pg, PAGED) + chunk * 8,
-                        tile + (wave * kPerWave + i) * 1024);
-      }
-    }
-  }
 };
 
 // FP8 V tile of D columns (head-major pages): 16-byte items loaded to
@@ -347,43 +297,6 @@ __device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
 __device__ __forceinline__ i32x8 cat8(i32x4 x, i32x4 y) {
   return i32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
 }
-
-// Active-tile bits of the block-mask rows that a workgroup spans (one per
-// 128-query half), 64 mask key-blocks at a time: one vector load and a ballot
-// per row and 64 blocks; the per-tile tests are scalar.  tile_bits(t) has bit
-// h set when half h has tile t active.
-struct MaskBits {
-  const uint8_t* row[kHalves];
-  int nkb, bk;
-  int chunk;
-  uint64_t bits[kHalves];
-  __device__ __forceinline__ void init(const PrefillArgs& a, const SeqView& sv, int q0) {
-    nkb = a.bm_nkb;
-    bk = a.bm_bk;
-    chunk = -1;
-#pragma unroll
-    for (int h = 0; h < kHalves; ++h) {
-      const int qh = min(q0 + h * kMaskRows, sv.sq - 1);   // halves past the end reuse the last row
-      row[h] = a.bmask ? a.bmask + (((int64_t)sv.b * a.Hq + sv.h) * a.bm_nqb + qh / a.bm_bq) * a.bm_nkb : nullptr;
-      bits[h] = ~0ull;
-    }
-  }
-  __device__ __forceinline__ unsigned tile_bits(int t) {
-    if (!row[0]) return (1u << kHalves) - 1;
-    const int kb = (t * BN) / bk;
-    const int c = kb >> 6;
-    if (c != chunk) {
-      const int idx = c * 64 + __lane_id();
-#pragma unroll
-      for (int h = 0; h < kHalves; ++h) bits[h] = __builtin_amdgcn_ballot_w64(idx < nkb && row[h][idx] != 0);
-      chunk = c;
-    }
-    unsigned r = 0;
-#pragma unroll
-    for (int h = 0; h < kHalves; ++h) r |= (unsigned)((bits[h] >> (kb & 63)) & 1ull) << h;
-    return r;
-  }
-};
 
 template <int DQK, int DV, bool FP8, bool PAGED, bool VEC, bool Q8, int MODS>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2)))
@@ -862,6 +775,9 @@ static hipError_t launch_prefill(const PrefillArgs& a, int n_bh, int n_qtiles, h
 hipError_t prefill_dispatch(const PrefillArgs& a, int dqk, int dv, bool fp8, bool paged, bool vec, int mods,
                             int n_bh, int n_qtiles, hipStream_t stream, bool* supported) {
   *supported = true;
+#ifndef FA_OLD_BF16
+  if (!fp8) return prefill_bf16_dispatch(a, dqk == dv ? dqk : -1, paged, mods, n_bh, n_qtiles, stream, supported);
+#endif
 #define FA_CASE(DQ, DVV, F8, PG, VC, MD)                                                       \
   if (dqk == DQ && dv == DVV && fp8 == F8 && paged == PG && vec == VC && mods == MD)           \
     return launch_prefill<DQ, DVV, F8, PG, VC, MD>(a, n_bh, n_qtiles, stream);

@@ -6,11 +6,47 @@
 
 namespace fa {
 
+constexpr int NWAVES = 4;
+constexpr int BM = 32 * NWAVES;
+constexpr int BN = 64;
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr int kMaskRows = 128;          // block-mask query tiles are multiples of this
+constexpr int kHalves = BM / kMaskRows; // mask rows one workgroup can span
+constexpr float kLazyTau = 8.0f;
+
 struct SeqView {
   int b, h, g;
   int sq, skv;            // lengths of this sequence
   int64_t qstart, kstart; // first token row (packed Q/O; contiguous K/V)
 };
+
+// Lengths and token offsets of the (sequence, q-head) that workgroup row bh
+// works on: dense batches (b*Sq, b*Skv), packed sequences (cu_seqlens) or a
+// paged cache (seqlen_k, bounded by the pages the block table can name).
+__device__ __forceinline__ void seq_view(const PrefillArgs& a, int bh, bool paged, SeqView& sv) {
+  sv.b = bh / a.Hq;
+  sv.h = bh % a.Hq;
+  sv.g = sv.h / a.group;
+  if (a.cu_q) {
+    const int s0 = a.cu_q[sv.b], s1 = a.cu_q[sv.b + 1];
+    sv.qstart = s0;
+    sv.sq = s1 - s0;
+  } else {
+    sv.qstart = (int64_t)sv.b * a.Sq;
+    sv.sq = a.Sq;
+  }
+  if (paged) {
+    sv.kstart = 0;
+    sv.skv = (int)min((int64_t)a.seqlen_k[sv.b], (int64_t)a.max_pages << a.page_shift);
+  } else if (a.cu_k) {
+    const int s0 = a.cu_k[sv.b], s1 = a.cu_k[sv.b + 1];
+    sv.kstart = s0;
+    sv.skv = s1 - s0;
+  } else {
+    sv.kstart = (int64_t)sv.b * a.Skv;
+    sv.skv = a.Skv;
+  }
+}
 
 // LDS row swizzle: 16-byte chunk c of tile row r is stored at c ^ swz(r).
 // The LDS behaves as 64 four-byte banks (256 bytes per conflict-free cycle).
@@ -106,5 +142,106 @@ __device__ __forceinline__ void wg_tile(bool causal, int& bh, int& qt) {
   bh = (p / gy) * 8 + (i & 7);
   qt = gy - 1 - p % gy;
 }
+
+// bf16 tile of D columns: global -> LDS with one 1 KB global_load_lds per
+// wave instruction.  Instruction n covers LDS bytes [n*1024, n*1024+1024);
+// lane l fills 16 bytes at n*1024 + 16*l, i.e. tile row r, stored chunk pos,
+// which holds source chunk pos ^ swz(r).
+template <int D, bool PAGED>
+struct Bf16Stager {
+  static constexpr int kRow = D * 2;
+  static constexpr int kPerWave = BN * kRow / 1024 / NWAVES;
+  static_assert(kPerWave >= 1, "a bf16 tile must give every wavefront a 1 KB piece");
+  unsigned off[kPerWave];   // byte offset of this lane's 16 bytes from tile row 0
+  __device__ __forceinline__ static void place(int i, int wave, int lane, int& row, int& chunk) {
+    const int byte = (wave * kPerWave + i) * 1024 + lane * 16;
+    row = byte / kRow;
+    chunk = ((byte % kRow) >> 4) ^ swz<kRow>(row);
+  }
+  __device__ __forceinline__ void init(int64_t st, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      int row, chunk;
+      place(i, wave, lane, row, chunk);
+      off[i] = (unsigned)(row * (int)st + chunk * 8) * 2u;
+    }
+  }
+  // Whole tiles and the sequence tail of contiguous K/V: buffer loads into
+  // LDS from a descriptor based at the tile's first row (32-bit per-lane
+  // offsets; the tail re-reads the last row).  Paged tails and pages smaller
+  // than a tile: per-row page lookups and 64-bit addresses.
+  __device__ __forceinline__ void issue(const PrefillArgs& a, const SeqView& sv, const bf16* base, int64_t st,
+                                        int64_t sh, int64_t pg, char FA_LDS* tile, int k0, bool fast, int wave,
+                                        int lane) {
+    if (fast || !PAGED) {
+      const bf16* tb = base + tile_base(a, sv, k0, st, sh, pg, PAGED);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(tb);
+      if (fast) {
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i) buffer_to_lds16(rs, off[i], tile + (wave * kPerWave + i) * 1024);
+      } else {
+        // the lane index goes through an opaque copy so that the per-row
+        // offsets are computed here, not kept live across the tile loop
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        const int last = sv.skv - 1 - k0;
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i) {
+          int row, chunk;
+          place(i, wave, l, row, chunk);
+          const unsigned o = (unsigned)(min(row, last) * (int)st + chunk * 8) * 2u;
+          buffer_to_lds16(rs, o, tile + (wave * kPerWave + i) * 1024);
+        }
+      }
+    } else {
+      int l = lane;
+      asm volatile("" : "+v"(l));
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i) {
+        int row, chunk;
+        place(i, wave, l, row, chunk);
+        global_to_lds16(base + key_row_offset(a, sv, k0 + row, st, sh, pg, PAGED) + chunk * 8,
+                        tile + (wave * kPerWave + i) * 1024);
+      }
+    }
+  }
+};
+
+// Active-tile bits of the block-mask rows that a workgroup spans (one per
+// 128-query half), 64 mask key-blocks at a time: one vector load and a ballot
+// per row and 64 blocks; the per-tile tests are scalar.  tile_bits(t) has bit
+// h set when half h has tile t active.
+struct MaskBits {
+  const uint8_t* row[kHalves];
+  int nkb, bk;
+  int chunk;
+  uint64_t bits[kHalves];
+  __device__ __forceinline__ void init(const PrefillArgs& a, const SeqView& sv, int q0) {
+    nkb = a.bm_nkb;
+    bk = a.bm_bk;
+    chunk = -1;
+#pragma unroll
+    for (int h = 0; h < kHalves; ++h) {
+      const int qh = min(q0 + h * kMaskRows, sv.sq - 1);   // halves past the end reuse the last row
+      row[h] = a.bmask ? a.bmask + (((int64_t)sv.b * a.Hq + sv.h) * a.bm_nqb + qh / a.bm_bq) * a.bm_nkb : nullptr;
+      bits[h] = ~0ull;
+    }
+  }
+  __device__ __forceinline__ unsigned tile_bits(int t) {
+    if (!row[0]) return (1u << kHalves) - 1;
+    const int kb = (t * BN) / bk;
+    const int c = kb >> 6;
+    if (c != chunk) {
+      const int idx = c * 64 + __lane_id();
+#pragma unroll
+      for (int h = 0; h < kHalves; ++h) bits[h] = __builtin_amdgcn_ballot_w64(idx < nkb && row[h][idx] != 0);
+      chunk = c;
+    }
+    unsigned r = 0;
+#pragma unroll
+    for (int h = 0; h < kHalves; ++h) r |= (unsigned)((bits[h] >> (kb & 63)) & 1ull) << h;
+    return r;
+  }
+};
 
 }  // namespace fa
