@@ -601,3 +601,100 @@ def test_backward_delta_is_rowsum_do_o():
     p = np.exp(s - s.max(axis=1, keepdims=True))
     p /= p.sum(axis=1, keepdims=True)
     assert np.allclose((p * (do @ v.T)).sum(axis=1), (do * o).sum(axis=1), atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- row samplers
+# varlen_rows / paged_rows give the expected rows of every full-size parity
+# test; they must equal the same rows of the full drivers above (which the
+# closed forms, brute force and library cases pin).  Picks are a seeded
+# shuffle of every (sequence, q-head, row) triple, so consecutive picks jump
+# between sequences and kv-head groups (paged_rows keeps one gathered
+# (sequence, kv-head) at a time and must refresh it on every change).  The
+# samplers compute each row alone, the drivers in blocks: agreement to fp64
+# rounding (1e-12) with identical -inf rows.
+def _all_picks(lq, Hq, seed):
+    picks = [(b, h, i) for b, n in enumerate(lq) for h in range(Hq) for i in range(n)]
+    order = np.random.default_rng(seed).permutation(len(picks))
+    return [picks[k] for k in order]
+
+
+def _check_rows(o_full, lse_full, cu_q, picks, o_r, l_r):
+    assert len(picks) > 0
+    for n, (b, h, i) in enumerate(picks):
+        t = int(cu_q[b]) + i
+        if np.isneginf(lse_full[h, t]):
+            assert np.isneginf(l_r[n]) and np.all(o_r[n] == 0.0), (b, h, i)
+        else:
+            assert abs(l_r[n] - lse_full[h, t]) <= 1e-12, (b, h, i, l_r[n], lse_full[h, t])
+            assert np.max(np.abs(o_r[n] - o_full[t, h])) <= 1e-12, (b, h, i)
+
+
+def _row_mods(case, B, Hq, nq, nk, seed):
+    if case == "causal":
+        return dict(causal=True)
+    if case == "noncausal":
+        return {}
+    if case == "window":
+        return dict(window=(7, 2))
+    if case == "causal_window":
+        return dict(causal=True, window=(5, -1))
+    if case == "alibi_softcap":
+        return dict(alibi_slope=0.3, softcap=5.0)
+    if case == "block_mask":
+        bm = synth.bernoulli_block_mask(B * Hq, -(-nq // 8), -(-nk // 8), 0.5, seed=seed).numpy()
+        return dict(block_mask=bm, mask_block=(8, 8), causal=True)
+    raise ValueError(case)
+
+
+@pytest.mark.parametrize("case", ["causal", "noncausal", "window", "causal_window", "alibi_softcap", "block_mask"])
+def test_varlen_rows_equal_the_full_driver(case):
+    """Cross lengths (Sq != Skv both ways), a zero-length sequence, GQA 6/2."""
+    lq, lk = [17, 0, 40, 5, 33], [25, 0, 40, 9, 20]
+    Hq, Hkv = 6, 2
+    d = synth.make_varlen(lq, lk, Hq, Hkv, 16, 8, seed=501)
+    mods = _row_mods(case, len(lq), Hq, max(lq), max(lk), seed=502)
+    q, k, v = _np(d["q"]), _np(d["k"]), _np(d["v"])
+    cu_q, cu_k = d["cu_q"].numpy(), d["cu_k"].numpy()
+    o, lse = oracle.attention_varlen(q, k, v, cu_q, cu_k, mods)
+    picks = _all_picks(lq, Hq, seed=503)
+    o_r, l_r = oracle.varlen_rows(q, k, v, cu_q, cu_k, picks, mods)
+    _check_rows(o, lse, cu_q, picks, o_r, l_r)
+
+
+@pytest.mark.parametrize("layout,kv,qdt", [("head_major", "fp8", "bf16"), ("head_major", "fp8", "fp8"),
+                                            ("vectorized", "fp8", "bf16"), ("vectorized", "fp8", "fp8"),
+                                            ("head_major", "bf16", "bf16")])
+@pytest.mark.parametrize("case", ["causal", "causal_window", "alibi_softcap", "block_mask"])
+def test_paged_rows_equal_the_full_driver(layout, kv, qdt, case):
+    """Both page layouts, E4M3 and bf16 caches, E4M3 and bf16 queries (E4M3
+    queries go with E4M3 caches), chunked-prefill lengths (Sq < Skv), GQA 4/2."""
+    lq, lk = [3, 40, 1, 17], [70, 40, 33, 17]
+    Hq, Hkv = 4, 2
+    d = synth.make_paged(lq, lk, Hq, Hkv, 64, 32, page_size=16, seed=511, extra_pages=3,
+                         kv_dtype=kv, q_dtype=qdt)
+    if layout == "vectorized":
+        d = synth.to_vectorized(d)
+    mods = _row_mods(case, len(lq), Hq, max(lq), max(lk), seed=512)
+    qd = float(d["q_descale"]) if qdt == "fp8" else None
+    args = (f64(d["q"]), f64(d["k_cache"]), f64(d["v_cache"]), d["cu_q"].numpy(), d["seqlen_k"].numpy(),
+            d["block_table"].numpy())
+    kd, vd = float(d["k_descale"]), float(d["v_descale"])
+    o, lse = oracle.attention_paged(*args, mods, kd, vd, layout=layout, q_descale=qd)
+    assert not np.isnan(o).any()
+    picks = _all_picks(lq, Hq, seed=513)
+    o_r, l_r = oracle.paged_rows(*args, picks, mods, kd, vd, layout=layout, q_descale=qd)
+    _check_rows(o, lse, d["cu_q"].numpy(), picks, o_r, l_r)
+
+
+def test_row_samplers_catch_a_wrong_row():
+    """The comparison above is sharp: sampling row i+1 in place of row i, or
+    the neighbouring q-head, is far outside the 1e-12 agreement."""
+    lq = [12, 20]
+    d = synth.make_varlen(lq, lq, 4, 2, 16, 8, seed=521)
+    q, k, v = _np(d["q"]), _np(d["k"]), _np(d["v"])
+    cu = d["cu_q"].numpy()
+    o, lse = oracle.attention_varlen(q, k, v, cu, cu, dict(causal=True))
+    for shifted in ([(1, 3, 5)], [(1, 2, 6)]):
+        o_r, l_r = oracle.varlen_rows(q, k, v, cu, cu, shifted, dict(causal=True))
+        with pytest.raises(AssertionError):
+            _check_rows(o, lse, cu, [(1, 3, 6)], o_r, l_r)
