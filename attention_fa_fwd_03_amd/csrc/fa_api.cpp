@@ -372,9 +372,9 @@ int paged_impl(const fa_paged_opts* opts, const void* q, const void* k_cache, co
                 (long long)(max_pages_per_seq * page_size), (long long)max_seqlen_k);
   Mods m;
   if ((rc = read_mods(mods, d_qk, max_seqlen_q, max_seqlen_k, &m))) return rc;
-  if (m.flags & (FA_ALIBI | FA_SOFTCAP | FA_BLOCK_MASK))
-    return fail(FA_ERR_UNSUPPORTED, "paged caches support FA_CAUSAL and FA_WINDOW only");
   const bool fp8 = kv_dtype == FA_FP8_E4M3;
+  if (fp8 && (m.flags & (FA_ALIBI | FA_SOFTCAP | FA_BLOCK_MASK)))
+    return fail(FA_ERR_UNSUPPORTED, "FP8 paged caches support FA_CAUSAL and FA_WINDOW only");
   const bool decode = uses_decode(max_seqlen_q, Hq, Hkv, d_qk, d_v, kv_dtype, page_size);
   if (!decode && !prefill_dims_built(d_qk, d_v, fp8, true))
     return fail(FA_ERR_UNSUPPORTED, "paged head dims (%lld, %lld) with kv_dtype %d not built", (long long)d_qk,
@@ -404,8 +404,17 @@ int paged_impl(const fa_paged_opts* opts, const void* q, const void* k_cache, co
     const size_t need = workspace_bytes(B, total_q, max_seqlen_q, max_seqlen_k, Hq, Hkv, d_qk, d_v, kv_dtype, page_size);
     if (!workspace || workspace_bytes_in < need)
       return fail(FA_ERR_WORKSPACE, "decode path needs a workspace of %zu bytes (got %zu)", need, workspace_bytes_in);
+    // the plan kernel writes the workspace while the same call reads the
+    // metadata, the caches and the descales: it may overlap none of them
     if (overlaps(workspace, need, o, no) || overlaps(workspace, need, lse, nl) || overlaps(workspace, need, q, nq))
       return fail(FA_ERR_INVALID, "workspace must not overlap q, o or lse");
+    if (overlaps(workspace, need, cu_seqlens_q, (size_t)(B + 1) * 4) || overlaps(workspace, need, seqlen_k, (size_t)B * 4) ||
+        overlaps(workspace, need, block_table, (size_t)(B * max_pages_per_seq) * 4))
+      return fail(FA_ERR_INVALID, "workspace must not overlap cu_seqlens_q, seqlen_k or block_table");
+    if (overlaps(workspace, need, k_cache, nk) || overlaps(workspace, need, v_cache, nv) ||
+        overlaps(workspace, need, k_descale, 4) || overlaps(workspace, need, v_descale, 4) ||
+        (q8 && overlaps(workspace, need, opts->q_descale, 4)))
+      return fail(FA_ERR_INVALID, "workspace must not overlap the caches or the descales");
     if (B * Hkv * ((max_seqlen_k + 31) / 32) >= kI32) return fail(FA_ERR_LIMIT, "decode tile count exceeds 2^31");
     const DecodeLayout L = decode_layout(B, max_seqlen_q, max_seqlen_k, Hq, Hkv, d_v,
                                          std::min<int64_t>(max_pages_per_seq * page_size, kI32 - 1), vec);
@@ -489,7 +498,7 @@ int paged_impl(const fa_paged_opts* opts, const void* q, const void* k_cache, co
   a.page_shift = shift;
   a.num_pages = (int)num_pages;
   fill_mods(a, m);
-  return launch_prefill(a, d_qk, d_v, fp8, true, vec, 0, B, Hq, max_seqlen_q, st);
+  return launch_prefill(a, d_qk, d_v, fp8, true, vec, fp8 ? 0 : mod_bits(m), B, Hq, max_seqlen_q, st);
 }
 
 }  // namespace

@@ -222,8 +222,9 @@ void fa_decode_kernel(const DecodeArgs a) {
   const int krow = lane & 15, kx = VEC ? 0 : dec_kswz(krow);
   const char FA_LDS* krd = klds + (VEC ? krow * 16 : krow * DQK) + (kgrp & 1) * 8;
   const float kdesc = *a.k_descale, vdesc = *a.v_descale;
-  // bf16 Q enters scaled by 16 (split below); E4M3 Q enters as it is, with its descale
-  const float C = Q8 ? a.qk_scale * kLog2e * kdesc * *a.q_descale : a.qk_scale * kLog2e * kdesc * (1.0f / 16.0f);
+  // E4M3 Q enters as it is, with its descale; bf16 Q scaled per row by the
+  // power of two of its split (folded into that row's constant below)
+  const float C0 = Q8 ? a.qk_scale * kLog2e * kdesc * *a.q_descale : a.qk_scale * kLog2e * kdesc;
   const int pmask = (1 << a.page_shift) - 1;
 
   // One unit segment: sequence b, kv-head g, tiles [t0, t1) -> partial slot.
@@ -355,20 +356,40 @@ void fa_decode_kernel(const DecodeArgs a) {
     // the first tile is requested, so waiting for them never waits for the
     // cache loads
     i32x2 qhi[NRB][kSteps], qlo[NRB][kSteps];
+    float C[NRB];        // per row block: raw dot product -> log2-domain scaled logit
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const int64_t qoff = tok[rb] * a.q_st + (int64_t)hq[rb] * a.q_sh + kgrp * 8;
+      C[rb] = C0;
+      if (Q8) {
 #pragma unroll
-      for (int st = 0; st < kSteps; ++st) {
-        if (Q8) {
+        for (int st = 0; st < kSteps; ++st) {
           // E4M3 queries are the B operand as they are (one product per step)
           i32x2 x = *reinterpret_cast<const i32x2*>(reinterpret_cast<const uint8_t*>(a.q) + qoff + 32 * st);
           qhi[rb][st] = rvalid[rb] ? x : i32x2{};
           qlo[rb][st] = i32x2{};
-        } else {
-          bf16x8 x = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(a.q) + qoff + 32 * st);
+        }
+      } else {
+        // the row's power-of-two split scale from its largest magnitude (its
+        // dims are spread over the four lanes with this lane % 16)
+        const bf16* qp = reinterpret_cast<const bf16*>(a.q) + qoff;
+        float amax = 0.0f;
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) {
+          bf16x8 x = *reinterpret_cast<const bf16x8*>(qp + 32 * st);
           if (!rvalid[rb]) x = bf16x8{};
-          split_e4m3(x, qhi[rb][st], qlo[rb][st]);
+          amax = amax8(x, amax);
+        }
+        float qinv;
+        const float qscale = split_scale(max_quad16(amax), &qinv);
+        C[rb] = C0 * qinv;
+        // read the row again (cached) rather than keep it in registers
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) {
+          bf16x8 x = *reinterpret_cast<const bf16x8*>(qp + 32 * st);
+          if (!rvalid[rb]) x = bf16x8{};
+          split_e4m3(x, qscale, qhi[rb][st], qlo[rb][st]);
         }
       }
     }
@@ -458,7 +479,7 @@ void fa_decode_kernel(const DecodeArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[rb][kh][i]);
         mx = max_quad16(mx);
-        const float m_new = fmaxf(m_run[rb], mx * C);
+        const float m_new = fmaxf(m_run[rb], mx * C[rb]);
         if (__builtin_amdgcn_ballot_w64(m_new > m_run[rb] + 8.0f) != 0) {
           const float alpha = exp2_hw(m_run[rb] - m_new);
           m_run[rb] = m_new;
@@ -470,7 +491,7 @@ void fa_decode_kernel(const DecodeArgs a) {
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float p = exp2_hw(fmaf(sacc[rb][kh][i], C, -m_run[rb]));
+            const float p = exp2_hw(fmaf(sacc[rb][kh][i], C[rb], -m_run[rb]));
             l_run[rb] += p;
             pf[rb][kh * 4 + i] = (bf16)p;
           }

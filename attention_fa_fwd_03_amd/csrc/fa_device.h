@@ -125,14 +125,29 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(i32x2 w) {
   return r;
 }
 
-// Eight bf16 values x -> E4M3 parts (hi, lo) of 16 x, with 16 x ~= hi + lo:
-// the two 3-bit mantissas carry x to about 2^-8 relative, the factor 16 keeps
-// N(0,1)-scale values clear of the E4M3 subnormal range, and each part times
-// an E4M3 operand is exact in an FP8 product.
-__device__ __forceinline__ void split_e4m3(bf16x8 x, i32x2& hi, i32x2& lo) {
+// Power-of-two scale for the E4M3 split of one query row whose largest
+// magnitude is amax: returns 2^e with amax * 2^e in [128, 256), so every
+// scaled value stays below the E4M3 maximum (448) and the row's large values
+// keep both parts in the normal range; *inv = 2^-e.  e is clamped to
+// [-126, 126]; an all-zero row takes e = 0.
+__device__ __forceinline__ float split_scale(float amax, float* inv) {
+  int E;
+  (void)frexpf(amax, &E);            // amax = m 2^E, m in [0.5, 1)
+  int e = amax > 0.0f ? 8 - E : 0;
+  e = min(max(e, -126), 126);
+  *inv = ldexpf(1.0f, -e);
+  return ldexpf(1.0f, e);
+}
+
+// Eight bf16 values x -> E4M3 parts (hi, lo) of scale * x, with
+// scale * x ~= hi + lo: the two 3-bit mantissas carry each value to about
+// 2^-8 relative (values far below the row's maximum to about 2^-17 of that
+// maximum, absolute), and each part times an E4M3 operand is exact in an
+// FP8 product.  scale comes from split_scale of the row's maximum.
+__device__ __forceinline__ void split_e4m3(bf16x8 x, float scale, i32x2& hi, i32x2& lo) {
   float f[8], r[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = 16.0f * (float)x[e];
+  for (int e = 0; e < 8; ++e) f[e] = scale * (float)x[e];
   int h0 = 0, h1 = 0, l0 = 0, l1 = 0;
   h0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], h0, false);
   h0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], h0, true);
@@ -152,6 +167,12 @@ __device__ __forceinline__ void split_e4m3(bf16x8 x, i32x2& hi, i32x2& lo) {
   l1 = __builtin_amdgcn_cvt_pk_fp8_f32(r[6], r[7], l1, true);
   hi = i32x2{h0, h1};
   lo = i32x2{l0, l1};
+}
+
+__device__ __forceinline__ float amax8(bf16x8 x, float m) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)x[e]));
+  return m;
 }
 
 // 16 OCP E4M3 bytes -> 16 bf16 (exact).

@@ -375,6 +375,7 @@ void fa_prefill_kernel(const PrefillArgs a) {
   constexpr int kQ8 = FP8 ? DQK / 64 : 1;
   bf16x8 qf[kQf];
   i32x8 qhi[kQ8], qlo[kQ8];
+  float qinv = 1.0f;   // bf16 queries split into E4M3 parts: 2^-e of this row's split scale
   const int64_t qrow_off = (sv.qstart + (qvalid ? qrow : 0)) * a.q_st + (int64_t)sv.h * a.q_sh;
   if (FP8) {
     if (Q8) {
@@ -387,16 +388,26 @@ void fa_prefill_kernel(const PrefillArgs a) {
         qlo[s] = i32x8{};
       }
     } else {
+      // the row's power-of-two split scale from its largest magnitude (the
+      // row's other half sits in lane l ^ 32)
       const bf16* qp = reinterpret_cast<const bf16*>(a.q) + qrow_off + (lane >> 5) * 32;
+      bf16x8 qv[kQ8][4];
+      float amax = 0.0f;
 #pragma unroll
-      for (int s = 0; s < kQ8; ++s) {
-        i32x2 h[4], l[4];
+      for (int s = 0; s < kQ8; ++s)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + s * 64 + u * 8);
           if (!qvalid) v = bf16x8{};
-          split_e4m3(v, h[u], l[u]);
+          qv[s][u] = v;
+          amax = amax8(v, amax);
         }
+      const float qscale = split_scale(max_pair32(amax), &qinv);
+#pragma unroll
+      for (int s = 0; s < kQ8; ++s) {
+        i32x2 h[4], l[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) split_e4m3(qv[s][u], qscale, h[u], l[u]);
         qhi[s] = i32x8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
         qlo[s] = i32x8{l[0][0], l[0][1], l[1][0], l[1][1], l[2][0], l[2][1], l[3][0], l[3][1]};
       }
@@ -425,7 +436,7 @@ void fa_prefill_kernel(const PrefillArgs a) {
     kdesc = *a.k_descale;
     vdesc = *a.v_descale;
     if (Q8) kdesc *= *a.q_descale;       // both descales scale every logit
-    else kdesc *= 0.0625f;               // the split carries 16 q
+    else kdesc *= qinv;                  // the split carries 2^e q
   }
   // C: multiplier from the raw MFMA dot product to log2-domain scaled logits
   const float C = ANYMOD ? 1.0f : a.qk_scale * kLog2e * kdesc;
@@ -768,33 +779,22 @@ static hipError_t launch_prefill(const PrefillArgs& a, int n_bh, int n_qtiles, h
   return hipGetLastError();
 }
 
-// Instantiated shapes: (D_qk, D_v) in {(64,64), (128,128)} for bf16 K/V
-// (dense, varlen, paged) with every score-mod combination; (192,128) and
-// (128,128) and (192,192) for FP8 E4M3 paged caches without score mods,
-// head-major or vectorised pages.
+// Instantiated shapes here: (192,128), (128,128) and (192,192) for FP8 E4M3
+// paged caches without score mods, head-major or vectorised pages.  bf16 K/V
+// go to the software-pipelined kernel (fa_prefill_bf16.hip).
 hipError_t prefill_dispatch(const PrefillArgs& a, int dqk, int dv, bool fp8, bool paged, bool vec, int mods,
                             int n_bh, int n_qtiles, hipStream_t stream, bool* supported) {
   *supported = true;
-#ifndef FA_OLD_BF16
   if (!fp8) return prefill_bf16_dispatch(a, dqk == dv ? dqk : -1, paged, mods, n_bh, n_qtiles, stream, supported);
-#endif
 #define FA_CASE(DQ, DVV, F8, PG, VC, MD)                                                       \
   if (dqk == DQ && dv == DVV && fp8 == F8 && paged == PG && vec == VC && mods == MD)           \
     return launch_prefill<DQ, DVV, F8, PG, VC, MD>(a, n_bh, n_qtiles, stream);
-#define FA_MODS4(DQ, DVV, F8, PG)                                                          \
-  FA_CASE(DQ, DVV, F8, PG, false, 0) FA_CASE(DQ, DVV, F8, PG, false, 1)                    \
-  FA_CASE(DQ, DVV, F8, PG, false, 2) FA_CASE(DQ, DVV, F8, PG, false, 3)
-  FA_MODS4(64, 64, false, false)
-  FA_MODS4(128, 128, false, false)
-  FA_CASE(128, 128, false, true, false, 0)
-  FA_CASE(64, 64, false, true, false, 0)
   FA_CASE(192, 128, true, true, false, 0)
   FA_CASE(128, 128, true, true, false, 0)
   FA_CASE(192, 128, true, true, true, 0)
   FA_CASE(128, 128, true, true, true, 0)
   FA_CASE(192, 192, true, true, false, 0)
   FA_CASE(192, 192, true, true, true, 0)
-#undef FA_MODS4
 #undef FA_CASE
   *supported = false;
   return hipSuccess;

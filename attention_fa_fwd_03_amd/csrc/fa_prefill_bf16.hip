@@ -415,7 +415,7 @@ static hipError_t launch_bf16(const PrefillArgs& a, int n_bh, int n_qtiles, hipS
 }
 
 // bf16 K/V: head dims 64 and 128 (D_qk = D_v), contiguous (dense, varlen)
-// with every score-mod combination, or bf16 pages without mods.
+// or in bf16 pages, with every score-mod combination.
 hipError_t prefill_bf16_dispatch(const PrefillArgs& a, int d, bool paged, int mods, int n_bh, int n_qtiles,
                                  hipStream_t stream, bool* supported) {
   *supported = true;
@@ -423,7 +423,8 @@ hipError_t prefill_bf16_dispatch(const PrefillArgs& a, int d, bool paged, int mo
   if (d == DD && paged == PG && mods == MD) return launch_bf16<DD, PG, MD>(a, n_bh, n_qtiles, stream);
   FA_CASE(64, false, 0) FA_CASE(64, false, 1) FA_CASE(64, false, 2) FA_CASE(64, false, 3)
   FA_CASE(128, false, 0) FA_CASE(128, false, 1) FA_CASE(128, false, 2) FA_CASE(128, false, 3)
-  FA_CASE(64, true, 0) FA_CASE(128, true, 0)
+  FA_CASE(64, true, 0) FA_CASE(64, true, 1) FA_CASE(64, true, 2) FA_CASE(64, true, 3)
+  FA_CASE(128, true, 0) FA_CASE(128, true, 1) FA_CASE(128, true, 2) FA_CASE(128, true, 3)
 #undef FA_CASE
   *supported = false;
   return hipSuccess;

@@ -127,12 +127,18 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  * page_size: a power of two in [1, 1024].
  * Built: FP8 (d_qk, d_v) in {(192, 128), (128, 128), (192, 192)} (192/192:
  * the V192 variant of the paged FP8 PR); bf16 (64, 64), (128, 128).
- * Mods: FA_CAUSAL and FA_WINDOW only.
+ * Mods: FP8 caches take FA_CAUSAL and FA_WINDOW (others: FA_ERR_UNSUPPORTED);
+ * bf16 caches take every mod, as for fa_fwd_dense.
+ * bf16 queries against an FP8 cache enter the FP8 products as two E4M3
+ * parts of 2^e q, e chosen per query row from its largest magnitude
+ * (2^e amax in [128, 256)): any finite bf16 query row is representable, each
+ * element to about 2^-8 of itself or 2^-17 of the row's maximum.
  * When max_seqlen_q * (Hq / Hkv) <= 32 (decode) and kv_dtype is FP8, the
  * keys are split and partial results merged; that path needs a device
  * workspace of fa_fwd_paged_workspace_size(...) bytes (else
- * FA_ERR_WORKSPACE).
- * The workspace is scratch, overwritten by the call.
+ * FA_ERR_WORKSPACE).  The workspace is scratch, overwritten by the call; it
+ * may overlap no argument array (q, caches, o, lse, cu_seqlens_q, seqlen_k,
+ * block_table, descales: FA_ERR_INVALID).
  */
 int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                  const int32_t* cu_seqlens_q, const int32_t* seqlen_k, const int32_t* block_table,

@@ -187,6 +187,16 @@ def test_paged_ex_rejects(opt_kw, kw, code, frag):
     assert rc == code and frag in msg, (rc, msg)
 
 
+@pytest.mark.parametrize("target", ["q", "o", "lse", "cu", "sk", "bt", "kc", "vc", "kd", "vd"])
+def test_paged_decode_workspace_must_not_overlap(target):
+    """The decode path's plan kernel writes the workspace while the call
+    reads the metadata, the caches and the descales and writes O and LSE."""
+    base = dict(q=FAKE, kc=FAKE * 2, vc=FAKE * 3, o=FAKE * 4, lse=FAKE * 5, cu=FAKE * 6, sk=FAKE * 7, bt=FAKE * 8,
+                kd=FAKE * 9, vd=FAKE * 10)
+    rc, msg = _paged(ws=base[target])
+    assert rc == -1 and "overlap" in msg, (target, rc, msg)
+
+
 def test_paged_rejects_unsupported_mods():
     fa = _lib()
     m = fa.Mods(alibi_slope=0.5).to_c()

@@ -1,0 +1,137 @@
+"""GPU parity of exported paths beyond the main parity file: bf16 page caches
+(prefill, chunked prefill and single-query rows, page sizes 1 to 64, with
+and without score mods), score mods at D = 64, windows on the FP8 paged
+prefill, and bf16 queries far from unit scale against FP8 caches (the
+per-row power-of-two split of the queries).  Every call goes through the C
+ABI; every result is compared with the fp64 oracle on the same inputs.
+"""
+import math
+
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.helpers import TOL_O_BF16, TOL_O_FP8, compare, f64
+from tests.test_gpu_parity import (FLEX_CASES, _dense_run, _oracle_mods, _paged_ref, _paged_run, _paged_vec_run,
+                                   _varlen_run)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _cmp_packed(o, lse, o_ref, l_ref, tol, what):
+    compare(o.permute(1, 0, 2), lse, o_ref.transpose(1, 0, 2), l_ref, tol, what=what)
+
+
+# ----------------------------------------------------------------------------- bf16 pages
+BF16_PAGED_LQ = {"prefill": [70, 3, 128, 129, 300], "chunked": [40, 3, 1, 64, 100], "decode": [1, 1, 1, 1, 1]}
+
+
+@pytest.mark.parametrize("case", sorted(BF16_PAGED_LQ))
+@pytest.mark.parametrize("ps", [1, 16, 64])
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_paged_matches_oracle(D, ps, case):
+    """bf16 caches in head-major pages (NaN in unused pages and past
+    seqlen_k), GQA 4/2, causal."""
+    lk = [70, 3, 128, 129, 300]
+    d = synth.make_paged(BF16_PAGED_LQ[case], lk, 4, 2, D, D, page_size=ps, seed=601 + D + ps, kv_dtype="bf16",
+                         extra_pages=3)
+    o, lse = _paged_run(d, dict(causal=True), D)
+    o_ref, l_ref = _paged_ref(d, dict(causal=True))
+    _cmp_packed(o, lse, o_ref, l_ref, TOL_O_BF16, f"bf16 paged D{D} ps{ps} {case}")
+
+
+@pytest.mark.parametrize("case", ["alibi", "softcap", "window_sym", "alibi_softcap_causal", "block_mask"])
+def test_bf16_paged_mods(case):
+    """Score mods and a block mask on bf16 pages (pages of 16, chunked rows)."""
+    lq, lk = [300, 40, 200], [300, 64, 500]
+    B, Hq = len(lq), 4
+    d = synth.make_paged(lq, lk, Hq, 4, 128, 128, page_size=16, seed=611, kv_dtype="bf16", extra_pages=2)
+    if case == "block_mask":
+        bm = synth.bernoulli_block_mask(B * Hq, math.ceil(max(lq) / 128), math.ceil(max(lk) / 128), 0.5, seed=612)
+        bm[1, 0, :] = 0    # a fully masked query block
+        mods = dict(block_mask=bm.to(DEV), mask_block=(128, 128))
+    else:
+        mods = dict(FLEX_CASES[case])
+    o, lse = _paged_run(d, mods, 128)
+    o_ref, l_ref = _paged_ref(d, _oracle_mods(mods))
+    _cmp_packed(o, lse, o_ref, l_ref, TOL_O_BF16, f"bf16 paged {case}")
+
+
+# ----------------------------------------------------------------------------- mods at D = 64
+@pytest.mark.parametrize("case", sorted(FLEX_CASES))
+@pytest.mark.parametrize("layout", ["dense", "varlen"])
+def test_flex_mods_d64(case, layout):
+    mods = FLEX_CASES[case]
+    if layout == "dense":
+        d = synth.make_dense(2, 300, 300, 2, 2, 64, 64, seed=621)
+        o, lse = _dense_run(d, mods, 64)
+        o_ref, l_ref = oracle.attention_dense(f64(d["q"]), f64(d["k"]), f64(d["v"]), dict(mods))
+        compare(o.permute(0, 2, 1, 3), lse, o_ref.transpose(0, 2, 1, 3), l_ref, TOL_O_BF16, what=f"d64 {case}")
+    else:
+        lq, lk = [5, 0, 130, 64, 300], [40, 0, 130, 64, 333]
+        d = synth.make_varlen(lq, lk, 4, 2, 64, 64, seed=622)
+        o, lse = _varlen_run(d, mods, 64)
+        o_ref, l_ref = oracle.attention_varlen(f64(d["q"]), f64(d["k"]), f64(d["v"]), d["cu_q"], d["cu_k"],
+                                               dict(mods))
+        _cmp_packed(o, lse, o_ref, l_ref, TOL_O_BF16, f"d64 varlen {case}")
+
+
+def test_flex_block_mask_d64():
+    B, H, S = 2, 2, 640
+    nb = math.ceil(S / 128)
+    bm = synth.bernoulli_block_mask(B * H, nb, nb, 0.5, seed=631)
+    d = synth.make_dense(B, S, S, H, H, 64, 64, seed=632)
+    mods = dict(block_mask=bm.to(DEV), mask_block=(128, 128), causal=True)
+    o, lse = _dense_run(d, mods, 64)
+    o_ref, l_ref = oracle.attention_dense(f64(d["q"]), f64(d["k"]), f64(d["v"]), _oracle_mods(mods))
+    compare(o.permute(0, 2, 1, 3), lse, o_ref.transpose(0, 2, 1, 3), l_ref, TOL_O_BF16, what="d64 block mask")
+
+
+# ----------------------------------------------------------------------------- FP8 paged prefill windows
+@pytest.mark.parametrize("window", [(100, 0), (50, 3), (0, 0)])
+@pytest.mark.parametrize("vec", [False, True])
+def test_paged_fp8_prefill_window(window, vec):
+    """Sliding windows on the FP8 paged prefill (rows enough for the prefill
+    kernel), both page formats, D 192/128."""
+    lq, lk = [300, 40, 200], [300, 64, 700]
+    d = synth.make_paged(lq, lk, 4, 4, 192, 128, page_size=64, seed=641, extra_pages=2)
+    mods = dict(causal=True, window=window)
+    o, lse = _paged_vec_run(d, mods, 128) if vec else _paged_run(d, mods, 128)
+    o_ref, l_ref = _paged_ref(d, mods)
+    _cmp_packed(o, lse, o_ref, l_ref, TOL_O_FP8, f"fp8 window {window} vec={vec}")
+
+
+# ----------------------------------------------------------------------------- query range
+def _scaled_queries(d, how):
+    """bf16 queries far from N(0,1) and the softmax scale that keeps the
+    logits where they were: every element times 40 or 1e-3, or one element
+    per row times 200 (a row whose maximum dwarfs the rest)."""
+    q = d["q"].float()
+    base = 1.0 / math.sqrt(q.shape[-1])
+    if how == "mixed":
+        q[..., 7] *= 200.0
+        return q.to(torch.bfloat16), base / 20.0
+    return (q * how).to(torch.bfloat16), base / how
+
+
+@pytest.mark.parametrize("how", [40.0, 1e-3, "mixed"])
+@pytest.mark.parametrize("vec", [False, True])
+@pytest.mark.parametrize("path", ["prefill", "decode"])
+def test_fp8_cache_bf16_query_range(path, vec, how):
+    """The E4M3 split of bf16 queries takes a power-of-two scale per row, so
+    queries whose magnitudes would overflow (x40: |16 q| > 448) or sink into
+    E4M3 subnormals (x1e-3) with a fixed scale stay within the FP8
+    tolerance, on the paged prefill and on the decode."""
+    if path == "prefill":
+        lq, lk, Hq, Hkv = [200, 77], [200, 300], 4, 4
+    else:
+        lq, lk, Hq, Hkv = [1, 1, 1], [300, 64, 700], 8, 2
+    d = synth.make_paged(lq, lk, Hq, Hkv, 192, 128, page_size=64, seed=651, extra_pages=2)
+    d["q"], scale = _scaled_queries(d, how)
+    mods = dict(causal=True, scale=scale)
+    o, lse = _paged_vec_run(d, mods, 128) if vec else _paged_run(d, mods, 128)
+    o_ref, l_ref = _paged_ref(d, mods)
+    _cmp_packed(o, lse, o_ref, l_ref, TOL_O_FP8, f"query range {how} {path} vec={vec}")
