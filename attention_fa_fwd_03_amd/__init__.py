@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     fa_fwd_dense,
     fa_fwd_varlen,
     fa_fwd_paged,
+    fa_fwd_paged_noalloc,
     fa_fwd_paged_vec,
     FA_PAGES_HEAD_MAJOR,
     FA_PAGES_VECTORIZED,

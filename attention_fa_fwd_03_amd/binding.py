@@ -64,6 +64,9 @@ lib.fa_fwd_varlen.restype = ctypes.c_int
 lib.fa_fwd_paged.argtypes = ([_vp] * 8 + [_i64] * 11 + [ctypes.c_int, _vp, _vp, _vp, _sz,
                                                          ctypes.POINTER(_FaMods), _vp])
 lib.fa_fwd_paged.restype = ctypes.c_int
+lib.fa_fwd_paged_noalloc.argtypes = ([_vp] * 8 + [_i64] * 11 + [ctypes.c_int, _vp, _vp, ctypes.POINTER(_FaMods),
+                                                                 _vp])
+lib.fa_fwd_paged_noalloc.restype = ctypes.c_int
 lib.fa_fwd_paged_vec.argtypes = lib.fa_fwd_paged.argtypes
 lib.fa_fwd_paged_vec.restype = ctypes.c_int
 lib.fa_fwd_paged_ex.argtypes = ([_vp] * 8 + [_i64] * 11 + [ctypes.c_int, _vp, _vp, _vp, _sz,
@@ -219,6 +222,38 @@ def fa_fwd_paged(q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_tabl
     _paged_call(FA_PAGES_HEAD_MAJOR, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table,
                 max_seqlen_q, max_seqlen_k, P, Hkv, ps, Dqk, Dv, fp8, k_descale, v_descale, workspace, mods, stream,
                 q_descale)
+
+
+def fa_fwd_paged_noalloc(q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, max_seqlen_q,
+                         max_seqlen_k, k_descale=None, v_descale=None, mods=None, stream=None):
+    """fa_fwd_paged without a workspace (see include/fa.h): bf16 queries,
+    head-major pages; the decode path's scratch is the library's static
+    device array."""
+    P, Hkv, ps, Dqk = k_cache.shape
+    Dv = v_cache.shape[3]
+    fp8 = k_cache.dtype == torch.uint8
+    cdt = torch.uint8 if fp8 else torch.bfloat16
+    _need(k_cache, "k_cache", cdt, (P, Hkv, ps, Dqk))
+    _need(v_cache, "v_cache", cdt, (P, Hkv, ps, Dv))
+    Tq, Hq = q.shape[0], q.shape[1]
+    B = cu_seqlens_q.shape[0] - 1
+    _need(q, "q", torch.bfloat16, (Tq, Hq, Dqk))
+    _need(o, "o", torch.bfloat16, (Tq, Hq, Dv))
+    _need(lse, "lse", torch.float32, (Hq, Tq))
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, (B + 1,))
+    _need(seqlen_k, "seqlen_k", torch.int32, (B,))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [B, max_pages], got {tuple(block_table.shape)}")
+    if fp8:
+        _need(k_descale, "k_descale", torch.float32)
+        _need(v_descale, "v_descale", torch.float32)
+    _check(lib.fa_fwd_paged_noalloc(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), lse.data_ptr(),
+        cu_seqlens_q.data_ptr(), seqlen_k.data_ptr(), block_table.data_ptr(),
+        B, Tq, int(max_seqlen_q), int(max_seqlen_k), P, ps, block_table.shape[1], Hq, Hkv, Dqk, Dv,
+        FA_FP8_E4M3 if fp8 else FA_BF16, k_descale.data_ptr() if fp8 else None,
+        v_descale.data_ptr() if fp8 else None, _mods(mods), _stream(stream, q.device)))
 
 
 def fa_fwd_paged_vec(q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, max_seqlen_q,

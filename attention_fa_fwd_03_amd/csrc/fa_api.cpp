@@ -4,7 +4,8 @@
 // enqueues nothing (and the checks can be exercised without a GPU).  Nothing
 // in this file allocates memory, synchronises, or copies between host and
 // device: all metadata is consumed on the device, with the host-side maxima
-// passed by the caller.
+// passed by the caller.  The one static device array (the decode scratch of
+// fa_fwd_paged_noalloc) is part of the code object, not an allocation.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -14,6 +15,7 @@
 #include <cstdio>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 
 #include "fa.h"
@@ -39,6 +41,9 @@ constexpr int kMaskBQ = 128;       // block-mask query tiles: multiples of a wor
 constexpr int kBN = 64;            // prefill keys per tile
 constexpr int kKvLdsBytes = 24576;  // KV-cache writer: LDS for 16 tokens' codes per workgroup
 constexpr int kDecodeRows = 32;    // decode rows (query x q-head-in-group) per wavefront
+
+// Decode scratch of fa_fwd_paged_noalloc (see below): at most this many bytes.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   if (!a || !b || na == 0 || nb == 0) return false;
@@ -330,7 +335,36 @@ size_t fa_fwd_paged_workspace_size(int64_t B, int64_t total_q, int64_t max_seqle
 
 }  // extern "C"
 
+// Decode scratch of fa_fwd_paged_noalloc: the tile prefix and the split-KV
+// partials of one call, in a static device array (each GPU that runs the
+// library holds its own copy until the process ends).  Host code never uses
+// the array's name as an address: its device address is looked up once per
+// device with hipGetSymbolAddress and kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on its first use).
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_LIMIT, "device %d beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(FA_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
 
 // The paged entry points.
 int paged_impl(const fa_paged_opts* opts, const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
@@ -340,7 +374,7 @@ int paged_impl(const fa_paged_opts* opts, const void* q, const void* k_cache, co
                int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v, fa_dtype kv_dtype,
                const float* k_descale, const float* v_descale,
                void* workspace, size_t workspace_bytes_in,
-               const fa_mods* mods, void* stream) {
+               const fa_mods* mods, void* stream, bool use_scratch = false) {
   g_err.clear();
   int rc = check_common(B, Hq, Hkv, d_qk, d_v);
   if (rc) return rc;
@@ -402,22 +436,32 @@ int paged_impl(const fa_paged_opts* opts, const void* q, const void* k_cache, co
 
   if (decode) {
     const size_t need = workspace_bytes(B, total_q, max_seqlen_q, max_seqlen_k, Hq, Hkv, d_qk, d_v, kv_dtype, page_size);
-    if (!workspace || workspace_bytes_in < need)
-      return fail(FA_ERR_WORKSPACE, "decode path needs a workspace of %zu bytes (got %zu)", need, workspace_bytes_in);
-    // the plan kernel writes the workspace while the same call reads the
-    // metadata, the caches and the descales: it may overlap none of them
-    if (overlaps(workspace, need, o, no) || overlaps(workspace, need, lse, nl) || overlaps(workspace, need, q, nq))
-      return fail(FA_ERR_INVALID, "workspace must not overlap q, o or lse");
-    if (overlaps(workspace, need, cu_seqlens_q, (size_t)(B + 1) * 4) || overlaps(workspace, need, seqlen_k, (size_t)B * 4) ||
-        overlaps(workspace, need, block_table, (size_t)(B * max_pages_per_seq) * 4))
-      return fail(FA_ERR_INVALID, "workspace must not overlap cu_seqlens_q, seqlen_k or block_table");
-    if (overlaps(workspace, need, k_cache, nk) || overlaps(workspace, need, v_cache, nv) ||
-        overlaps(workspace, need, k_descale, 4) || overlaps(workspace, need, v_descale, 4) ||
-        (q8 && overlaps(workspace, need, opts->q_descale, 4)))
-      return fail(FA_ERR_INVALID, "workspace must not overlap the caches or the descales");
+    if (use_scratch) {
+      if (need > kScratchBytes)
+        return fail(FA_ERR_LIMIT, "this decode call needs %zu bytes of scratch; fa_fwd_paged_noalloc holds %zu "
+                    "(fa_fwd_paged with a workspace has no such limit)", need, kScratchBytes);
+    } else {
+      if (!workspace || workspace_bytes_in < need)
+        return fail(FA_ERR_WORKSPACE, "decode path needs a workspace of %zu bytes (got %zu)", need, workspace_bytes_in);
+      // the plan kernel writes the workspace while the same call reads the
+      // metadata, the caches and the descales: it may overlap none of them
+      if (overlaps(workspace, need, o, no) || overlaps(workspace, need, lse, nl) || overlaps(workspace, need, q, nq))
+        return fail(FA_ERR_INVALID, "workspace must not overlap q, o or lse");
+      if (overlaps(workspace, need, cu_seqlens_q, (size_t)(B + 1) * 4) ||
+          overlaps(workspace, need, seqlen_k, (size_t)B * 4) ||
+          overlaps(workspace, need, block_table, (size_t)(B * max_pages_per_seq) * 4))
+        return fail(FA_ERR_INVALID, "workspace must not overlap cu_seqlens_q, seqlen_k or block_table");
+      if (overlaps(workspace, need, k_cache, nk) || overlaps(workspace, need, v_cache, nv) ||
+          overlaps(workspace, need, k_descale, 4) || overlaps(workspace, need, v_descale, 4) ||
+          (q8 && overlaps(workspace, need, opts->q_descale, 4)))
+        return fail(FA_ERR_INVALID, "workspace must not overlap the caches or the descales");
+    }
     if (B * Hkv * ((max_seqlen_k + 31) / 32) >= kI32) return fail(FA_ERR_LIMIT, "decode tile count exceeds 2^31");
     const DecodeLayout L = decode_layout(B, max_seqlen_q, max_seqlen_k, Hq, Hkv, d_v,
                                          std::min<int64_t>(max_pages_per_seq * page_size, kI32 - 1), vec);
+    // every host check is done: the first HIP call of the no-allocation path
+    // looks up this device's copy of the scratch array
+    if (use_scratch && (rc = scratch_for_current_device(&workspace))) return rc;
     int32_t* tiles = (int32_t*)workspace;
     float* part_o = (float*)((char*)workspace + L.tiles_bytes);
     float* part_lse = (float*)((char*)part_o + L.o_bytes);
@@ -516,6 +560,18 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* 
   return paged_impl(nullptr, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, B, total_q,
                     max_seqlen_q, max_seqlen_k, num_pages, page_size, max_pages_per_seq, Hq, Hkv, d_qk, d_v,
                     kv_dtype, k_descale, v_descale, workspace, workspace_bytes_in, mods, stream);
+}
+
+int fa_fwd_paged_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                         const int32_t* cu_seqlens_q, const int32_t* seqlen_k, const int32_t* block_table,
+                         int64_t B, int64_t total_q, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                         int64_t num_pages, int64_t page_size, int64_t max_pages_per_seq,
+                         int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v, fa_dtype kv_dtype,
+                         const float* k_descale, const float* v_descale,
+                         const fa_mods* mods, void* stream) {
+  return paged_impl(nullptr, q, k_cache, v_cache, o, lse, cu_seqlens_q, seqlen_k, block_table, B, total_q,
+                    max_seqlen_q, max_seqlen_k, num_pages, page_size, max_pages_per_seq, Hq, Hkv, d_qk, d_v,
+                    kv_dtype, k_descale, v_descale, nullptr, 0, mods, stream, true);
 }
 
 int fa_fwd_paged_vec(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,

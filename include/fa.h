@@ -150,6 +150,27 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* 
                  const fa_mods* mods, void* stream);
 
 /*
+ * fa_fwd_paged without a workspace argument, for callers that cannot
+ * allocate device memory per call: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Arguments, results and
+ * errors are fa_fwd_paged's (bitwise the same outputs).  The decode path's
+ * scratch (tile prefix and split-KV partials) lives in a static device
+ * array of 64 MiB that every GPU running the library holds until the
+ * process ends; a call whose decode path would need more returns
+ * FA_ERR_LIMIT (fa_fwd_paged_workspace_size gives the need).  Nothing is
+ * allocated and no part of the array needs clearing (each call writes what
+ * it reads).  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (other streams, other threads) race.
+ */
+int fa_fwd_paged_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                         const int32_t* cu_seqlens_q, const int32_t* seqlen_k, const int32_t* block_table,
+                         int64_t B, int64_t total_q, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                         int64_t num_pages, int64_t page_size, int64_t max_pages_per_seq,
+                         int64_t Hq, int64_t Hkv, int64_t d_qk, int64_t d_v, fa_dtype kv_dtype,
+                         const float* k_descale, const float* v_descale,
+                         const fa_mods* mods, void* stream);
+
+/*
  * Paged KV cache in the vectorised 5-D page format (review of "Support paged
  * FP8 Flash attention with asymmetric K/V head dim on gfx950", which gives
  * the two cache shapes and the permutes that take them back to token-major):

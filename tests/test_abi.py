@@ -298,3 +298,38 @@ def test_bwd_rejects_score_mods_and_overlap():
     rc = fa.lib.fa_bwd_dense(*ptrs, 1, 16, 16, 2, 2, 64, 64, None, FAKE * 30, 1 << 20, None)
     assert rc == -1 and "overlap" in fa.fa_last_error()
     assert fa.fa_bwd_workspace_size(0, 4) == 0 and fa.fa_bwd_workspace_size(10, 4) == 160
+
+
+def _noalloc(**kw):
+    fa = _lib()
+    a = dict(q=FAKE, kc=FAKE * 2, vc=FAKE * 3, o=FAKE * 4, lse=FAKE * 5, cu=FAKE * 6, sk=FAKE * 7, bt=FAKE * 8,
+             B=2, Tq=2, msq=1, msk=100, P=10, ps=64, mp=2, Hq=16, Hkv=2, dqk=192, dv=128, kv=1,
+             kd=FAKE * 9, vd=FAKE * 10, mods=None)
+    a.update(kw)
+    rc = fa.lib.fa_fwd_paged_noalloc(a["q"], a["kc"], a["vc"], a["o"], a["lse"], a["cu"], a["sk"], a["bt"], a["B"],
+                                     a["Tq"], a["msq"], a["msk"], a["P"], a["ps"], a["mp"], a["Hq"], a["Hkv"],
+                                     a["dqk"], a["dv"], a["kv"], a["kd"], a["vd"], a["mods"], None)
+    return rc, fa.fa_last_error()
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(ps=48), -2, "power of two"),
+    (dict(kd=0), -1, "descale"),
+    (dict(bt=0), -1, "non-NULL"),
+    # a decode call whose scratch need exceeds the static 64 MiB array
+    (dict(B=4096, Tq=4096, msk=1 << 20, mp=(1 << 20) // 64, Hq=64, Hkv=8,
+          **{n: (i + 1) << 30 for i, n in enumerate(["q", "kc", "vc", "o", "lse", "cu", "sk", "bt", "kd", "vd"])}),
+     -3, "scratch"),
+])
+def test_paged_noalloc_rejects(kw, code, frag):
+    """The no-allocation entry point validates like fa_fwd_paged (before any
+    HIP call) and refuses decode calls whose scratch exceeds its array."""
+    rc, msg = _noalloc(**kw)
+    assert rc == code and frag in msg, (rc, msg)
+
+
+def test_paged_noalloc_limit_matches_the_workspace_query():
+    fa = _lib()
+    need = fa.fa_fwd_paged_workspace_size(4096, 4096, 1, 1 << 20, 64, 8, 192, 128, 64)
+    assert need > 64 << 20
+    assert fa.fa_fwd_paged_workspace_size(64, 64, 1, 32768, 64, 8, 192, 128, 64) <= 64 << 20
