@@ -8,7 +8,19 @@ whole hot path: work enumeration, K/V addressing and staging, Q.K^T, masks,
 online softmax, P.V, epilogue with O and LSE).  Inputs are resident in HBM
 before timing starts.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+The default line also carries the metric's second half and the other
+workloads, each timed the same way (HIP events on the launch stream plus the
+host clock):
+  "decode":    the paged FP8 decode (64 sequences, contexts U[1024, 32768],
+               GQA 64/8, D 192/128, pages of 64): HBM GB/s, roofline and
+               the oracle's CPU baseline;
+  "secondary": the paged FP8 prefill (4 x 2048, D 192/128) and the five
+               flex workloads (B2 H16 S8192 D128: ALiBi, soft-cap, window
+               (256, 0), Bernoulli block mask, block-causal);
+  "latency":   per-call cost of the dense 1x128x2x64 forward (GPU time,
+               wall time, host cost of the binding and of the C call).
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--only]
                   [--flex alibi|softcap|window|bernoulli|block_causal|none|causal] [--page-size P]
                   [--layout head_major|vec] [--q-dtype bf16|fp8] [--dv 128|192]
                   [--no-cpu-baseline]
@@ -17,11 +29,12 @@ before timing starts.
 
 --config selects another workload for investigation (1 dense D64, 3 paged
 FP8 prefill, 4 paged FP8 decode, 5 flex, 6 FP8 KV-cache write of the decode
-cache, 7 backward pass of config 2's batch); the default line is config 2.
---layout vec runs configs 3 and 4 on the vectorised 5-D page format
-(fa_fwd_paged_vec) instead of head-major pages; --q-dtype fp8 gives them
-E4M3 queries with a per-tensor descale (fa_fwd_paged_ex); --dv 192 runs them
-with value/output width 192.
+cache, 7 backward pass of config 2's batch); the default line is config 2
+(--only leaves out its decode, secondary and latency entries).  --layout vec
+runs configs 3 and 4 on the vectorised 5-D page format (fa_fwd_paged_vec)
+instead of head-major pages; --q-dtype fp8 gives them E4M3 queries with a
+per-tensor descale (fa_fwd_paged_ex); --dv 192 runs them with value/output
+width 192.
 Prints ONE JSON line.
 """
 from __future__ import annotations
@@ -41,10 +54,13 @@ METRIC = "attention fwd TFLOP/s + fraction of MFMA peak; paged-decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 COPY_BYTES = 256 << 20        # calibration copy for the HBM byte counters
-DOMINANT = {"prefill": "fa_prefill_kernel", "decode": "fa_decode_kernel", "kvwrite": "fa_kv_write_kernel",
+# dominant kernel of each kind, matched as a substring of the kernel name
+# (the bf16 prefill is fa_prefill_bf16_kernel, the FP8 one fa_prefill_kernel)
+DOMINANT = {"prefill": "fa_prefill", "decode": "fa_decode_kernel", "kvwrite": "fa_kv_write_kernel",
             "backward": "fa_bwd_dkdv_kernel"}
 KERNEL_SOURCES = {
-    "prefill": ["attention_fa_fwd_03_amd/csrc/fa_prefill.hip", "attention_fa_fwd_03_amd/csrc/fa_prefill_common.h",
+    "prefill": ["attention_fa_fwd_03_amd/csrc/fa_prefill.hip", "attention_fa_fwd_03_amd/csrc/fa_prefill_bf16.hip",
+                "attention_fa_fwd_03_amd/csrc/fa_prefill_common.h",
                 "attention_fa_fwd_03_amd/csrc/fa_device.h",
                 "attention_fa_fwd_03_amd/csrc/fa_kernels.h"],
     "decode": ["attention_fa_fwd_03_amd/csrc/fa_decode.hip", "attention_fa_fwd_03_amd/csrc/fa_device.h",
@@ -325,12 +341,138 @@ def _timed_reps(fn, min_seconds: float = 10.0, max_reps: int = 30):
     return time.perf_counter() - t0, reps
 
 
-def _cores() -> int:
+def _affinity() -> int:
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+        return os.cpu_count() or 1
+
+
+def _cores() -> int:
+    """Oracle worker threads: the affinity cores, at most 16 (the GPU machine's
+    CPU share for one GPU)."""
+    return max(1, min(_affinity(), 16))
+
+
+def _key(cfg, flex="alibi", page_size=64, layout="head_major", q_dtype="bf16", dv=128):
+    key = f"config{cfg}" + (f"_{flex}" if cfg == 5 else "")
+    if cfg == 4 and page_size != 64:
+        key += f"_ps{page_size}"
+    if cfg == 6:
+        key += f"_ps{page_size}" + ("_vec" if layout == "vec" else "") + (f"_dv{dv}" if dv != 128 else "")
+    if cfg in (3, 4) and layout == "vec":
+        key += "_vec"
+    if cfg in (3, 4) and q_dtype == "fp8":
+        key += "_q8"
+    if cfg in (3, 4) and dv != 128:
+        key += f"_dv{dv}"
+    return key
+
+
+def measure(torch, synth, fa, cfg, flex="alibi", steps=30, warmup=10, page_size=64, layout="head_major",
+            q_dtype="bf16", dv=128, cpu=True):
+    """One workload: W untimed steps, then K steps timed by the host clock
+    and by HIP events on the launch stream (torch's current stream, where
+    the binding enqueues).  Returns a dict with value/unit/roofline/config
+    and, for workloads that have one and when asked, the oracle's cpu_baseline."""
+    name, run, work, cfg_extra, sample = build_workload(cfg, flex, torch, synth, fa, page_size, layout, q_dtype, dv)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_s = ev0.elapsed_time(ev1) * 1e-3 / steps
+    tflops = work["flops"] * steps / wall / 1e12
+    if work["bound"] == "hbm":
+        value, unit = work["bytes"] * steps / wall / 1e9, "GB/s"
+        achieved = work["bytes"] / per_launch_s / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 2), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBS, 4))
+    else:
+        value, unit = tflops, "TFLOP/s"
+        achieved = work["flops"] / per_launch_s / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 4))
+    roof["traffic"] = measured_traffic(_key(cfg, flex, page_size, layout, q_dtype, dv), work["kind"])
+    roof["kernel_ms"] = round(per_launch_s * 1e3, 4)
+    out = dict(value=round(value, 3), unit=unit, ms_per_step=round(wall * 1e3 / steps, 4),
+               config={"workload": name, **cfg_extra}, roofline=roof, cpu_baseline=None,
+               dtype=("fp8-qkv/bf16" if q_dtype == "fp8" else "fp8-kv/bf16") if cfg in (3, 4)
+               else ("bf16->fp8" if cfg == 6 else "bf16"))
+    if work["bound"] == "hbm" and work["flops"]:
+        out["config"]["tflops"] = round(tflops, 3)
+    if sample is not None and cpu:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            r = sample()
+        cval = r["work"] / r["seconds"] / (1e9 if work["bound"] == "hbm" else 1e12)
+        out["cpu_baseline"] = dict(value=round(cval, 6), unit=unit, cores=_cores(), cores_available=_affinity(),
+                                   kind="oracle", sample=r["sample"], seconds=round(r["seconds"], 2))
+    return out
+
+
+def call_latency(torch, synth, fa, calls=2000):
+    """Per-call cost of the dense 1x128x2x64 forward (launch-bound: 8.4 MFLOP):
+    GPU time of one launch (HIP events over many back-to-back launches),
+    wall time per call with the queue kept busy, wall time of one call
+    waited on, and the host side split into the Python binding's
+    marshalling and the C call (validation and kernel launch), timed by
+    calling the C entry point through ctypes with prepared arguments."""
+    import ctypes
+    from attention_fa_fwd_03_amd import binding as B
+    d = synth.make_dense(1, 128, 128, 2, 2, 64, 64, seed=synth.seed_for(1), device="cuda")
+    o = torch.empty(1, 128, 2, 64, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(1, 2, 128, dtype=torch.float32, device="cuda")
+    mods = fa.Mods(scale=1 / 8)
+    run = lambda: fa.fa_fwd_dense(d["q"], d["k"], d["v"], o, lse, mods)
+    for _ in range(50):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(calls):
+        run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_busy = (time.perf_counter() - t0) / calls
+    gpu = ev0.elapsed_time(ev1) * 1e-3 / calls
+    # one call waited on, repeatedly
+    n1 = 200
+    t0 = time.perf_counter()
+    for _ in range(n1):
+        run()
+        torch.cuda.synchronize()
+    wall_sync = (time.perf_counter() - t0) / n1
+    # the C entry point alone (validation + launch), arguments prepared once
+    cmods = mods.to_c()
+    cm = ctypes.byref(cmods)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    args = (d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(), o.data_ptr(), lse.data_ptr(),
+            1, 128, 128, 2, 2, 64, 64, cm, sp)
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        B.lib.fa_fwd_dense(*args)
+    c_call = (time.perf_counter() - t0) / calls
+    torch.cuda.synchronize()
+    # an empty ctypes call into the library: the foreign-call floor
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        B.lib.fa_abi_version()
+    ffi = (time.perf_counter() - t0) / calls
+    us = lambda x: round(x * 1e6, 2)
+    return dict(workload="dense non-causal B1 H2 S128 D64 bf16 (launch-bound)", unit="us per call",
+                gpu_us=us(gpu), wall_us_queued=us(wall_busy), wall_us_synchronised=us(wall_sync),
+                host_us_binding=us(max(wall_busy - c_call, 0.0)), host_us_c_call=us(c_call),
+                host_us_ctypes_floor=us(ffi), calls=calls)
 
 
 def main():
@@ -347,22 +489,14 @@ def main():
                     help="paged configs: bf16 or E4M3 queries")
     ap.add_argument("--dv", type=int, choices=[128, 192], default=128, help="paged configs: value/output width")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", action="store_true",
+                    help="default config only: leave out the decode, secondary and latency entries")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (reference for HBM byte counters)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="record HBM bytes per launch from two rocprofv3 --pmc counter CSVs and exit")
     args = ap.parse_args()
-    key = f"config{args.config}" + (f"_{args.flex}" if args.config == 5 else "")
-    if args.config == 4 and args.page_size != 64:
-        key += f"_ps{args.page_size}"
-    if args.config == 6:
-        key += f"_ps{args.page_size}" + ("_vec" if args.layout == "vec" else "") + (f"_dv{args.dv}" if args.dv != 128 else "")
-    if args.config in (3, 4) and args.layout == "vec":
-        key += "_vec"
-    if args.config in (3, 4) and args.q_dtype == "fp8":
-        key += "_q8"
-    if args.config in (3, 4) and args.dv != 128:
-        key += f"_dv{args.dv}"
+    key = _key(args.config, args.flex, args.page_size, args.layout, args.q_dtype, args.dv)
     if args.traffic_from:
         kind = {4: "decode", 6: "kvwrite", 7: "backward"}.get(args.config, "prefill")
         print(json.dumps({key: traffic_from_counters(args.traffic_from[0], args.traffic_from[1], key, kind)}))
@@ -377,8 +511,6 @@ def main():
     import attention_fa_fwd_03_amd as fa
 
     torch.cuda.init()
-    name, run, work, cfg_extra, sample = build_workload(args.config, args.flex, torch, synth, fa, args.page_size,
-                                                       args.layout, args.q_dtype, args.dv)
     if args.copy_calibration:
         # reference for the HBM byte counters: one device-to-device copy of
         # COPY_BYTES through the HIP runtime's own copy kernel
@@ -396,71 +528,45 @@ def main():
             raise SystemExit(f"hipMemcpyAsync failed: {rc}")
         del a, b
 
-    for _ in range(args.warmup):
-        run()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        run()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = wall * 1e3 / args.steps
-    per_launch_s = gpu_ms * 1e-3 / args.steps
-
-    tflops = work["flops"] * args.steps / wall / 1e12
-    if work["bound"] == "hbm":
-        value = work["bytes"] * args.steps / wall / 1e9
-        unit = "GB/s"
-        achieved = work["bytes"] / per_launch_s / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 2), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(achieved / PEAK_HBM_GBS, 4))
-    else:
-        value = tflops
-        unit = "TFLOP/s"
-        achieved = work["flops"] / per_launch_s / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / PEAK_BF16_TFLOPS, 4))
-    roof["traffic"] = measured_traffic(key, work["kind"])
-    roof["kernel_ms"] = round(per_launch_s * 1e3, 4)
-
-    cpu = None
-    if sample is not None and not args.no_cpu_baseline:
-        from threadpoolctl import threadpool_limits
-        with threadpool_limits(limits=1):
-            r = sample()
-        if work["bound"] == "hbm":
-            cval, cunit = r["work"] / r["seconds"] / 1e9, "GB/s"
-        else:
-            cval, cunit = r["work"] / r["seconds"] / 1e12, "TFLOP/s"
-        cpu = dict(value=round(cval, 6), unit=cunit, cores=_cores(), kind="oracle", sample=r["sample"],
-                   seconds=round(r["seconds"], 2))
-
+    cpu = not args.no_cpu_baseline
+    m = measure(torch, synth, fa, args.config, args.flex, args.steps, args.warmup, args.page_size, args.layout,
+                args.q_dtype, args.dv, cpu=cpu)
     line = {
         "metric": METRIC,
-        "value": round(value, 3),
-        "unit": unit,
+        "value": m["value"],
+        "unit": m["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("fp8-qkv/bf16" if args.q_dtype == "fp8" else "fp8-kv/bf16") if args.config in (3, 4)
-        else ("bf16->fp8" if args.config == 6 else "bf16"),
+        "dtype": m["dtype"],
         "data": "synthetic",
-        "config": {"workload": name, **cfg_extra},
-        "roofline": roof,
-        "cpu_baseline": cpu,
+        "config": m["config"],
+        "roofline": m["roofline"],
+        "cpu_baseline": m["cpu_baseline"],
     }
-    if work["bound"] == "hbm" and work["flops"]:
-        line["config"]["tflops"] = round(tflops, 3)
+    if args.config == 2 and not args.only:
+        # the metric's second half: the paged FP8 decode's HBM GB/s (config 4),
+        # timed the same way, with its own oracle baseline
+        torch.cuda.empty_cache()
+        dm = measure(torch, synth, fa, 4, steps=args.steps, warmup=args.warmup, cpu=cpu)
+        line["decode"] = {"metric": "paged-decode HBM GB/s", **dm}
+        torch.cuda.empty_cache()
+        sec = []
+        k2, w2 = min(args.steps, 20), min(args.warmup, 5)
+        for cfg, flex in [(3, None), (5, "alibi"), (5, "softcap"), (5, "window"), (5, "bernoulli"),
+                          (5, "block_causal")]:
+            sm = measure(torch, synth, fa, cfg, flex or "alibi", k2, w2, cpu=False)
+            sec.append({"workload": sm["config"]["workload"], "value": sm["value"], "unit": sm["unit"],
+                        "dtype": sm["dtype"], "roofline": {k: sm["roofline"][k] for k in
+                                                           ("bound", "achieved", "peak", "unit", "frac",
+                                                            "kernel_ms")}})
+            torch.cuda.empty_cache()
+        line["secondary"] = sec
+        line["latency"] = call_latency(torch, synth, fa)
     print(json.dumps(line))
 
 
