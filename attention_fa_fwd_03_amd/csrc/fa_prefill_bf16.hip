@@ -35,7 +35,7 @@
 
 namespace fa {
 
-template <int D, bool PAGED, int MODS>
+template <int D, bool PAGED, int MODS, bool BMASK>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_prefill_bf16_kernel(const PrefillArgs a) {
   constexpr int kRow = D * 2;                 // bytes per K / V row in LDS
@@ -102,6 +102,10 @@ void fa_prefill_bf16_kernel(const PrefillArgs a) {
   const int wq0 = q0 + wave * 32;
   const int wq1 = min(wq0 + 31, q1 - 1);
   const int wave_lo_max = row_lo(wq1), wave_hi_min = row_hi(wq0);
+  // the last key this wavefront's rows can see (-1 if every row is past the
+  // sequence's end): tiles after it would only add zero products
+  const int wave_hi_max = wq0 < q1 ? row_hi(wq1) : -1;
+  auto wave_reaches = [&](int t) { return t * BN <= wave_hi_max; };
 
   // C: raw dot product -> log2-domain scaled logit (mods: applied explicitly)
   const float C = ANYMOD ? 1.0f : a.qk_scale * kLog2e;
@@ -115,9 +119,12 @@ void fa_prefill_bf16_kernel(const PrefillArgs a) {
   for (int d = 0; d < ND; ++d) oacc[d] = f32x16{};
   float m_run = kMaxFloor, l_run = 0.0f;
 
+  // next active tile at or after t (t_end + 1 when none): every tile, or
+  // with a block mask the tiles active for this workgroup's query tile
   MaskBits mb;
-  mb.init(a, sv, q0);
+  if (BMASK) mb.init(a, sv, q0);
   auto next_tile = [&](int t) {
+    if (!BMASK) return t;
     for (; t <= t_end; ++t)
       if (mb.tile_bits(t)) return t;
     return t;
@@ -357,16 +364,22 @@ void fa_prefill_bf16_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) xs[kb][i] = fmaf(xs[kb][i], C, -m_run);
     }
-    // step n: K_{n+1} and V_n published at its barrier; the last tile's
-    // step (no K_{n+1}) runs after the loop
+    // step n: K_{n+1} and V_n published at its barrier.  Every wavefront
+    // takes part in every barrier and issues its share of every copy; it
+    // computes the tiles up to its last visible key (a tile before its
+    // first visible key is computed and masked, contributing nothing).
     int n = 0;
-    while (tn <= t_end) {
+    auto publish = [&]() {
       // publish K_{n+1} and V_n; every wavefront is done with K_n and V_{n-1}
       FA_WAIT_VMCNT(0);
       __syncthreads();
-      const int tnn = next_tile(tn + 1);
+      const int tnn = tn <= t_end ? next_tile(tn + 1) : t_end + 1;
       if (tnn <= t_end) issue_k(tnn, kslot(n & 1));
-      issue_v(tn, vslot((n + 1) & 1));
+      if (tn <= t_end) issue_v(tn, vslot((n + 1) & 1));
+      return tnn;
+    };
+    while (tn <= t_end && wave_reaches(tn)) {
+      const int tnn = publish();
       phase_a(std::true_type{}, kslot((n + 1) & 1));
       prep(sn, tn);
       phase_b(std::true_type{}, vslot(n & 1));
@@ -374,10 +387,24 @@ void fa_prefill_bf16_kernel(const PrefillArgs a) {
       tc = tn;
       tn = tnn;
     }
-    FA_WAIT_VMCNT(0);
-    __syncthreads();
-    phase_a(std::false_type{}, kslot(0));
-    phase_b(std::false_type{}, vslot(n & 1));
+    // the last tile this wavefront computes: P.V only
+    {
+      const int tnn = publish();
+      if (wave_reaches(tc)) {
+        phase_a(std::false_type{}, kslot(0));
+        phase_b(std::false_type{}, vslot(n & 1));
+      }
+      ++n;
+      tc = tn;
+      tn = tnn;
+    }
+    // tiles past this wavefront's keys: barriers and copies only
+    while (tc <= t_end) {
+      const int tnn = publish();
+      ++n;
+      tc = tn;
+      tn = tnn;
+    }
   }
 
   // ---------------- epilogue ----------------
@@ -410,7 +437,10 @@ void fa_prefill_bf16_kernel(const PrefillArgs a) {
 template <int D, bool PAGED, int MODS>
 static hipError_t launch_bf16(const PrefillArgs& a, int n_bh, int n_qtiles, hipStream_t stream) {
   dim3 grid((n_bh + 7) / 8 * 8, n_qtiles);
-  hipLaunchKernelGGL((fa_prefill_bf16_kernel<D, PAGED, MODS>), grid, dim3(NTHREADS), 0, stream, a);
+  if (a.bmask)
+    hipLaunchKernelGGL((fa_prefill_bf16_kernel<D, PAGED, MODS, true>), grid, dim3(NTHREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fa_prefill_bf16_kernel<D, PAGED, MODS, false>), grid, dim3(NTHREADS), 0, stream, a);
   return hipGetLastError();
 }
 
