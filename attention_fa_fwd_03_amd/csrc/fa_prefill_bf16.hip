@@ -109,8 +109,16 @@ void fa_prefill_bf16_kernel(const PrefillArgs a) {
 
   // C: raw dot product -> log2-domain scaled logit (mods: applied explicitly)
   const float C = ANYMOD ? 1.0f : a.qk_scale * kLog2e;
-  const float raw_scale = a.qk_scale;
-  const float cap = a.softcap, inv_cap = SOFTCAP ? 1.0f / a.softcap : 0.0f;
+  // Mods in the log2 domain with every constant folded.  Soft-cap:
+  // c tanh(x / c) log2(e) = c' - 2 c' / (1 + 2^(k s)) for the raw score s,
+  // k = 2 scale log2(e) / c and c' = c log2(e) (tanh(u) = 1 - 2 / (1 + e^{2u});
+  // +-inf from the exponential give +-c', the correct limits): one multiply,
+  // exp2, add, reciprocal and FMA per score.  ALiBi: - slope log2(e) |i' - j|
+  // by one FMA with an absolute-value operand.
+  const float lin2 = a.qk_scale * kLog2e;
+  const float cap_k = SOFTCAP ? 2.0f * a.qk_scale * kLog2e / a.softcap : 0.0f;
+  const float cap_c = SOFTCAP ? a.softcap * kLog2e : 0.0f;
+  const float slope2 = ALIBI ? a.alibi_slope * kLog2e : 0.0f;
   const int ip = qrow + delta;
   const int lane_key = (lane >> 5) * 4;      // key offset of this lane's S^T registers
 
@@ -188,17 +196,18 @@ void fa_prefill_bf16_kernel(const PrefillArgs a) {
   auto prep = [&](f32x16 (&s)[2], int t) {
     const int k0 = t * BN;
     if (ANYMOD) {
+      // i' - j of register (kb, i) is d0 - (32 kb + 8 (i/4) + i%4), exact in
+      // fp32 below 2^24 keys apart
+      const float d0 = (float)(ip - k0 - lane_key);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float x = s[kb][i] * raw_scale;
-          if (SOFTCAP) x = cap * tanh_fast(x * inv_cap);
-          if (ALIBI) {
-            const int j = k0 + kb * 32 + (i >> 2) * 8 + lane_key + (i & 3);
-            x -= a.alibi_slope * fabsf((float)(ip - j));
-          }
-          s[kb][i] = x * kLog2e;
+          float x;
+          if (SOFTCAP) x = fmaf(rcp_hw(1.0f + exp2_hw(s[kb][i] * cap_k)), -2.0f * cap_c, cap_c);
+          else x = s[kb][i] * lin2;
+          if (ALIBI) x = fmaf(-slope2, fabsf(d0 - (float)(kb * 32 + (i >> 2) * 8 + (i & 3))), x);
+          s[kb][i] = x;
         }
     }
     if (!(k0 >= wave_lo_max && k0 + BN - 1 <= wave_hi_min)) {
