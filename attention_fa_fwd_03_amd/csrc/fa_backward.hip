@@ -173,7 +173,9 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int bg = blockIdx.x;
+  // causal: key blocks near the start see the most rows and come first (y
+  // ascending); the head rotates by one slot of 8 per level as in the dQ grid
+  const int bg = a.causal ? ((int)blockIdx.x + 8 * (int)blockIdx.y) % (int)gridDim.x : (int)blockIdx.x;
   if (bg >= a.B * a.Hkv) return;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const BwSeq sv = bw_seq(a, b);
@@ -346,11 +348,16 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int bh = blockIdx.x;
+  // causal: the head rotates by one slot of 8 per level, so that a CU does
+  // not meet the same (sequence, head) at every level it serves
+  const int bh = a.causal ? ((int)blockIdx.x + 8 * (int)blockIdx.y) % (int)gridDim.x : (int)blockIdx.x;
   if (bh >= a.B * a.Hq) return;
   const int b = bh / a.Hq, h = bh % a.Hq, g = h / a.group;
   const BwSeq sv = bw_seq(a, b);
-  const int q0 = blockIdx.y * kBwRowsQ;
+  // causal: the longest query tiles (the last ones) start first, so the
+  // grid ends on short tiles instead of long ones
+  const int qt = a.causal ? (int)gridDim.y - 1 - (int)blockIdx.y : (int)blockIdx.y;
+  const int q0 = qt * kBwRowsQ;
   if (q0 >= sv.sq) return;
   const int q1 = min(q0 + kBwRowsQ, sv.sq);
   const int delta_al = sv.skv - sv.sq;
