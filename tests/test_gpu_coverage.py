@@ -135,3 +135,20 @@ def test_fp8_cache_bf16_query_range(path, vec, how):
     o, lse = _paged_vec_run(d, mods, 128) if vec else _paged_run(d, mods, 128)
     o_ref, l_ref = _paged_ref(d, mods)
     _cmp_packed(o, lse, o_ref, l_ref, TOL_O_FP8, f"query range {how} {path} vec={vec}")
+
+
+# ----------------------------------------------------------------------------- soft-cap saturation
+@pytest.mark.parametrize("qscale", [30.0, 500.0])
+@pytest.mark.parametrize("D", [64, 128])
+def test_softcap_saturation(D, qscale):
+    """Soft-cap where tanh saturates: queries scaled so that |logit| / cap
+    reaches ~10 (x30) or ~100 (x500), past the point where the kernel's
+    2^(2u log2 e) overflows to +inf or underflows to 0; the capped logits
+    must come out at +-cap, alone and with ALiBi and a causal mask."""
+    d = synth.make_dense(1, 300, 300, 2, 2, D, D, seed=661 + D)
+    d["q"] = (d["q"].float() * qscale).to(torch.bfloat16)
+    for mods in (dict(softcap=5.0), dict(softcap=5.0, alibi_slope=0.25, causal=True)):
+        o, lse = _dense_run(d, mods, D)
+        o_ref, l_ref = oracle.attention_dense(f64(d["q"]), f64(d["k"]), f64(d["v"]), dict(mods))
+        compare(o.permute(0, 2, 1, 3), lse, o_ref.transpose(0, 2, 1, 3), l_ref, TOL_O_BF16,
+                what=f"softcap saturation D{D} x{qscale} {sorted(mods)}")
