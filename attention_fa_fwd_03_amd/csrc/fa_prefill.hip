@@ -654,15 +654,18 @@ void fa_prefill_kernel(const PrefillArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
       }
+      // P^T operand of key step u = registers 8 (u%2) .. +8 of key block u/2
+      auto p_elem = [&](int u, int e) {
+        const float p = exp2_hw(fmaf(sacc[u >> 1][(u & 1) * 8 + e], C, -m_run));
+        l_run += p;
+        return (bf16)p;
+      };
       bf16x8 pf[4];
+      if constexpr (!(FP8 && !VREG)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = exp2_hw(fmaf(sacc[kb][i], C, -m_run));
-          l_run += p;
-          pf[kb * 2 + (i >> 3)][i & 7] = (bf16)p;
-        }
+          for (int e = 0; e < 8; ++e) pf[u][e] = p_elem(u, e);
       }
 
       // ---------------- O^T += V^T P^T ----------------
@@ -677,14 +680,31 @@ void fa_prefill_kernel(const PrefillArgs a) {
         const int i16 = lane & 15, t8 = i16 >> 1, q = i16 & 1;
         const int key = (t8 < 4 ? t8 : 4 + t8) + 4 * h;   // key within the 16-key step
         const int cg = (lane >> 4) & 1;                    // 16-dim half of the 32-dim block
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        // the exponentials of key step u + 1 run under the products of
+        // step u (only step 0's are computed ahead of the products)
+        constexpr int NDV = DV / 32;
+        constexpr int NV = 4 * NDV;      // products of the step, n = u NDV + d
+        constexpr int kAhead = 4;        // raw V fragments read this many products ahead
+        auto vraw = [&](int n) {
+          const int u = n / NDV, d = n % NDV;
           const int r = u * 16 + key;
-          const char FA_LDS* rp = vt + r * DV + q * 8;
-          const int sw = swzv8<DV>(r);
+          return lds_read_tr8(vt + r * DV + q * 8 + (((2 * d + cg) ^ swzv8<DV>(r)) << 4));
+        };
+        decltype(vraw(0)) vr[NV];
 #pragma unroll
-          for (int d = 0; d < DV / 32; ++d)
-            oacc[d] = mfma32(fp8x8_to_bf16(lds_read_tr8(rp + (((2 * d + cg) ^ sw) << 4))), pf[u], oacc[d]);
+        for (int n = 0; n < kAhead && n < NV; ++n) vr[n] = vraw(n);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[0][e] = p_elem(0, e);
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+          const int u = n / NDV, d = n % NDV;
+          if (n + kAhead < NV) vr[n + kAhead] = vraw(n + kAhead);
+          oacc[d] = mfma32(fp8x8_to_bf16(vr[n]), pf[u], oacc[d]);
+          if (u + 1 < 4) {
+#pragma unroll
+            for (int e = d * 8 / NDV; e < (d + 1) * 8 / NDV; ++e) pf[u + 1][e] = p_elem(u + 1, e);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       } else if constexpr (VEC) {
         // V^T tile: row d = 32 blk + lane%32, chunk 2u + lane/32
