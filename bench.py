@@ -55,14 +55,14 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 COPY_BYTES = 256 << 20        # calibration copy for the HBM byte counters
 # dominant kernel of each kind, matched as a substring of the kernel name
-# (the bf16 prefill is fa_prefill_bf16_kernel, the FP8 one fa_prefill_kernel)
-DOMINANT = {"prefill": "fa_prefill", "decode": "fa_decode_kernel", "kvwrite": "fa_kv_write_kernel",
-            "backward": "fa_bwd_dkdv_kernel"}
+# (the bf16 prefill is fa_prefill_bf16_kernel, the FP8-cache one fa_prefill_kernel)
+DOMINANT = {"prefill": "fa_prefill_bf16_kernel", "prefill_fp8": "fa_prefill_kernel", "decode": "fa_decode_kernel",
+            "kvwrite": "fa_kv_write_kernel", "backward": "fa_bwd_dkdv_kernel"}
 KERNEL_SOURCES = {
-    "prefill": ["attention_fa_fwd_03_amd/csrc/fa_prefill.hip", "attention_fa_fwd_03_amd/csrc/fa_prefill_bf16.hip",
-                "attention_fa_fwd_03_amd/csrc/fa_prefill_common.h",
-                "attention_fa_fwd_03_amd/csrc/fa_device.h",
-                "attention_fa_fwd_03_amd/csrc/fa_kernels.h"],
+    "prefill": ["attention_fa_fwd_03_amd/csrc/fa_prefill_bf16.hip", "attention_fa_fwd_03_amd/csrc/fa_prefill_common.h",
+                "attention_fa_fwd_03_amd/csrc/fa_device.h", "attention_fa_fwd_03_amd/csrc/fa_kernels.h"],
+    "prefill_fp8": ["attention_fa_fwd_03_amd/csrc/fa_prefill.hip", "attention_fa_fwd_03_amd/csrc/fa_prefill_common.h",
+                    "attention_fa_fwd_03_amd/csrc/fa_device.h", "attention_fa_fwd_03_amd/csrc/fa_kernels.h"],
     "decode": ["attention_fa_fwd_03_amd/csrc/fa_decode.hip", "attention_fa_fwd_03_amd/csrc/fa_device.h",
                "attention_fa_fwd_03_amd/csrc/fa_kernels.h"],
     "kvwrite": ["attention_fa_fwd_03_amd/csrc/fa_kvcache.hip", "attention_fa_fwd_03_amd/csrc/fa_device.h",
@@ -189,7 +189,7 @@ def build_workload(cfg: int, flex: str, torch, synth, fa, page_size: int = 64, l
                          q_descale=d["q_descale"])
         name = f"paged FP8 causal prefill 4x2048 H16 Dqk192 Dv{dv} page64" + (" vectorised" if layout == "vec" else "") \
             + (" fp8-q" if q_dtype == "fp8" else "")
-        return name, run, dict(flops=flops, kind="prefill", bound="mfma"), \
+        return name, run, dict(flops=flops, kind="prefill_fp8", bound="mfma"), \
             {"B": 4, "S": 2048, "H": 16, "d_qk": 192, "d_v": dv, "page_size": 64, "layout": layout,
              "q_dtype": q_dtype}, None
     if cfg == 4:
@@ -498,7 +498,7 @@ def main():
     args = ap.parse_args()
     key = _key(args.config, args.flex, args.page_size, args.layout, args.q_dtype, args.dv)
     if args.traffic_from:
-        kind = {4: "decode", 6: "kvwrite", 7: "backward"}.get(args.config, "prefill")
+        kind = {3: "prefill_fp8", 4: "decode", 6: "kvwrite", 7: "backward"}.get(args.config, "prefill")
         print(json.dumps({key: traffic_from_counters(args.traffic_from[0], args.traffic_from[1], key, kind)}))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
