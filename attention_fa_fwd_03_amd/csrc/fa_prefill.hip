@@ -660,36 +660,16 @@ void fa_prefill_kernel(const PrefillArgs a) {
         l_run += p;
         return (bf16)p;
       };
+      // O^T += V^T P^T, product n = u NDV + d.  For E4M3 V and vectorised
+      // pages the exponentials of key step u + 1 run under the products of
+      // step u (only step 0's are computed ahead of the products), with the
+      // V fragments read four products ahead.  A = V^T: lane m + 32 h takes d = 32 blk + m and, of the 16
+      // keys of step u, keys 4h..4h+3 and 8+4h..8+4h+3 (the order of P^T).
       bf16x8 pf[4];
-      if constexpr (!(FP8 && !VREG)) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pf[u][e] = p_elem(u, e);
-      }
-
-      // ---------------- O^T += V^T P^T ----------------
-      // A = V^T: lane m + 32 h takes d = 32 blk + m and, of the 16 keys of
-      // step u, keys 4h..4h+3 and 8+4h..8+4h+3 (the order of P^T)
-      if constexpr (FP8 && !VREG) {
-        // E4M3 key-major rows: lanes 2t+q of a 16-lane group read half q of
-        // row t of the group's eight keys; the transposing read gives lane i
-        // byte column i of those rows, converted exactly to bf16
-        const char FA_LDS* vt = cur + T::kTileK;
-        const int h = lane >> 5;
-        const int i16 = lane & 15, t8 = i16 >> 1, q = i16 & 1;
-        const int key = (t8 < 4 ? t8 : 4 + t8) + 4 * h;   // key within the 16-key step
-        const int cg = (lane >> 4) & 1;                    // 16-dim half of the 32-dim block
-        // the exponentials of key step u + 1 run under the products of
-        // step u (only step 0's are computed ahead of the products)
+      auto pv_loop = [&](auto vraw, auto vconv) {
         constexpr int NDV = DV / 32;
-        constexpr int NV = 4 * NDV;      // products of the step, n = u NDV + d
-        constexpr int kAhead = 4;        // raw V fragments read this many products ahead
-        auto vraw = [&](int n) {
-          const int u = n / NDV, d = n % NDV;
-          const int r = u * 16 + key;
-          return lds_read_tr8(vt + r * DV + q * 8 + (((2 * d + cg) ^ swzv8<DV>(r)) << 4));
-        };
+        constexpr int NV = 4 * NDV;
+        constexpr int kAhead = 4;
         decltype(vraw(0)) vr[NV];
 #pragma unroll
         for (int n = 0; n < kAhead && n < NV; ++n) vr[n] = vraw(n);
@@ -699,24 +679,49 @@ void fa_prefill_kernel(const PrefillArgs a) {
         for (int n = 0; n < NV; ++n) {
           const int u = n / NDV, d = n % NDV;
           if (n + kAhead < NV) vr[n + kAhead] = vraw(n + kAhead);
-          oacc[d] = mfma32(fp8x8_to_bf16(vr[n]), pf[u], oacc[d]);
+          oacc[d] = mfma32(vconv(vr[n]), pf[u], oacc[d]);
           if (u + 1 < 4) {
 #pragma unroll
             for (int e = d * 8 / NDV; e < (d + 1) * 8 / NDV; ++e) pf[u + 1][e] = p_elem(u + 1, e);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+      };
+      auto as_is = [](bf16x8 x) { return x; };
+      if constexpr (FP8 && !VREG) {
+        // E4M3 key-major rows: lanes 2t+q of a 16-lane group read half q of
+        // row t of the group's eight keys; the transposing read gives lane i
+        // byte column i of those rows, converted exactly to bf16
+        const char FA_LDS* vt = cur + T::kTileK;
+        const int h = lane >> 5;
+        const int i16 = lane & 15, t8 = i16 >> 1, q = i16 & 1;
+        const int key = (t8 < 4 ? t8 : 4 + t8) + 4 * h;   // key within the 16-key step
+        const int cg = (lane >> 4) & 1;                    // 16-dim half of the 32-dim block
+        pv_loop(
+            [&](int n) {
+              const int u = n / (DV / 32), d = n % (DV / 32);
+              const int r = u * 16 + key;
+              return lds_read_tr8(vt + r * DV + q * 8 + (((2 * d + cg) ^ swzv8<DV>(r)) << 4));
+            },
+            [](auto w) { return fp8x8_to_bf16(w); });
       } else if constexpr (VEC) {
         // V^T tile: row d = 32 blk + lane%32, chunk 2u + lane/32
         const char FA_LDS* vt = cur + T::kTileK + (lane & 31) * (BN * 2);
         const int sw = ((lane & 31) >> 1) & 7;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int c = ((2 * u + (lane >> 5)) ^ sw) << 4;
-#pragma unroll
-          for (int d = 0; d < DV / 32; ++d) oacc[d] = mfma32(lds_read_b128(vt + d * 32 * (BN * 2) + c), pf[u], oacc[d]);
-        }
+        pv_loop(
+            [&](int n) {
+              const int u = n / (DV / 32), d = n % (DV / 32);
+              return lds_read_b128(vt + d * 32 * (BN * 2) + (((2 * u + (lane >> 5)) ^ sw) << 4));
+            },
+            as_is);
       } else {
+        // bf16 V^T fragments read transposed (V staged through registers);
+        // here every exponential first, then the products (interleaving
+        // measured slower for this variant)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pf[u][e] = p_elem(u, e);
         const char FA_LDS* vt = cur + T::kTileK;
         const int grp = lane >> 4, i16 = lane & 15;
         const int hsel = grp >> 1;
