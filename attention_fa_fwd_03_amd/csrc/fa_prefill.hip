@@ -1,21 +1,21 @@
-// Fused attention forward (prefill / dense / varlen / paged) for gfx950.
+// Fused attention forward over FP8 E4M3 paged caches (head-major or
+// vectorised pages) for gfx950.  bf16 K/V and the score mods are served by
+// the software-pipelined kernel in fa_prefill_bf16.hip.
 //
 // One workgroup = 4 wavefronts = 128 query rows of one (sequence, q-head);
 // each wavefront owns 32 query rows.  A workgroup keeps its LDS ring within
 // 80 KB, so two workgroups share each CU and each SIMD runs one wavefront of
-// each: their barriers are independent, so one workgroup's vector and scalar
-// stretches overlap the other's matrix work.  The key axis is walked in tiles
-// of 64 keys staged in LDS (a ring of three stages, two tiles in flight, when
-// three fit in 80 KB: bf16 at D <= 64 and the FP8 caches; otherwise two
-// stages, the next tile loading while the current one is computed).  Per
-// tile and wavefront:
+// each.  The key axis is walked in tiles of 64 keys staged in LDS (a ring of
+// three stages, two tiles in flight).  Per tile and wavefront:
 //
-//   S^T[64 x 32]  = K_tile . Q^T          v_mfma_f32_32x32x16_bf16, A = K from LDS,
-//                                          B = Q fragments kept in registers
+//   S^T[64 x 32]  = K_tile . Q^T          v_mfma_scale_f32_32x32x64_f8f6f4 on the
+//                                          E4M3 K bytes (64 dims a step, unit
+//                                          scales), B = Q parts in registers
 //   online softmax on S^T                 lane l owns query row l%32; the row
 //                                          max needs one permlane32 swap
-//   O^T[Dv x 32] += V_tile^T . P^T        A = V read transposed from LDS
-//                                          (ds_read_b64_tr_b16), B = P in registers
+//   O^T[Dv x 32] += V_tile^T . P^T        v_mfma_f32_32x32x16_bf16, A = V read
+//                                          transposed and converted to bf16,
+//                                          B = P in registers
 //
 // Computing the transposed products keeps every per-row quantity (running
 // max, denominator, rescale factor, output scaling) lane-local.  The P^T
@@ -23,36 +23,37 @@
 // an MFMA step in the order that swaps bits 2 and 3 of the key index; the V
 // transposed reads fetch rows in that same order, so K and V stay paired.
 //
+// Queries: E4M3 codes as given (one product per step, q_descale folded into
+// the logit constant), or bf16 split per row into two E4M3 parts of 2^e q
+// (hi + lo, about 2^-8 relative; each part times a K byte is exact), e from
+// the row's largest magnitude so that hi stays in the E4M3 normal range;
+// 2^-e and the K descale fold into that row's logit constant.
+//
 // Softmax works in the log2 domain: the running max m is kept in units of
 // scale*log2(e)*logit so that p = exp2(fma(x, C, -m)) is one FMA and one
 // v_exp_f32 per score (method: LSE PR, "log2 domain with the logit scale
 // folded"; the paged FP8 PR folds the K descale into that same constant).
 // The output is rescaled only when some row's max grows by more than 2^8
 // (lazy rescaling, paged FP8 PR review), which leaves the result unchanged.
+// The exponentials of key step u + 1 run under the P.V products of step u.
 //
 // Masking is by select to -inf (never by multiply, so NaN bytes in unused
 // cache slots cannot leak), with rows that see no key producing O = 0 and
-// LSE = -inf.  Tiles wholly outside the causal / window range or inactive in
-// the block mask are not loaded; a wavefront whose own 32 rows see nothing
-// in a loaded tile skips its math for that tile; tiles wholly inside a
-// wavefront's range skip the per-score mask.
+// LSE = -inf.  Tiles wholly outside the causal / window range are not
+// loaded; a wavefront whose own 32 rows see nothing in a loaded tile skips
+// its math for that tile; tiles wholly inside a wavefront's range skip the
+// per-score mask.
 //
-// FP8 E4M3 caches keep K as bytes: S^T = K Q^T runs on the FP8 product
-// v_mfma_scale_f32_32x32x64_f8f6f4 (64 dims a step, unit scales) against E4M3
-// queries as given, or against bf16 queries split into two E4M3 parts of
-// 16 q (hi + lo, about 2^-8 relative; each part times a K byte is exact), so
-// the K descale (and the query descale or 1/16) folds into the logit constant.
-//
-// K/V staging: bf16 K/V, FP8 K and the FP8 V of head-major pages go
-// global -> LDS with global_load_lds_dwordx4 (no registers), one or two
-// tiles ahead; FP8 V stays E4M3 there and its P.V fragments come from the
-// transposing byte read (ds_read_b64_tr_b8), converted exactly to bf16.  For
-// vectorised pages, and for E4M3 queries at D_v = 128, FP8 V is loaded to
-// registers one tile ahead instead (two LDS stages), converted exactly to
-// bf16 and written to LDS.  LDS rows are 16-byte-chunk XOR swizzled so that
-// the K reads and the transposed V reads are bank-conflict free.  Whole tiles take a fast addressing path (per-lane
-// 32-bit offsets from one scalar tile base); the sequence tail and pages
-// smaller than a tile take a clamped per-row path.
+// K/V staging: K and the V of head-major pages go global -> LDS with
+// global_load_lds_dwordx4 (no registers) as E4M3 bytes; the P.V fragments
+// of that V come from the transposing byte read (ds_read_b64_tr_b8),
+// converted exactly to bf16.  For vectorised pages, and for E4M3 queries at
+// D_v = 128, V is loaded to registers one tile ahead instead, converted
+// exactly to bf16 and written to LDS.  LDS rows are 16-byte-chunk XOR
+// swizzled so that the K reads and the transposed V reads are bank-conflict
+// free.  Whole tiles take a fast addressing path (per-lane 32-bit offsets
+// from one scalar tile base); the sequence tail and pages smaller than a
+// tile take a clamped per-row path.
 #include "fa_device.h"
 #include "fa_kernels.h"
 #include "fa_prefill_common.h"
@@ -301,7 +302,10 @@ __device__ __forceinline__ i32x8 cat8(i32x4 x, i32x4 y) {
 template <int DQK, int DV, bool FP8, bool PAGED, bool VEC, bool Q8, int MODS>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_prefill_kernel(const PrefillArgs a) {
-  static_assert(!VEC || (FP8 && PAGED), "vectorised pages hold FP8 K/V");
+  // bf16 K/V and the score mods are served by fa_prefill_bf16_kernel; the
+  // FP8 paged entry points reject mods
+  static_assert(FP8 && MODS == 0, "this kernel serves FP8 caches without score mods");
+  static_assert(!VEC || PAGED, "vectorised pages are a page format");
   static_assert(!Q8 || FP8, "E4M3 queries go with an FP8 cache");
   // FP8 V through registers for vectorised pages and for E4M3 queries at
   // D_v = 128; E4M3 in LDS otherwise (the faster of the two, measured)
@@ -310,9 +314,6 @@ void fa_prefill_kernel(const PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[T::kLds];
   char FA_LDS* lds = (char FA_LDS*)(lds_raw);
 
-  constexpr bool ALIBI = (MODS & kModAlibi) != 0;
-  constexpr bool SOFTCAP = (MODS & kModSoftcap) != 0;
-  constexpr bool ANYMOD = ALIBI || SOFTCAP;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -366,18 +367,16 @@ void fa_prefill_kernel(const PrefillArgs a) {
   if (hi_max < lo_min) t_end = t_begin - 1;
 
   // ---- per-lane query row and its Q fragments (B operand of S^T = K Q^T) ----
-  // bf16 K: eight dims per lane and 16-dim step.  FP8 K (E4M3 products, 64
-  // dims a step, 32 per lane): E4M3 queries as they are; bf16 queries as two
-  // E4M3 parts of 16 q (hi + lo), each multiplied exactly.
+  // FP8 K (E4M3 products, 64 dims a step, 32 per lane): E4M3 queries as they
+  // are; bf16 queries as two E4M3 parts of 2^e q (hi + lo, e per row), each
+  // multiplied exactly.
   const int qrow = q0 + wave * 32 + (lane & 31);
   const bool qvalid = qrow < sv.sq;
-  constexpr int kQf = FP8 ? 1 : DQK / 16;
-  constexpr int kQ8 = FP8 ? DQK / 64 : 1;
-  bf16x8 qf[kQf];
+  constexpr int kQ8 = DQK / 64;
   i32x8 qhi[kQ8], qlo[kQ8];
   float qinv = 1.0f;   // bf16 queries split into E4M3 parts: 2^-e of this row's split scale
   const int64_t qrow_off = (sv.qstart + (qvalid ? qrow : 0)) * a.q_st + (int64_t)sv.h * a.q_sh;
-  if (FP8) {
+  {
     if (Q8) {
       const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.q) + qrow_off + (lane >> 5) * 32;
 #pragma unroll
@@ -412,14 +411,6 @@ void fa_prefill_kernel(const PrefillArgs a) {
         qlo[s] = i32x8{l[0][0], l[0][1], l[1][0], l[1][1], l[2][0], l[2][1], l[3][0], l[3][1]};
       }
     }
-  } else {
-    const bf16* qp = reinterpret_cast<const bf16*>(a.q) + qrow_off + (lane >> 5) * 8;
-#pragma unroll
-    for (int s = 0; s < kQf; ++s) {
-      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + s * 16);
-      if (!qvalid) v = bf16x8{};
-      qf[s] = v;
-    }
   }
   const int my_lo = row_lo(qrow), my_hi = row_hi(qrow);
   const unsigned my_cnt = (unsigned)max(my_hi - my_lo + 1, 0);
@@ -431,18 +422,12 @@ void fa_prefill_kernel(const PrefillArgs a) {
   const int wave_lo_max = row_lo(wq1), wave_hi_min = row_hi(wq0);
   const int my_half = wave * 32 / kMaskRows;
 
-  float kdesc = 1.0f, vdesc = 1.0f;
-  if (FP8) {
-    kdesc = *a.k_descale;
-    vdesc = *a.v_descale;
-    if (Q8) kdesc *= *a.q_descale;       // both descales scale every logit
-    else kdesc *= qinv;                  // the split carries 2^e q
-  }
+  float kdesc = *a.k_descale;
+  const float vdesc = *a.v_descale;
+  if (Q8) kdesc *= *a.q_descale;         // both descales scale every logit
+  else kdesc *= qinv;                    // the split carries 2^e q
   // C: multiplier from the raw MFMA dot product to log2-domain scaled logits
-  const float C = ANYMOD ? 1.0f : a.qk_scale * kLog2e * kdesc;
-  const float raw_scale = a.qk_scale * kdesc;      // raw dot -> natural scaled logit
-  const float cap = a.softcap, inv_cap = SOFTCAP ? 1.0f / a.softcap : 0.0f;
-  const int ip = qrow + delta;
+  const float C = a.qk_scale * kLog2e * kdesc;
   const int lane_key = (lane >> 5) * 4;            // key offset of this lane's S^T registers
 
   f32x16 oacc[DV / 32];
@@ -462,42 +447,28 @@ void fa_prefill_kernel(const PrefillArgs a) {
     return t;
   };
 
-  const int64_t kpg = a.k_pg, vpg = a.v_pg;
+  const int64_t vpg = a.v_pg;
   const bool small_pages = PAGED && a.page_shift < 6;
   auto fast_tile = [&](int k0) { return k0 + BN <= sv.skv && !small_pages; };
 
-  Bf16Stager<DQK, PAGED> kdma;
-  Bf16Stager<DV, PAGED> vdma;
   Fp8KDma<DQK, VEC> k8;
   Fp8VDma<DV> v8d;
   Fp8Stager<DV, PAGED> v8r;
   Fp8VecV<DV> vv8;
-  constexpr int kDmaPerTile = FP8 ? Fp8KDma<DQK, VEC>::kPerWave + (VREG ? 0 : Fp8VDma<DV>::kPerWave)
-                                  : Bf16Stager<DQK, PAGED>::kPerWave + Bf16Stager<DV, PAGED>::kPerWave;
-  if (FP8) {
-    k8.init(a.page_shift, wave, lane);
-    if (!VREG) v8d.init(wave, lane);
-    else if (!VEC) v8r.init(a.v_st, tid);
-  } else {
-    kdma.init(a.k_st, wave, lane);
-    vdma.init(a.v_st, wave, lane);
-  }
+  constexpr int kDmaPerTile = Fp8KDma<DQK, VEC>::kPerWave + (VREG ? 0 : Fp8VDma<DV>::kPerWave);
+  k8.init(a.page_shift, wave, lane);
+  if (!VREG) v8d.init(wave, lane);
+  else if (!VEC) v8r.init(a.v_st, tid);
   auto stage_ptr = [&](int i) { return lds + i * T::kStage; };
   // K (and V unless VREG) by DMA straight into the stage, FP8 as E4M3
   // bytes; VREG: V into registers, converted when stored (fp8_store)
   auto issue = [&](int t, char FA_LDS* st) {
     const int k0 = t * BN;
     const bool fast = fast_tile(k0);
-    if (FP8) {
-      k8.issue(a, sv, reinterpret_cast<const uint8_t*>(a.k), k0, fast, st, wave, lane);
-      if (!VREG) v8d.issue(a, sv, reinterpret_cast<const uint8_t*>(a.v), k0, fast, st + T::kTileK, wave, lane);
-      else if (VEC) vv8.load(a, sv, reinterpret_cast<const uint8_t*>(a.v), k0, fast, tid);
-      else v8r.load(a, sv, reinterpret_cast<const uint8_t*>(a.v), a.v_st, a.v_sh, vpg, k0, fast, tid);
-    } else {
-      kdma.issue(a, sv, reinterpret_cast<const bf16*>(a.k), a.k_st, a.k_sh, kpg, st, k0, fast, wave, lane);
-      vdma.issue(a, sv, reinterpret_cast<const bf16*>(a.v), a.v_st, a.v_sh, vpg, st + T::kTileK, k0, fast, wave,
-                 lane);
-    }
+    k8.issue(a, sv, reinterpret_cast<const uint8_t*>(a.k), k0, fast, st, wave, lane);
+    if (!VREG) v8d.issue(a, sv, reinterpret_cast<const uint8_t*>(a.v), k0, fast, st + T::kTileK, wave, lane);
+    else if (VEC) vv8.load(a, sv, reinterpret_cast<const uint8_t*>(a.v), k0, fast, tid);
+    else v8r.load(a, sv, reinterpret_cast<const uint8_t*>(a.v), a.v_st, a.v_sh, vpg, k0, fast, tid);
   };
 
   // VREG: the registers -> bf16 in the stage, then wait for the K copies
@@ -546,7 +517,7 @@ void fa_prefill_kernel(const PrefillArgs a) {
       // two independent accumulation chains (key blocks 0 and 1); the K
       // fragments of step s+1 are read while the products of step s run
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
-      if constexpr (FP8) {
+      {
         // K rows as E4M3: lane holds dims 64 s + 32 (lane/32) + [0, 32) of
         // key row lane%32 of each block, two 16-byte chunks
         const int r = lane & 31;                       // swz8(r) == swz8(r + 32)
@@ -562,7 +533,7 @@ void fa_prefill_kernel(const PrefillArgs a) {
         // once that block's last product of this step has been issued
         constexpr int S = DQK / 64;
         i32x8 ka = kread(0, 0), kb = kread(0, 1);
-#pragma unroll
+  #pragma unroll
         for (int s = 0; s < S; ++s) {
           sacc[0] = mfma32_fp8(ka, qhi[s], sacc[0]);
           sacc[1] = mfma32_fp8(kb, qhi[s], sacc[1]);
@@ -583,46 +554,8 @@ void fa_prefill_kernel(const PrefillArgs a) {
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-      } else {
-        const int r = lane & 31;                       // swz(r) == swz(r + 32)
-        const char FA_LDS* rowp = cur + r * T::kRowK;
-        const int sw = swz<T::kRowK>(r);
-        auto kread = [&](int s, int kb) {
-          return lds_read_b128(rowp + kb * 32 * T::kRowK + (((s * 2 + (lane >> 5)) ^ sw) << 4));
-        };
-        bf16x8 kc0 = kread(0, 0), kc1 = kread(0, 1);
-#pragma unroll
-        for (int s = 0; s < DQK / 16; ++s) {
-          bf16x8 kn0, kn1;
-          if (s + 1 < DQK / 16) {
-            kn0 = kread(s + 1, 0);
-            kn1 = kread(s + 1, 1);
-          }
-          // keep the reads of step s+1 ahead of the products of step s
-          __builtin_amdgcn_sched_barrier(0);
-          sacc[0] = mfma32(kc0, qf[s], sacc[0]);
-          sacc[1] = mfma32(kc1, qf[s], sacc[1]);
-          kc0 = kn0;
-          kc1 = kn1;
-        }
       }
 
-      // ---------------- score mods (log2 domain) ----------------
-      if (ANYMOD) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float x = sacc[kb][i] * raw_scale;
-            if (SOFTCAP) x = cap * tanh_fast(x * inv_cap);
-            if (ALIBI) {
-              const int j = k0 + kb * 32 + (i >> 2) * 8 + lane_key + (i & 3);
-              x -= a.alibi_slope * fabsf((float)(ip - j));
-            }
-            sacc[kb][i] = x * kLog2e;
-          }
-        }
-      }
       // ---------------- masks: only tiles that straddle a row's key interval ----------------
       const bool need_mask = !(k0 >= wave_lo_max && k0 + BN - 1 <= wave_hi_min);
       if (need_mask) {
