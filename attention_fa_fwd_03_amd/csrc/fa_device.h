@@ -78,13 +78,6 @@ __device__ __forceinline__ float sum_pair32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Hyperbolic tangent from the exponential: tanh(x) = 1 - 2 / (1 + e^{2x}).
-// Saturates correctly at +-1 (e^{2x} -> inf gives 1, -> 0 gives -1).
-__device__ __forceinline__ float tanh_fast(float x) {
-  float e = exp2_hw(x * (2.0f * kLog2e));
-  return 1.0f - 2.0f * rcp_hw(1.0f + e);
-}
-
 __device__ __forceinline__ bf16x8 lds_read_b128(const char FA_LDS* p) {
   return *reinterpret_cast<const bf16x8 FA_LDS*>(p);
 }
