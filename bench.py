@@ -349,8 +349,8 @@ def _affinity() -> int:
 
 
 def _cores() -> int:
-    """Oracle worker threads: the affinity cores, at most 16 (the GPU machine's
-    CPU share for one GPU)."""
+    """Oracle worker threads: the affinity cores, at most 16 (a host's CPU
+    share for one GPU)."""
     return max(1, min(_affinity(), 16))
 
 
@@ -503,7 +503,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(the path shards by sequence and head; see DESIGN.md)", file=sys.stderr)
+              "(sequences and heads are independent units that would shard across GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import torch
