@@ -563,7 +563,7 @@ def main():
             sec.append({"workload": sm["config"]["workload"], "value": sm["value"], "unit": sm["unit"],
                         "dtype": sm["dtype"], "roofline": {k: sm["roofline"][k] for k in
                                                            ("bound", "achieved", "peak", "unit", "frac",
-                                                            "kernel_ms")}})
+                                                            "traffic", "kernel_ms")}})
             torch.cuda.empty_cache()
         line["secondary"] = sec
         line["latency"] = call_latency(torch, synth, fa)
