@@ -18,6 +18,9 @@ from tests.test_gpu_parity import (FLEX_CASES, _dense_run, _oracle_mods, _paged_
 
 pytestmark = pytest.mark.gpu
 
+if torch.cuda.is_available():
+    import attention_fa_fwd_03_amd as fa
+
 DEV = "cuda"
 
 
@@ -152,3 +155,31 @@ def test_softcap_saturation(D, qscale):
         o_ref, l_ref = oracle.attention_dense(f64(d["q"]), f64(d["k"]), f64(d["v"]), dict(mods))
         compare(o.permute(0, 2, 1, 3), lse, o_ref.transpose(0, 2, 1, 3), l_ref, TOL_O_BF16,
                 what=f"softcap saturation D{D} x{qscale} {sorted(mods)}")
+
+
+# ----------------------------------------------------------------------------- launch stream
+def test_calls_follow_the_current_stream():
+    """The binding launches on torch's current stream (read as a raw handle)
+    or on an explicit stream: queued behind a slow producer of Q on a side
+    stream (default priority), the result is the oracle's only if the
+    attention kernel ran after the producer on that same stream."""
+    d = synth.make_dense(1, 256, 256, 2, 2, 128, 128, seed=671)
+    k, v = d["k"].to(DEV), d["v"].to(DEV)
+    o_ref, l_ref = oracle.attention_dense(f64(d["q"]), f64(d["k"]), f64(d["v"]), {})
+    side = torch.cuda.Stream()
+    for how in ("current", "explicit"):
+        q = torch.zeros_like(d["q"], device=DEV)
+        o = torch.full((1, 256, 2, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+        lse = torch.full((1, 2, 256), float("nan"), dtype=torch.float32, device=DEV)
+        big = torch.randn(4096, 4096, device=DEV)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            for _ in range(8):          # keep the side stream busy before Q is written
+                big = big @ big / 64.0
+            q.copy_(d["q"].to(DEV, non_blocking=True))
+            if how == "current":
+                fa.fa_fwd_dense(q, k, v, o, lse)
+        if how == "explicit":
+            fa.fa_fwd_dense(q, k, v, o, lse, stream=side)
+        side.synchronize()
+        compare(o.permute(0, 2, 1, 3), lse, o_ref.transpose(0, 2, 1, 3), l_ref, TOL_O_BF16, what=f"stream {how}")
