@@ -183,3 +183,47 @@ def test_calls_follow_the_current_stream():
             fa.fa_fwd_dense(q, k, v, o, lse, stream=side)
         side.synchronize()
         compare(o.permute(0, 2, 1, 3), lse, o_ref.transpose(0, 2, 1, 3), l_ref, TOL_O_BF16, what=f"stream {how}")
+
+
+# ----------------------------------------------------------------------------- seeded sweep
+def _sweep_case(i):
+    """Case i of the sweep: seeded lengths (zero, short, tile-straddling),
+    head dims, GQA ratio and mods, chosen by a generator of its own."""
+    g = torch.Generator().manual_seed(7000 + i)
+    ri = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=g))
+    B = ri(1, 4)
+    cross = ri(0, 1) == 1
+    lq = [ri(0, 260) for _ in range(B)]
+    lk = [ri(0, 300) if cross else n for n in lq]
+    if B > 1 and ri(0, 2) == 0:
+        z = ri(0, B - 1)
+        lq[z] = 0
+        if not cross:
+            lk[z] = 0
+    D = (64, 128)[ri(0, 1)]
+    Hkv = ri(1, 2)
+    Hq = Hkv * (1, 2, 4)[ri(0, 2)]
+    mods = {}
+    if ri(0, 1):
+        mods["causal"] = True
+    kind = ri(0, 4)
+    if kind == 1:
+        mods["window"] = (ri(0, 80), ri(0, 40))
+    elif kind == 2:
+        mods["alibi_slope"] = 0.05 * ri(1, 6)
+    elif kind == 3:
+        mods["softcap"] = float(ri(2, 30))
+    elif kind == 4:
+        mods["alibi_slope"], mods["softcap"] = 0.1, 8.0
+    return lq, lk, Hq, Hkv, D, mods
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_seeded_varlen_sweep(i):
+    """24 seeded small varlen problems across lengths, head dims, GQA and
+    mods, each against the oracle."""
+    lq, lk, Hq, Hkv, D, mods = _sweep_case(i)
+    d = synth.make_varlen(lq, lk, Hq, Hkv, D, D, seed=7100 + i)
+    o, lse = _varlen_run(d, mods, D)
+    o_ref, l_ref = oracle.attention_varlen(f64(d["q"]), f64(d["k"]), f64(d["v"]), d["cu_q"], d["cu_k"], dict(mods))
+    _cmp_packed(o, lse, o_ref, l_ref, TOL_O_BF16, f"sweep {i}: lq={lq} lk={lk} Hq={Hq} Hkv={Hkv} D={D} {mods}")
