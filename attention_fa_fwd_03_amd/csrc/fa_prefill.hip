@@ -703,20 +703,13 @@ void fa_prefill_kernel(const PrefillArgs a) {
   const float l_tot = sum_pair32(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float osc = inv * vdesc;
+  // every wavefront is done with the stages (and no copy is in flight)
+  // after this barrier: O leaves through them
+  static_assert(4 * 32 * DV * 2 <= T::kLds, "the output rows fit in the stages");
+  __syncthreads();
+  store_o_rows<DV>(oacc, osc, lds + wave * 32 * (DV * 2),
+                   a.o + (sv.qstart + wq0) * a.o_st + (int64_t)sv.h * a.o_sh, a.o_st, sv.sq - wq0, lane);
   if (qvalid) {
-    bf16* op = a.o + (sv.qstart + qrow) * a.o_st + (int64_t)sv.h * a.o_sh + (lane >> 5) * 4;
-#pragma unroll
-    for (int d = 0; d < DV / 32; ++d) {
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        bf16x4 w;
-        w[0] = (bf16)(oacc[d][gi * 4 + 0] * osc);
-        w[1] = (bf16)(oacc[d][gi * 4 + 1] * osc);
-        w[2] = (bf16)(oacc[d][gi * 4 + 2] * osc);
-        w[3] = (bf16)(oacc[d][gi * 4 + 3] * osc);
-        *reinterpret_cast<bf16x4*>(op + d * 32 + gi * 8) = w;
-      }
-    }
     if (lane < 32) {
       const float lse = l_tot > 0.0f ? (m_run + log2_hw(l_tot)) * kLn2 : -INFINITY;
       int64_t li;

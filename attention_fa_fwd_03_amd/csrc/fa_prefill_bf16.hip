@@ -419,43 +419,10 @@ void fa_prefill_bf16_kernel(const PrefillArgs a) {
   // ---------------- epilogue ----------------
   const float l_tot = sum_pair32(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  // O leaves through LDS so that every store writes whole rows: this
-  // wavefront's 32 x D tile goes row-major into its quarter of the K ring,
-  // which is free here (every wavefront is past its last barrier, no copy is
-  // in flight and K is not read again), and comes back 16 bytes per lane.
-  // Chunk c of row r sits at c ^ osw(r); rows 16-31 also swap the two 8-byte
-  // halves of each chunk, so that the 32 rows that half a wavefront writes
-  // at one chunk fill all 64 banks.
-  constexpr int kChunks = D / 8;               // 16-byte chunks per row
-  constexpr int kRowsPer = 64 / kChunks;       // rows per read-back instruction
-  auto osw = [](int r) { return kChunks == 16 ? (r & 15) : ((r >> 1) & 7); };
-  char FA_LDS* ot = lds + wave * 32 * kRow;
-  {
-    const int r = lane & 31;
-    char FA_LDS* rowp = ot + r * kRow + (((lane >> 5) ^ (r >> 4)) << 3);
-#pragma unroll
-    for (int d = 0; d < ND; ++d)
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        bf16x4 w;
-        w[0] = (bf16)(oacc[d][gi * 4 + 0] * inv);
-        w[1] = (bf16)(oacc[d][gi * 4 + 1] * inv);
-        w[2] = (bf16)(oacc[d][gi * 4 + 2] * inv);
-        w[3] = (bf16)(oacc[d][gi * 4 + 3] * inv);
-        *reinterpret_cast<bf16x4 FA_LDS*>(rowp + (((d * 4 + gi) ^ osw(r)) << 4)) = w;
-      }
-  }
-  {
-    const int c = lane % kChunks;
-    bf16* op = a.o + (sv.qstart + wq0) * a.o_st + (int64_t)sv.h * a.o_sh + c * 8;
-#pragma unroll
-    for (int i = 0; i < 32 / kRowsPer; ++i) {
-      const int r = i * kRowsPer + lane / kChunks;
-      bf16x8 v = *reinterpret_cast<const bf16x8 FA_LDS*>(ot + r * kRow + ((c ^ osw(r)) << 4));
-      if (i * kRowsPer >= 16) v = __builtin_shufflevector(v, v, 4, 5, 6, 7, 0, 1, 2, 3);
-      if (wq0 + r < sv.sq) *reinterpret_cast<bf16x8*>(op + r * a.o_st) = v;
-    }
-  }
+  // the K ring is free here: every wavefront is past its last barrier, no
+  // copy is in flight and K is not read again
+  store_o_rows<D>(oacc, inv, lds + wave * 32 * kRow,
+                  a.o + (sv.qstart + wq0) * a.o_st + (int64_t)sv.h * a.o_sh, a.o_st, sv.sq - wq0, lane);
   if (qvalid && lane < 32) {
     const float lse = l_tot > 0.0f ? (m_run + log2_hw(l_tot)) * kLn2 : -INFINITY;
     int64_t li;

@@ -244,4 +244,50 @@ struct MaskBits {
   }
 };
 
+// Output rows of one wavefront: the 32 x D tile held as O^T accumulators
+// (lane l: row l % 32, columns 32 d + 8 g + 4 (l / 32) + [0, 4)) is scaled,
+// rounded to bf16 and written row-major into this wavefront's 32 x 2D bytes
+// of free LDS at ot, then read back 16 bytes per lane so that every global
+// store writes whole rows (non-temporal: O is not read again here, and the
+// stores retire sooner).  Chunk c of row r sits at c ^ osw(r) (inside its
+// aligned group of eight or sixteen chunks); rows 16-31 also swap the two
+// 8-byte halves of each chunk, so that the 32 rows that half a wavefront
+// writes at one chunk fill all 64 banks.  Rows >= nrows are not stored.
+template <int D>
+__device__ __forceinline__ void store_o_rows(const f32x16 (&oacc)[D / 32], float scale, char FA_LDS* ot,
+                                             bf16* o_row0, int64_t o_st, int nrows, int lane) {
+  constexpr int kRow = D * 2;
+  constexpr int kChunks = D / 8;               // 16-byte chunks per row
+  static_assert(kChunks == 8 || kChunks == 16 || kChunks == 24, "row widths of 64, 128 or 192 elements");
+  auto osw = [](int r) { return kChunks == 16 ? (r & 15) : ((r >> 1) & 7); };
+  {
+    const int r = lane & 31;
+    char FA_LDS* rowp = ot + r * kRow + (((lane >> 5) ^ (r >> 4)) << 3);
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        bf16x4 w;
+        w[0] = (bf16)(oacc[d][gi * 4 + 0] * scale);
+        w[1] = (bf16)(oacc[d][gi * 4 + 1] * scale);
+        w[2] = (bf16)(oacc[d][gi * 4 + 2] * scale);
+        w[3] = (bf16)(oacc[d][gi * 4 + 3] * scale);
+        *reinterpret_cast<bf16x4 FA_LDS*>(rowp + (((d * 4 + gi) ^ osw(r)) << 4)) = w;
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < 32 * kChunks / 64; ++i) {
+    const int f = i * 64 + lane;
+    const int r = f / kChunks, c = f % kChunks;
+    bf16x8 v = *reinterpret_cast<const bf16x8 FA_LDS*>(ot + r * kRow + ((c ^ osw(r)) << 4));
+    const bf16x8 sw = __builtin_shufflevector(v, v, 4, 5, 6, 7, 0, 1, 2, 3);
+    if constexpr (64 % kChunks == 0) {
+      if (i * (64 / kChunks) >= 16) v = sw;    // the rows of one read are all on one side
+    } else {
+      if (r >= 16) v = sw;
+    }
+    if (r < nrows) __builtin_nontemporal_store(v, reinterpret_cast<bf16x8*>(o_row0 + r * o_st + c * 8));
+  }
+}
+
 }  // namespace fa
