@@ -117,24 +117,35 @@ __device__ __forceinline__ int64_t tile_base(const PrefillArgs& a, const SeqView
 
 // Workgroup -> (sequence*head, query tile).  The grid is (B*Hq rounded up
 // to a multiple of 8) x (query tiles); workgroups are dispatched in linear
-// order (x fastest) and dealt round-robin to the 8 XCDs, so XCD x gets the
-// heads congruent to x mod 8 either way.
-//  - causal (query tiles of unequal cost): query-tile major, longest first,
-//    so the costliest tiles of every head start first (the tail is short);
-//    the few tiles of a head that run together read its K/V in step.  Within
-//    an XCD, workgroups are dealt to SEs and CUs round-robin in dispatch
-//    order whatever their cost, so the head of each slot rotates per level.
+// order i and dealt round-robin to the 8 XCDs, so XCD x = i mod 8 takes the
+// heads bh = 8 s + x (head slots s) whatever the order below.
+//  - causal (query tiles of unequal cost): an XCD takes its head slots in
+//    groups of 8 and, within a group, query-tile levels longest first, so
+//    the costliest tiles start first (the tail is short) while only a group's
+//    heads stream their K/V through the XCD's L2: the 8 longest tiles of a
+//    head start together and read its K/V in step.  On the varlen causal
+//    batch this fetches 39 % fewer bytes than levels over all heads (+1.2 %);
+//    the balance cost is under 1 % on most batch shapes.  Workgroups are
+//    dealt to SEs and CUs round-robin in dispatch order whatever their cost,
+//    so the head of each slot rotates per level.
 //  - otherwise (equal cost): head major, all query tiles of one head in a
 //    row, so the workgroups that read the same K/V share one XCD's L2.
 __device__ __forceinline__ void wg_tile(bool causal, int& bh, int& qt) {
   const int gx = (int)gridDim.x, gy = (int)gridDim.y;
   if (causal) {
-    // the head rotates by one XCD slot per query-tile level: workgroups go to
-    // CUs round-robin in dispatch order, so without the rotation a CU would
-    // meet the same (sequence, head) at every level it serves and inherit
-    // that sequence's length as its load
-    bh = ((int)blockIdx.x + 8 * (int)blockIdx.y) % gx;
-    qt = gy - 1 - (int)blockIdx.y;
+    // k-th workgroup of XCD x: group g of (up to) G head slots, level y
+    // within it, and the slot rotated by one per level (without the rotation
+    // a CU would meet the same (sequence, head) at every level it serves and
+    // inherit that sequence's length as its load)
+    constexpr int G = 8;
+    const int i = (int)blockIdx.y * gx + (int)blockIdx.x;
+    const int x = i & 7, k = i >> 3;
+    const int g = k / (G * gy);
+    const int gs = min(G, (gx >> 3) - g * G);
+    const int rem = k - g * G * gy;
+    const int y = rem / gs;
+    bh = (g * G + (rem % gs + y) % gs) * 8 + x;
+    qt = gy - 1 - y;
     return;
   }
   const int i = (int)blockIdx.y * gx + (int)blockIdx.x;
