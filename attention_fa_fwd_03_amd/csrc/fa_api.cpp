@@ -407,8 +407,6 @@ int paged_impl(const fa_paged_opts* opts, const void* q, const void* k_cache, co
   Mods m;
   if ((rc = read_mods(mods, d_qk, max_seqlen_q, max_seqlen_k, &m))) return rc;
   const bool fp8 = kv_dtype == FA_FP8_E4M3;
-  if (fp8 && (m.flags & (FA_ALIBI | FA_SOFTCAP | FA_BLOCK_MASK)))
-    return fail(FA_ERR_UNSUPPORTED, "FP8 paged caches support FA_CAUSAL and FA_WINDOW only");
   const bool decode = uses_decode(max_seqlen_q, Hq, Hkv, d_qk, d_v, kv_dtype, page_size);
   if (!decode && !prefill_dims_built(d_qk, d_v, fp8, true))
     return fail(FA_ERR_UNSUPPORTED, "paged head dims (%lld, %lld) with kv_dtype %d not built", (long long)d_qk,
@@ -498,6 +496,13 @@ int paged_impl(const fa_paged_opts* opts, const void* q, const void* k_cache, co
     d.causal = (m.flags & FA_CAUSAL) ? 1 : 0;
     d.win_left = (m.flags & FA_WINDOW) ? clamp_i32(m.wl) : -1;
     d.win_right = (m.flags & FA_WINDOW) ? clamp_i32(m.wr) : -1;
+    d.alibi_slope = (m.flags & FA_ALIBI) ? m.slope : 0.0f;
+    d.softcap = (m.flags & FA_SOFTCAP) ? m.cap : 0.0f;
+    d.bmask = (m.flags & FA_BLOCK_MASK) ? m.bm : nullptr;
+    d.bm_bq = (int)m.bq;
+    d.bm_bk = (int)m.bk;
+    d.bm_nqb = (int)m.nqb;
+    d.bm_nkb = (int)m.nkb;
     bool supported = false;
     hipError_t e = fa::decode_dispatch(pl, d, (int)d_qk, (int)d_v, fp8, vec, q8, st, &supported);
     if (!supported) return fail(FA_ERR_UNSUPPORTED, "no decode kernel for (%lld, %lld)", (long long)d_qk, (long long)d_v);
@@ -542,7 +547,7 @@ int paged_impl(const fa_paged_opts* opts, const void* q, const void* k_cache, co
   a.page_shift = shift;
   a.num_pages = (int)num_pages;
   fill_mods(a, m);
-  return launch_prefill(a, d_qk, d_v, fp8, true, vec, fp8 ? 0 : mod_bits(m), B, Hq, max_seqlen_q, st);
+  return launch_prefill(a, d_qk, d_v, fp8, true, vec, mod_bits(m), B, Hq, max_seqlen_q, st);
 }
 
 }  // namespace

@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void fa_decode_plan_kernel(const DecodePlanArg
 // worker that owns tile i of T in a split over W workers
 __device__ __forceinline__ int worker_of(int64_t i, int64_t T, int W) { return (int)(((i + 1) * W - 1) / T); }
 
-template <int DQK, int DV, int NRB, int NBUF, bool VEC, bool Q8>
+template <int DQK, int DV, int NRB, int NBUF, bool VEC, bool Q8, bool MODS>
 __global__ __launch_bounds__(kDecWaves * 64)
 __attribute__((amdgpu_waves_per_eu((NBUF >= 3 || DV > 128) ? 1 : (NRB == 1 && NBUF == 1 ? 3 : 2))))
 void fa_decode_kernel(const DecodeArgs a) {
@@ -239,8 +239,9 @@ void fa_decode_kernel(const DecodeArgs a) {
 
     // rows of this lane: row block rb holds rows rb*16 + lane%16
     bool rvalid[NRB];
-    int hq[NRB], my_lo[NRB], my_hi[NRB];
+    int hq[NRB], my_lo[NRB], my_hi[NRB], ipos[NRB];
     int64_t tok[NRB];
+    const uint8_t* bmrow[NRB];   // block-mask row of each row block (null: no mask)
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const int r = rb * 16 + (lane & 15);
@@ -249,6 +250,12 @@ void fa_decode_kernel(const DecodeArgs a) {
       hq[rb] = g * a.group + (rvalid[rb] ? r % a.group : 0);
       tok[rb] = qs + qi;
       const int ip = qi + delta;
+      ipos[rb] = ip;
+      // (mask indices are clamped / bounded like the prefill's: a query or
+      // key block past the mask's extent reads as inactive or as its last row)
+      bmrow[rb] = (MODS && a.bmask) ? a.bmask + (((int64_t)b * a.Hq + hq[rb]) * a.bm_nqb + min(qi / a.bm_bq, a.bm_nqb - 1)) *
+                                          a.bm_nkb
+                          : nullptr;
       int hi = k_hi - 1, lo = k_lo;
       if (a.causal) hi = min(hi, ip);
       if (a.win_right >= 0) hi = min(hi, ip + a.win_right);
@@ -393,6 +400,21 @@ void fa_decode_kernel(const DecodeArgs a) {
         }
       }
     }
+    // Score mods (the MODS variant; which ones is a runtime, uniform choice):
+    // the scores are converted to log2-domain logits explicitly and C
+    // becomes 1.  Soft-cap: c tanh(u / c) log2(e) =
+    // c' - 2 c' / (1 + 2^(k s)) for the raw dot product s (u = s C / log2(e),
+    // k = 2 C / c, c' = c log2(e)); ALiBi: - slope log2(e) |i' - j|.
+    const bool mods_on = MODS && (a.alibi_slope != 0.0f || a.softcap > 0.0f);
+    const bool capped = MODS && a.softcap > 0.0f;
+    const float cap_c = capped ? a.softcap * kLog2e : 0.0f, slope2 = a.alibi_slope * kLog2e;
+    float lin[NRB], cap_k[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      lin[rb] = C[rb];
+      cap_k[rb] = capped ? 2.0f * C[rb] / a.softcap : 0.0f;
+      if (mods_on) C[rb] = 1.0f;
+    }
 #pragma unroll
     for (int j = 0; j < NBUF; ++j) load_tile(min(j, last), kbuf[j], vbuf[j]);
 
@@ -431,6 +453,21 @@ void fa_decode_kernel(const DecodeArgs a) {
       }
       if (refill) load_tile(min(t + NBUF, last), kb, vb);
 
+      // block-mask activity of this tile for each row block (a 32-key tile
+      // lies in one mask block); read before the products so that they
+      // cover the load
+      const int k0 = k_lo + t * kDecKT;
+      bool act[NRB];
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) act[rb] = true;
+      if (MODS && a.bmask) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const int kb = k0 / a.bm_bk;
+          act[rb] = kb < a.bm_nkb && bmrow[rb][kb] != 0;
+        }
+      }
+
       // ---- S^T = K Q^T ----  (fragment n = (kh, st); each read runs two
       // fragments ahead of its products, one chunk per fragment)
       constexpr int kNK = 2 * kSteps;
@@ -457,11 +494,29 @@ void fa_decode_kernel(const DecodeArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      // ---- masks and online softmax, per row block ----
-      const int k0 = k_lo + t * kDecKT;
+      // ---- score mods, masks and online softmax, per row block ----
       bf16x8 pf[NRB];
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
+        if (mods_on) {
+          // i' - j of register (kh, i) is d0 - (16 kh + i), exact in fp32
+          // below 2^24 keys apart
+          const float d0 = (float)(ipos[rb] - k0 - 4 * kgrp);
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float x = sacc[rb][kh][i];
+              x = capped ? fmaf(rcp_hw(1.0f + exp2_hw(x * cap_k[rb])), -2.0f * cap_c, cap_c) : x * lin[rb];
+              sacc[rb][kh][i] = fmaf(-slope2, fabsf(d0 - (float)(kh * 16 + i)), x);
+            }
+        }
+        if (MODS && a.bmask) {
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sacc[rb][kh][i] = act[rb] ? sacc[rb][kh][i] : -INFINITY;
+        }
         if (k0 < all_lo || k0 + kDecKT - 1 > all_hi) {
           // keeps this a real branch: selects would otherwise be speculated onto every tile
           asm volatile("" ::);
@@ -643,11 +698,19 @@ hipError_t decode_dispatch(const DecodePlanArgs& plan, const DecodeArgs& a, int 
   if (e != hipSuccess) return e;
   const dim3 grid((a.n_workers + kDecWaves - 1) / kDecWaves);
   const bool two = a.slot_rows > 16;
+  // score mods and block masks: one variant, with two row blocks (any unit)
+  const bool mods = a.alibi_slope != 0.0f || a.softcap > 0.0f || a.bmask;
 #define FA_DEC(DQ, DVV, VC, Q)                                                                           \
   if (dqk == DQ && dv == DVV && vec == VC && q8 == Q) {                                                    \
-    if (two) hipLaunchKernelGGL((fa_decode_kernel<DQ, DVV, 2, (DVV > 128 ? 2 : 1), VC, Q>), grid, dim3(kDecWaves * 64), 0, \
-                                stream, a);                                                                \
-    else hipLaunchKernelGGL((fa_decode_kernel<DQ, DVV, 1, 2, VC, Q>), grid, dim3(kDecWaves * 64), 0, stream, a);  \
+    if (mods)                                                                                              \
+      hipLaunchKernelGGL((fa_decode_kernel<DQ, DVV, 2, (DVV > 128 ? 2 : 1), VC, Q, true>), grid,           \
+                         dim3(kDecWaves * 64), 0, stream, a);                                              \
+    else if (two)                                                                                          \
+      hipLaunchKernelGGL((fa_decode_kernel<DQ, DVV, 2, (DVV > 128 ? 2 : 1), VC, Q, false>), grid,          \
+                         dim3(kDecWaves * 64), 0, stream, a);                                              \
+    else                                                                                                   \
+      hipLaunchKernelGGL((fa_decode_kernel<DQ, DVV, 1, 2, VC, Q, false>), grid, dim3(kDecWaves * 64), 0,   \
+                         stream, a);                                                                       \
     return hipGetLastError();                                                                              \
   }
 #define FA_DEC2(DQ, DVV, VC) FA_DEC(DQ, DVV, VC, false) FA_DEC(DQ, DVV, VC, true)

@@ -75,6 +75,10 @@ struct DecodeArgs {
   float qk_scale;
   int causal;
   int win_left, win_right;
+  float alibi_slope;           // 0: none
+  float softcap;               // <= 0: none
+  const uint8_t* bmask;        // [B*Hq, bm_nqb, bm_nkb] or null (bm_bk is a multiple of 64)
+  int bm_bq, bm_bk, bm_nqb, bm_nkb;
 };
 
 struct DecodePlanArgs {

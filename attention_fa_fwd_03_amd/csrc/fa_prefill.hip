@@ -1,6 +1,8 @@
 // Fused attention forward over FP8 E4M3 paged caches (head-major or
-// vectorised pages) for gfx950.  bf16 K/V and the score mods are served by
-// the software-pipelined kernel in fa_prefill_bf16.hip.
+// vectorised pages) for gfx950.  bf16 K/V are served by the
+// software-pipelined kernel in fa_prefill_bf16.hip.  Score mods (ALiBi,
+// soft-cap) run in one variant of this kernel; block masks and windows are
+// runtime arguments of every variant.
 //
 // One workgroup = 4 wavefronts = 128 query rows of one (sequence, q-head);
 // each wavefront owns 32 query rows.  A workgroup keeps its LDS ring within
@@ -302,9 +304,11 @@ __device__ __forceinline__ i32x8 cat8(i32x4 x, i32x4 y) {
 template <int DQK, int DV, bool FP8, bool PAGED, bool VEC, bool Q8, int MODS>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_prefill_kernel(const PrefillArgs a) {
-  // bf16 K/V and the score mods are served by fa_prefill_bf16_kernel; the
-  // FP8 paged entry points reject mods
-  static_assert(FP8 && MODS == 0, "this kernel serves FP8 caches without score mods");
+  // bf16 K/V go to fa_prefill_bf16_kernel.  Score mods come in one variant
+  // (MODS = both bits): ALiBi is always applied there (slope 0 is the
+  // identity) and the soft-cap when softcap > 0, a uniform branch per tile.
+  static_assert(FP8 && (MODS == 0 || MODS == (kModAlibi | kModSoftcap)), "FP8 caches: no mods or the mods variant");
+  constexpr bool ANYMOD = MODS != 0;
   static_assert(!VEC || PAGED, "vectorised pages are a page format");
   static_assert(!Q8 || FP8, "E4M3 queries go with an FP8 cache");
   // FP8 V through registers for vectorised pages and for E4M3 queries at
@@ -427,7 +431,18 @@ void fa_prefill_kernel(const PrefillArgs a) {
   if (Q8) kdesc *= *a.q_descale;         // both descales scale every logit
   else kdesc *= qinv;                    // the split carries 2^e q
   // C: multiplier from the raw MFMA dot product to log2-domain scaled logits
-  const float C = a.qk_scale * kLog2e * kdesc;
+  // (with mods the scores are converted explicitly and C is 1)
+  const float lin2 = a.qk_scale * kLog2e * kdesc;
+  const float C = ANYMOD ? 1.0f : lin2;
+  // Mods in the log2 domain with every constant folded (the K descale and
+  // the query's split scale included).  Soft-cap: c tanh(u / c) log2(e) =
+  // c' - 2 c' / (1 + 2^(k s)) for the raw dot product s, u = s scale kdesc,
+  // k = 2 scale kdesc log2(e) / c and c' = c log2(e); ALiBi:
+  // - slope log2(e) |i' - j| by one FMA.
+  const bool capped = ANYMOD && a.softcap > 0.0f;
+  const float cap_k = capped ? 2.0f * lin2 / a.softcap : 0.0f;
+  const float cap_c = capped ? a.softcap * kLog2e : 0.0f;
+  const float slope2 = ANYMOD ? a.alibi_slope * kLog2e : 0.0f;
   const int lane_key = (lane >> 5) * 4;            // key offset of this lane's S^T registers
 
   f32x16 oacc[DV / 32];
@@ -554,6 +569,30 @@ void fa_prefill_kernel(const PrefillArgs a) {
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+      }
+
+      // ---------------- score mods (log2-domain logits) ----------------
+      if (ANYMOD) {
+        if (capped) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              sacc[kb][i] = fmaf(rcp_hw(1.0f + exp2_hw(sacc[kb][i] * cap_k)), -2.0f * cap_c, cap_c);
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sacc[kb][i] *= lin2;
+        }
+        // i' - j of register (kb, i) is d0 - (32 kb + 8 (i/4) + i%4), exact in
+        // fp32 below 2^24 keys apart
+        const float d0 = (float)(qrow + delta - k0 - lane_key);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            sacc[kb][i] = fmaf(-slope2, fabsf(d0 - (float)(kb * 32 + (i >> 2) * 8 + (i & 3))), sacc[kb][i]);
       }
 
       // ---------------- masks: only tiles that straddle a row's key interval ----------------
@@ -731,7 +770,7 @@ static hipError_t launch_prefill(const PrefillArgs& a, int n_bh, int n_qtiles, h
 }
 
 // Instantiated shapes here: (192,128), (128,128) and (192,192) for FP8 E4M3
-// paged caches without score mods, head-major or vectorised pages.  bf16 K/V
+// paged caches, head-major or vectorised pages, without or with score mods.  bf16 K/V
 // go to the software-pipelined kernel (fa_prefill_bf16.hip).
 hipError_t prefill_dispatch(const PrefillArgs& a, int dqk, int dv, bool fp8, bool paged, bool vec, int mods,
                             int n_bh, int n_qtiles, hipStream_t stream, bool* supported) {
@@ -740,12 +779,14 @@ hipError_t prefill_dispatch(const PrefillArgs& a, int dqk, int dv, bool fp8, boo
 #define FA_CASE(DQ, DVV, F8, PG, VC, MD)                                                       \
   if (dqk == DQ && dv == DVV && fp8 == F8 && paged == PG && vec == VC && mods == MD)           \
     return launch_prefill<DQ, DVV, F8, PG, VC, MD>(a, n_bh, n_qtiles, stream);
-  FA_CASE(192, 128, true, true, false, 0)
-  FA_CASE(128, 128, true, true, false, 0)
-  FA_CASE(192, 128, true, true, true, 0)
-  FA_CASE(128, 128, true, true, true, 0)
-  FA_CASE(192, 192, true, true, false, 0)
-  FA_CASE(192, 192, true, true, true, 0)
+  // every score mod goes to the one mods variant
+  mods = mods ? (kModAlibi | kModSoftcap) : 0;
+  FA_CASE(192, 128, true, true, false, 0) FA_CASE(192, 128, true, true, false, 3)
+  FA_CASE(128, 128, true, true, false, 0) FA_CASE(128, 128, true, true, false, 3)
+  FA_CASE(192, 128, true, true, true, 0) FA_CASE(192, 128, true, true, true, 3)
+  FA_CASE(128, 128, true, true, true, 0) FA_CASE(128, 128, true, true, true, 3)
+  FA_CASE(192, 192, true, true, false, 0) FA_CASE(192, 192, true, true, false, 3)
+  FA_CASE(192, 192, true, true, true, 0) FA_CASE(192, 192, true, true, true, 3)
 #undef FA_CASE
   *supported = false;
   return hipSuccess;

@@ -127,8 +127,10 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  * page_size: a power of two in [1, 1024].
  * Built: FP8 (d_qk, d_v) in {(192, 128), (128, 128), (192, 192)} (192/192:
  * the V192 variant of the paged FP8 PR); bf16 (64, 64), (128, 128).
- * Mods: FP8 caches take FA_CAUSAL and FA_WINDOW (others: FA_ERR_UNSUPPORTED);
- * bf16 caches take every mod, as for fa_fwd_dense.
+ * Mods: every mod, as for fa_fwd_dense, with either cache type and on the
+ * decode path too (the flex page, part 4, applies its score mods and block
+ * sparsity to the forward in general).  A block mask's query blocks index
+ * the query's row i within its sequence, its key blocks the key index j.
  * bf16 queries against an FP8 cache enter the FP8 products as two E4M3
  * parts of 2^e q, e chosen per query row from its largest magnitude
  * (2^e amax in [128, 256)): any finite bf16 query row is representable, each

@@ -197,11 +197,27 @@ def test_paged_decode_workspace_must_not_overlap(target):
     assert rc == -1 and "overlap" in msg, (target, rc, msg)
 
 
-def test_paged_rejects_unsupported_mods():
+@pytest.mark.parametrize("mkw,code,frag", [
+    (dict(softcap=-1.0), -1, "softcap"),
+    (dict(alibi_slope=float("inf")), -1, "alibi_slope"),
+    (dict(block_mask="bq64"), -2, "multiples"),
+    (dict(block_mask="short"), -1, "does not cover"),
+])
+def test_paged_checks_mod_parameters(mkw, code, frag):
+    """FP8 paged calls take every score mod; their parameters are checked as
+    for the dense entry point, before any device work (every case here is
+    rejected, so no kernel is launched on the placeholder pointers)."""
     fa = _lib()
-    m = fa.Mods(alibi_slope=0.5).to_c()
+    bm = mkw.pop("block_mask", None)
+    m = fa.Mods(**mkw).to_c()
+    if bm is not None:
+        # the struct directly: the Python wrapper wants a device tensor
+        m.flags |= fa.FA_BLOCK_MASK
+        m.block_mask = FAKE * 12
+        m.mask_block_q, m.mask_block_k = (64, 64) if bm == "bq64" else (128, 64)
+        m.mask_nqb, m.mask_nkb = 1, 1   # "short": 1 key block cannot cover 100 keys
     rc, msg = _paged(mods=ctypes.byref(m))
-    assert rc == -2 and "FA_CAUSAL" in msg
+    assert rc == code and frag in msg, (rc, msg)
 
 
 def test_workspace_size_query():

@@ -1,8 +1,10 @@
 """GPU parity of exported paths beyond the main parity file: bf16 page caches
 (prefill, chunked prefill and single-query rows, page sizes 1 to 64, with
 and without score mods), score mods at D = 64, windows on the FP8 paged
-prefill, and bf16 queries far from unit scale against FP8 caches (the
-per-row power-of-two split of the queries).  Every call goes through the C
+prefill, score mods and block masks on FP8 paged caches (prefill and
+decode, every head-dim pair, both page formats, E4M3 queries), and bf16
+queries far from unit scale against FP8 caches (the per-row power-of-two
+split of the queries).  Every call goes through the C
 ABI; every result is compared with the fp64 oracle on the same inputs.
 """
 import math
@@ -13,8 +15,8 @@ import torch
 import oracle
 import synth
 from tests.helpers import TOL_O_BF16, TOL_O_FP8, compare, f64
-from tests.test_gpu_parity import (FLEX_CASES, _dense_run, _oracle_mods, _paged_ref, _paged_run, _paged_vec_run,
-                                   _varlen_run)
+from tests.test_gpu_parity import (FLEX_CASES, VEC_CASES, _dense_run, _oracle_mods, _paged_q8_run, _paged_ref,
+                                   _paged_run, _paged_vec_run, _varlen_run)
 
 pytestmark = pytest.mark.gpu
 
@@ -186,6 +188,78 @@ def test_calls_follow_the_current_stream():
 
 
 # ----------------------------------------------------------------------------- seeded sweep
+# ----------------------------------------------------------------------------- FP8 pages with score mods
+FP8_MODS = {
+    "alibi_causal": dict(causal=True, alibi_slope=0.0625),
+    "softcap": dict(softcap=20.0),
+    "alibi_softcap_causal": dict(causal=True, alibi_slope=0.0625, softcap=20.0),
+    "softcap_window": dict(window=(90, 5), softcap=15.0),
+    "bmask_causal": dict(causal=True, bmask=True),
+    "bmask_alibi": dict(alibi_slope=0.125, bmask=True),
+}
+
+
+def _fp8_mods(name, d, seed):
+    """The named mods for make_paged() data d; a block mask of 128 x 64
+    tiles (active with probability 0.5) where asked."""
+    m = dict(FP8_MODS[name])
+    if m.pop("bmask", False):
+        Hq = d["q"].shape[1]
+        B = len(d["lengths_k"])
+        nqb = max(1, math.ceil(max(d["lengths_q"]) / 128))
+        nkb = max(1, math.ceil(max(d["lengths_k"]) / 64))
+        m["block_mask"] = synth.bernoulli_block_mask(B * Hq, nqb, nkb, 0.5, seed=seed).to(DEV)
+        m["mask_block"] = (128, 64)
+    return m
+
+
+def _fp8_ref(d, m, q8=False):
+    kw = dict(q_descale=float(d["q_descale"])) if q8 else {}
+    return oracle.attention_paged(f64(d["q"]), f64(d["k_cache"]), f64(d["v_cache"]), d["cu_q"], d["seqlen_k"],
+                                  d["block_table"], _oracle_mods(m), float(d["k_descale"]), float(d["v_descale"]),
+                                  **kw)
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MODS))
+@pytest.mark.parametrize("shape", sorted(VEC_CASES))
+def test_paged_fp8_score_mods(shape, name):
+    """ALiBi, soft-cap, windows and block masks on FP8 head-major pages: the
+    prefill kernel's mods variant (prefill, chunked) and the decode kernel's
+    (one and two row blocks), against the oracle on the dequantised cache."""
+    lq, lk, Hq, Hkv, Dqk, _ = VEC_CASES[shape]
+    d = synth.make_paged(lq, lk, Hq, Hkv, Dqk, 128, page_size=64, seed=261 + len(name), extra_pages=3)
+    m = _fp8_mods(name, d, seed=271)
+    o, lse = _paged_run(d, m, 128)
+    o_ref, l_ref = _fp8_ref(d, m)
+    _cmp_packed(o, lse, o_ref, l_ref, TOL_O_FP8, f"fp8 mods {shape} {name}")
+
+
+@pytest.mark.parametrize("name", ["alibi_softcap_causal", "bmask_causal"])
+@pytest.mark.parametrize("shape", sorted(VEC_CASES))
+def test_paged_fp8_score_mods_variants(shape, name):
+    """The same mods through every other instantiation: vectorised pages
+    (bitwise the head-major result), E4M3 queries (oracle, and bitwise
+    across page formats), and D_qk = D_v = 192 (oracle, and vectorised)."""
+    lq, lk, Hq, Hkv, Dqk, _ = VEC_CASES[shape]
+    d = synth.make_paged(lq, lk, Hq, Hkv, Dqk, 128, page_size=16, seed=281, extra_pages=3)
+    m = _fp8_mods(name, d, seed=283)
+    o, lse = _paged_run(d, m, 128)
+    o2, l2 = _paged_vec_run(d, m, 128)
+    assert torch.equal(o, o2) and torch.equal(lse, l2), f"vec {shape} {name}"
+    d8 = synth.make_paged(lq, lk, Hq, Hkv, Dqk, 128, page_size=16, seed=285, extra_pages=3, q_dtype="fp8")
+    o, lse = _paged_q8_run(d8, m, 128)
+    o_ref, l_ref = _fp8_ref(d8, m, q8=True)
+    _cmp_packed(o, lse, o_ref, l_ref, TOL_O_FP8, f"q8 mods {shape} {name}")
+    o2, l2 = _paged_q8_run(d8, m, 128, vec=True)
+    assert torch.equal(o, o2) and torch.equal(lse, l2), f"q8 vec {shape} {name}"
+    d9 = synth.make_paged(lq, lk, Hq, Hkv, 192, 192, page_size=16, seed=287, extra_pages=3)
+    o, lse = _paged_run(d9, m, 192)
+    o_ref, l_ref = _fp8_ref(d9, m)
+    _cmp_packed(o, lse, o_ref, l_ref, TOL_O_FP8, f"v192 mods {shape} {name}")
+    o2, l2 = _paged_vec_run(d9, m, 192)
+    assert torch.equal(o, o2) and torch.equal(lse, l2), f"v192 vec {shape} {name}"
+
+
 def _sweep_case(i):
     """Case i of the sweep: seeded lengths (zero, short, tile-straddling),
     head dims, GQA ratio and mods, chosen by a generator of its own."""
