@@ -707,7 +707,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   if (max_sq > total_q || max_sk > total_k) return fail(FA_ERR_INVALID, "max_seqlen exceeds the packed token count");
   if (total_q >= kI32 || total_k >= kI32) return fail(FA_ERR_LIMIT, "token counts must stay below 2^31");
   if (B * Hq >= kI32 || B * Hkv >= 65536 * 16384) return fail(FA_ERR_LIMIT, "B*H exceeds the grid limit");
-  if (max_sq / 128 >= 65535 || max_sk / 128 >= 65535) return fail(FA_ERR_LIMIT, "sequence length exceeds the grid limit");
+  if (max_sq / 128 >= 65535 || max_sk / 64 >= 65535) return fail(FA_ERR_LIMIT, "sequence length exceeds the grid limit");
   Mods m;
   if ((rc = read_mods(mods, d_qk, max_sq, max_sk, &m))) return rc;
   if (m.flags & (FA_ALIBI | FA_SOFTCAP | FA_BLOCK_MASK))

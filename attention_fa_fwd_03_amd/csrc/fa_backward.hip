@@ -334,6 +334,212 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- dK + dV, 16 keys per wavefront
+// One kernel for both gradients at D = 128: a wavefront owns 16 keys, so its
+// K and V fragments (2 x 16 registers) and its dK^T, dV^T accumulators
+// (2 x 32) leave room for two wavefronts per SIMD, and S and dP are
+// computed once per (row, key) for both gradients.  Products are
+// v_mfma_f32_16x16x32_bf16 (lane l: A row / B column l%16, the 8 contraction
+// slots 8 (l/16) + j; accumulator: column l%16, rows 4 (l/16) + i):
+//   S  [16 rows x 16 keys] = Q K^T     A = Q rows from LDS, B = K in registers
+//   dP [16 rows x 16 keys] = dO V^T    A = dO rows from LDS, B = V in registers
+//   dV^T [16 d x keys] += dO^T P       over 32 rows: A = dO read transposed,
+//   dK^T [16 d x keys] += Q^T dS         B = P / dS from two row blocks' accumulators
+// Contraction slot j of lane group g = l/16 holds row 4 g + j (j < 4) or
+// 16 + 4 g + j - 4 (the rows the two accumulators give that lane); the
+// transposed reads fetch the same rows (any bijection of the summed rows
+// serves, as long as both operands use it).
+constexpr int kBw16Keys = 16 * kBwWaves;   // keys per workgroup
+
+__device__ __forceinline__ f32x4 bw_mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// A fragment of a 16x16x32 transposed product from a swizzled 64-row tile:
+// columns [16 dblk, +16) (lane l: column 16 dblk + l%16) and the 32 rows
+// 32 half + {4 g + [0, 4), 16 + 4 g + [0, 4)} of lane group g.
+template <int kRow>
+__device__ __forceinline__ bf16x8 tr_fragment16(const char FA_LDS* tile, int half, int dblk, int lane) {
+  const int grp = lane >> 4, i16 = lane & 15;
+  const int r1 = half * 32 + 4 * grp + (i16 >> 2);
+  const int r2 = r1 + 16;
+  const int dcol = dblk * 16 + 4 * (i16 & 3);
+  const int chunk = dcol >> 3, hv = (dcol >> 2) & 1;
+  const bf16x4 lo4 = lds_read_tr16(tile + r1 * kRow + ((chunk ^ swz<kRow>(r1)) << 4) + hv * 8);
+  const bf16x4 hi4 = lds_read_tr16(tile + r2 * kRow + ((chunk ^ swz<kRow>(r2)) << 4) + hv * 8);
+  bf16x8 f;
+  f[0] = lo4[0]; f[1] = lo4[1]; f[2] = lo4[2]; f[3] = lo4[3];
+  f[4] = hi4[0]; f[5] = hi4[1]; f[6] = hi4[2]; f[7] = hi4[3];
+  return f;
+}
+
+template <int D>
+__global__ __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void fa_bwd_dkdv16_kernel(const BwdArgs a) {
+  constexpr int kRow = D * 2;
+  constexpr int kTileB = kBwTile * kRow;
+  constexpr int kStage = 2 * kTileB + 2 * kBwTile * 4;
+  constexpr int NS = D / 32;                 // contraction steps of S and dP
+  constexpr int ND = D / 16;                 // 16-wide output blocks of dK^T, dV^T
+  __shared__ __attribute__((aligned(1024))) char lds_raw[2 * kStage];
+  char FA_LDS* lds = (char FA_LDS*)(lds_raw);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int grp = lane >> 4;
+  // causal: key blocks near the start see the most rows and come first (y
+  // ascending); the head rotates by one slot of 8 per level
+  const int bg = a.causal ? ((int)blockIdx.x + 8 * (int)blockIdx.y) % (int)gridDim.x : (int)blockIdx.x;
+  if (bg >= a.B * a.Hkv) return;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const BwSeq sv = bw_seq(a, b);
+  const int k0 = blockIdx.y * kBw16Keys;
+  if (k0 >= sv.skv) return;
+  const int key = k0 + wave * 16 + (lane & 15);
+  const bool kvalid = key < sv.skv;
+  const int delta_al = sv.skv - sv.sq;
+
+  // K and V fragments of this lane's key (B operands): d = 32 s + 8 grp + e
+  bf16x8 kf[NS], vf[NS];
+  {
+    const int64_t kr = sv.kstart + min(key, sv.skv - 1);
+    const bf16* kp = a.k + kr * a.k_st + (int64_t)g * a.k_sh + grp * 8;
+    const bf16* vp = a.v + kr * a.v_st + (int64_t)g * a.v_sh + grp * 8;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      kf[s] = kvalid ? *reinterpret_cast<const bf16x8*>(kp + 32 * s) : bf16x8{};
+      vf[s] = kvalid ? *reinterpret_cast<const bf16x8*>(vp + 32 * s) : bf16x8{};
+    }
+  }
+  f32x4 dk[ND], dv[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) dk[d] = dv[d] = f32x4{};
+
+  // query rows that see any key of [k0, j1]
+  const int j1 = min(k0 + kBw16Keys, sv.skv) - 1;
+  int r_lo = 0, r_hi = sv.sq - 1;
+  if (a.causal) r_lo = max(r_lo, k0 - delta_al);
+  if (a.win_right >= 0) r_lo = max(r_lo, k0 - delta_al - a.win_right);
+  if (a.win_left >= 0) r_hi = min(r_hi, j1 + a.win_left - delta_al);
+  const int qb0 = r_lo >= 0 ? r_lo / kBwTile : 0;
+  const int nqb = r_lo <= r_hi ? r_hi / kBwTile - qb0 + 1 : 0;
+  const int nsteps = nqb * a.group;
+  const float C = a.qk_scale * kLog2e;
+
+  RowStager<D> st;
+  st.init(wave, lane);
+  auto stage_ptr = [&](int i) { return lds + i * kStage; };
+  float ld_lse = 0.0f, ld_delta = 0.0f;
+  auto issue = [&](int n, int sb) {
+    const int h = g * a.group + n / nqb;
+    const int r0 = (qb0 + n % nqb) * kBwTile;
+    char FA_LDS* sp = stage_ptr(sb);
+    st.issue(a.q + sv.qstart * a.q_st + (int64_t)h * a.q_sh, a.q_st, r0, sv.sq, sp, wave);
+    st.issue(a.dout + sv.qstart * a.o_st + (int64_t)h * a.o_sh, a.o_st, r0, sv.sq, sp + kTileB, wave);
+    if (tid < kBwTile) {
+      const int r = min(r0 + tid, sv.sq - 1);
+      const int64_t li = bw_lse_index(a, b, h, sv.qstart, r);
+      ld_lse = lse_log2(a.lse[li]);
+      ld_delta = a.delta[li];
+    }
+  };
+  auto publish = [&](int sb) {
+    if (tid < kBwTile) {
+      float FA_LDS* lp = reinterpret_cast<float FA_LDS*>(stage_ptr(sb) + 2 * kTileB);
+      lp[tid] = ld_lse;
+      lp[kBwTile + tid] = ld_delta;
+    }
+  };
+
+  if (nsteps > 0) {
+    issue(0, 0);
+    FA_WAIT_VMCNT(0);
+    publish(0);
+  }
+  for (int n = 0; n < nsteps; ++n) {
+    const int sb = n & 1;
+    __syncthreads();   // step n visible; everyone is done with the other buffer
+    if (n + 1 < nsteps) issue(n + 1, sb ^ 1);
+    const char FA_LDS* qt = stage_ptr(sb);
+    const char FA_LDS* dt = qt + kTileB;
+    const float FA_LDS* lse2 = reinterpret_cast<const float FA_LDS*>(qt + 2 * kTileB);
+    const float FA_LDS* dl = lse2 + kBwTile;
+    const int r0 = (qb0 + n % nqb) * kBwTile;
+
+    // every row of the tile sees every key of this wavefront: no per-score mask
+    const int kw0 = k0 + wave * 16, kw1 = kw0 + 15;
+    bool full = kw1 < sv.skv && r0 + kBwTile <= sv.sq;
+    if (a.causal) full = full && kw1 <= r0 + delta_al;
+    if (a.win_right >= 0) full = full && kw1 <= r0 + delta_al + a.win_right;
+    if (a.win_left >= 0) full = full && kw0 >= r0 + kBwTile - 1 + delta_al - a.win_left;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      // S and dP of the rows [32 hf, +32): two 16-row blocks
+      f32x4 s[2] = {f32x4{}, f32x4{}}, dp[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+      for (int stp = 0; stp < NS; ++stp)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const int r = hf * 32 + rb * 16 + (lane & 15);
+          const int off = r * kRow + (((4 * stp + grp) ^ swz<kRow>(r)) << 4);
+          s[rb] = bw_mfma16(lds_read_b128(qt + off), kf[stp], s[rb]);
+          dp[rb] = bw_mfma16(lds_read_b128(dt + off), vf[stp], dp[rb]);
+        }
+      // P and dS: accumulator register i of block rb is row 32 hf + 16 rb + 4 grp + i
+      bf16x8 pf, dsf;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int rr = hf * 32 + rb * 16 + grp * 4;
+        const f32x4 l4 = *reinterpret_cast<const f32x4 FA_LDS*>(lse2 + rr);
+        const f32x4 d4 = *reinterpret_cast<const f32x4 FA_LDS*>(dl + rr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float p = exp2_hw(fmaf(s[rb][i], C, -l4[i]));
+          if (!full) {
+            const int qi = r0 + rr + i;
+            const int ip = qi + delta_al;
+            bool vis = kvalid && qi < sv.sq;
+            if (a.causal) vis = vis && key <= ip;
+            if (a.win_right >= 0) vis = vis && key <= ip + a.win_right;
+            if (a.win_left >= 0) vis = vis && key >= ip - a.win_left;
+            p = vis ? p : 0.0f;
+          }
+          pf[rb * 4 + i] = (bf16)p;
+          dsf[rb * 4 + i] = (bf16)(p * (dp[rb][i] - d4[i]));
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over these 32 rows
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        dv[d] = bw_mfma16(tr_fragment16<kRow>(dt, hf, d, lane), pf, dv[d]);
+        dk[d] = bw_mfma16(tr_fragment16<kRow>(qt, hf, d, lane), dsf, dk[d]);
+      }
+    }
+    if (n + 1 < nsteps) {
+      FA_WAIT_VMCNT(0);
+      publish(sb ^ 1);
+    }
+  }
+
+  // dK^T / dV^T register i of block d: dim 16 d + 4 grp + i of this lane's key
+  if (kvalid) {
+    const int64_t kr = sv.kstart + key;
+    bf16* kp = a.dk + kr * a.k_st + (int64_t)g * a.k_sh + grp * 4;
+    bf16* vp = a.dv + kr * a.v_st + (int64_t)g * a.v_sh + grp * 4;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      bf16x4 wk, wv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wk[i] = (bf16)(dk[d][i] * a.qk_scale);
+        wv[i] = (bf16)dv[d][i];
+      }
+      *reinterpret_cast<bf16x4*>(kp + d * 16) = wk;
+      *reinterpret_cast<bf16x4*>(vp + d * 16) = wv;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- dQ
 // Workgroup = (sequence, q-head, 128 query rows), as the forward kernel;
 // 64-key K / V tiles stream through two LDS stages.
@@ -493,13 +699,11 @@ static hipError_t launch_bwd(const BwdArgs& a, int max_sq, int max_skv, hipStrea
     if (e != hipSuccess) return e;
   }
   if (max_skv > 0) {
-    const dim3 grid(a.B * a.Hkv, (max_skv + kBwKeys - 1) / kBwKeys);
-    if (D > 64) {
-      hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, 1>), grid, dim3(kBwThreads), 0, stream, a);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, 2>), grid, dim3(kBwThreads), 0, stream, a);
+    if constexpr (D > 64) {
+      const dim3 grid(a.B * a.Hkv, (max_skv + kBw16Keys - 1) / kBw16Keys);
+      hipLaunchKernelGGL((fa_bwd_dkdv16_kernel<D>), grid, dim3(kBwThreads), 0, stream, a);
     } else {
+      const dim3 grid(a.B * a.Hkv, (max_skv + kBwKeys - 1) / kBwKeys);
       hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, 0>), grid, dim3(kBwThreads), 0, stream, a);
     }
     hipError_t e = hipGetLastError();
