@@ -68,11 +68,22 @@ __device__ __forceinline__ int64_t bw_lse_index(const BwdArgs& a, int b, int h, 
   return ((int64_t)b * a.Hq + h) * a.Sq + i;
 }
 
+// Row swizzle of the Q / dO tiles of the 16-key dK/dV kernel (256-byte
+// rows): its transposed reads take 8 consecutive rows x 2 adjacent chunks
+// per 32-lane pass, its A fragments 16 rows x 1 chunk per 16 lanes.  Bits
+// 1-3 from r mod 8 and bit 0 from bit 3 of r keep both conflict-free (the
+// forward's map sends rows r and r + 4 to the same chunk pair).
+__device__ __forceinline__ int swz_bw16(int r) {
+  const int g = (r >> 2) & 3, i = r & 3;
+  return ((2 * i + ((g ^ (g >> 1)) & 1)) << 1) | ((g >> 1) & 1);
+}
+
 // 64 rows x D bf16 of a packed tensor -> swizzled LDS tile, one 1 KB
 // global_load_lds per wavefront instruction (lane l fills 16 bytes at
-// 16 l of its KB: tile row r, stored chunk pos = source chunk pos ^ swz(r)).
-// Rows at or past nrows re-read the last row (their results are masked).
-template <int D>
+// 16 l of its KB: tile row r, stored chunk pos = source chunk pos ^ swz(r),
+// swz_bw16 when ALT).  Rows at or past nrows re-read the last row (their
+// results are masked).
+template <int D, bool ALT = false>
 struct RowStager {
   static constexpr int kRow = D * 2;
   static constexpr int kPerWave = kBwTile * kRow / 1024 / kBwWaves;
@@ -83,8 +94,21 @@ struct RowStager {
     for (int i = 0; i < kPerWave; ++i) {
       const int byte = (wave * kPerWave + i) * 1024 + lane * 16;
       row[i] = byte / kRow;
-      col[i] = ((((byte % kRow) >> 4) ^ swz<kRow>(row[i])) << 3);
+      col[i] = ((((byte % kRow) >> 4) ^ (ALT ? swz_bw16(row[i]) : swz<kRow>(row[i]))) << 3);
     }
+  }
+  // Whole tiles (rows r0..r0+63 all inside the sequence, row stride below
+  // 2^24 elements): one buffer descriptor at row r0 and 32-bit per-lane
+  // offsets computed once per stride, no per-piece address arithmetic.
+  __device__ __forceinline__ void offsets(int64_t st, unsigned (&off)[kPerWave]) const {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) off[i] = ((unsigned)row[i] * (unsigned)st + (unsigned)col[i]) * 2u;
+  }
+  __device__ __forceinline__ void issue_whole(const bf16* base, int64_t st, int r0, const unsigned (&off)[kPerWave],
+                                              char FA_LDS* tile, int wave) const {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)r0 * st);
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) buffer_to_lds16(rs, off[i], tile + (wave * kPerWave + i) * 1024);
   }
   __device__ __forceinline__ void issue(const bf16* base, int64_t st, int r0, int nrows, char FA_LDS* tile,
                                         int wave) const {
@@ -355,7 +379,7 @@ __device__ __forceinline__ f32x4 bw_mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// A fragment of a 16x16x32 transposed product from a swizzled 64-row tile:
+// A fragment of a 16x16x32 transposed product from a 64-row tile (swz_bw16):
 // columns [16 dblk, +16) (lane l: column 16 dblk + l%16) and the 32 rows
 // 32 half + {4 g + [0, 4), 16 + 4 g + [0, 4)} of lane group g.
 template <int kRow>
@@ -365,8 +389,8 @@ __device__ __forceinline__ bf16x8 tr_fragment16(const char FA_LDS* tile, int hal
   const int r2 = r1 + 16;
   const int dcol = dblk * 16 + 4 * (i16 & 3);
   const int chunk = dcol >> 3, hv = (dcol >> 2) & 1;
-  const bf16x4 lo4 = lds_read_tr16(tile + r1 * kRow + ((chunk ^ swz<kRow>(r1)) << 4) + hv * 8);
-  const bf16x4 hi4 = lds_read_tr16(tile + r2 * kRow + ((chunk ^ swz<kRow>(r2)) << 4) + hv * 8);
+  const bf16x4 lo4 = lds_read_tr16(tile + r1 * kRow + ((chunk ^ swz_bw16(r1)) << 4) + hv * 8);
+  const bf16x4 hi4 = lds_read_tr16(tile + r2 * kRow + ((chunk ^ swz_bw16(r2)) << 4) + hv * 8);
   bf16x8 f;
   f[0] = lo4[0]; f[1] = lo4[1]; f[2] = lo4[2]; f[3] = lo4[3];
   f[4] = hi4[0]; f[5] = hi4[1]; f[6] = hi4[2]; f[7] = hi4[3];
@@ -376,6 +400,7 @@ __device__ __forceinline__ bf16x8 tr_fragment16(const char FA_LDS* tile, int hal
 template <int D>
 __global__ __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_bwd_dkdv16_kernel(const BwdArgs a) {
+  static_assert(D == 128, "swz_bw16 is a map on the 16 chunks of 256-byte rows");
   constexpr int kRow = D * 2;
   constexpr int kTileB = kBwTile * kRow;
   constexpr int kStage = 2 * kTileB + 2 * kBwTile * 4;
@@ -415,6 +440,14 @@ void fa_bwd_dkdv16_kernel(const BwdArgs a) {
 #pragma unroll
   for (int d = 0; d < ND; ++d) dk[d] = dv[d] = f32x4{};
 
+  // rows that see this lane's key: [my_qlo, my_qlo + my_cnt) (causal:
+  // i + delta >= key; windows: key - delta - right <= i <= key - delta + left)
+  int my_qlo = 0, my_qhi = sv.sq - 1;
+  if (a.causal) my_qlo = max(my_qlo, key - delta_al);
+  if (a.win_right >= 0) my_qlo = max(my_qlo, key - delta_al - a.win_right);
+  if (a.win_left >= 0) my_qhi = min(my_qhi, key - delta_al + a.win_left);
+  const unsigned my_cnt = kvalid ? (unsigned)max(my_qhi - my_qlo + 1, 0) : 0u;
+
   // query rows that see any key of [k0, j1]
   const int j1 = min(k0 + kBw16Keys, sv.skv) - 1;
   int r_lo = 0, r_hi = sv.sq - 1;
@@ -426,21 +459,32 @@ void fa_bwd_dkdv16_kernel(const BwdArgs a) {
   const int nsteps = nqb * a.group;
   const float C = a.qk_scale * kLog2e;
 
-  RowStager<D> st;
+  RowStager<D, true> st;
   st.init(wave, lane);
+  unsigned offq[RowStager<D, true>::kPerWave], offo[RowStager<D, true>::kPerWave];
+  st.offsets(a.q_st, offq);
+  st.offsets(a.o_st, offo);
+  const bool whole_ok = a.q_st < (1 << 24) && a.o_st < (1 << 24);
   auto stage_ptr = [&](int i) { return lds + i * kStage; };
   float ld_lse = 0.0f, ld_delta = 0.0f;
   auto issue = [&](int n, int sb) {
     const int h = g * a.group + n / nqb;
     const int r0 = (qb0 + n % nqb) * kBwTile;
     char FA_LDS* sp = stage_ptr(sb);
-    st.issue(a.q + sv.qstart * a.q_st + (int64_t)h * a.q_sh, a.q_st, r0, sv.sq, sp, wave);
-    st.issue(a.dout + sv.qstart * a.o_st + (int64_t)h * a.o_sh, a.o_st, r0, sv.sq, sp + kTileB, wave);
+    const bf16* qb = a.q + sv.qstart * a.q_st + (int64_t)h * a.q_sh;
+    const bf16* ob = a.dout + sv.qstart * a.o_st + (int64_t)h * a.o_sh;
+    if (whole_ok && r0 + kBwTile <= sv.sq) {
+      st.issue_whole(qb, a.q_st, r0, offq, sp, wave);
+      st.issue_whole(ob, a.o_st, r0, offo, sp + kTileB, wave);
+    } else {
+      st.issue(qb, a.q_st, r0, sv.sq, sp, wave);
+      st.issue(ob, a.o_st, r0, sv.sq, sp + kTileB, wave);
+    }
     if (tid < kBwTile) {
+      const int64_t l0 = bw_lse_index(a, b, h, sv.qstart, 0);   // rows of one (sequence, head) are contiguous
       const int r = min(r0 + tid, sv.sq - 1);
-      const int64_t li = bw_lse_index(a, b, h, sv.qstart, r);
-      ld_lse = lse_log2(a.lse[li]);
-      ld_delta = a.delta[li];
+      ld_lse = lse_log2(a.lse[l0 + r]);
+      ld_delta = a.delta[l0 + r];
     }
   };
   auto publish = [&](int sb) {
@@ -472,49 +516,60 @@ void fa_bwd_dkdv16_kernel(const BwdArgs a) {
     if (a.causal) full = full && kw1 <= r0 + delta_al;
     if (a.win_right >= 0) full = full && kw1 <= r0 + delta_al + a.win_right;
     if (a.win_left >= 0) full = full && kw0 >= r0 + kBwTile - 1 + delta_al - a.win_left;
+    // S and dP of all 64 rows (four 16-row blocks) first, then P and dS,
+    // then the dV / dK products: the vector work of one half can run under
+    // the products of the other
+    f32x4 s[4], dp[4];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      // S and dP of the rows [32 hf, +32): two 16-row blocks
-      f32x4 s[2] = {f32x4{}, f32x4{}}, dp[2] = {f32x4{}, f32x4{}};
+    for (int rb = 0; rb < 4; ++rb) s[rb] = dp[rb] = f32x4{};
 #pragma unroll
-      for (int stp = 0; stp < NS; ++stp)
+    for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          const int r = hf * 32 + rb * 16 + (lane & 15);
-          const int off = r * kRow + (((4 * stp + grp) ^ swz<kRow>(r)) << 4);
-          s[rb] = bw_mfma16(lds_read_b128(qt + off), kf[stp], s[rb]);
-          dp[rb] = bw_mfma16(lds_read_b128(dt + off), vf[stp], dp[rb]);
-        }
-      // P and dS: accumulator register i of block rb is row 32 hf + 16 rb + 4 grp + i
-      bf16x8 pf, dsf;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int rr = hf * 32 + rb * 16 + grp * 4;
-        const f32x4 l4 = *reinterpret_cast<const f32x4 FA_LDS*>(lse2 + rr);
-        const f32x4 d4 = *reinterpret_cast<const f32x4 FA_LDS*>(dl + rr);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float p = exp2_hw(fmaf(s[rb][i], C, -l4[i]));
-          if (!full) {
-            const int qi = r0 + rr + i;
-            const int ip = qi + delta_al;
-            bool vis = kvalid && qi < sv.sq;
-            if (a.causal) vis = vis && key <= ip;
-            if (a.win_right >= 0) vis = vis && key <= ip + a.win_right;
-            if (a.win_left >= 0) vis = vis && key >= ip - a.win_left;
-            p = vis ? p : 0.0f;
-          }
-          pf[rb * 4 + i] = (bf16)p;
-          dsf[rb * 4 + i] = (bf16)(p * (dp[rb][i] - d4[i]));
-        }
+      for (int stp = 0; stp < NS; ++stp) {
+        const int r = rb * 16 + (lane & 15);
+        const int off = r * kRow + (((4 * stp + grp) ^ swz_bw16(r)) << 4);
+        s[rb] = bw_mfma16(lds_read_b128(qt + off), kf[stp], s[rb]);
+        dp[rb] = bw_mfma16(lds_read_b128(dt + off), vf[stp], dp[rb]);
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over these 32 rows
+    // P (in place of S): accumulator register i of block rb is row
+    // 16 rb + 4 grp + i
 #pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        dv[d] = bw_mfma16(tr_fragment16<kRow>(dt, hf, d, lane), pf, dv[d]);
-        dk[d] = bw_mfma16(tr_fragment16<kRow>(qt, hf, d, lane), dsf, dk[d]);
+    for (int rb = 0; rb < 4; ++rb) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4 FA_LDS*>(lse2 + rb * 16 + grp * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[rb][i] = exp2_hw(fmaf(s[rb][i], C, -l4[i]));
+    }
+    if (!full) {
+      // the bounds pass through an opaque copy made here, so the selects stay
+      // inside this branch instead of being speculated onto every tile
+      int base = r0 + grp * 4 - my_qlo;
+      unsigned cnt = my_cnt;
+      asm volatile("" : "+v"(base), "+v"(cnt));
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s[rb][i] = (unsigned)(base + rb * 16 + i) < cnt ? s[rb][i] : 0.0f;
+    }
+    // dS = P (dP - Delta); half hf takes blocks 2 hf and 2 hf + 1
+    bf16x8 pf[2], dsf[2];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4 FA_LDS*>(dl + rb * 16 + grp * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pf[rb >> 1][(rb & 1) * 4 + i] = (bf16)s[rb][i];
+        dsf[rb >> 1][(rb & 1) * 4 + i] = (bf16)(s[rb][i] * (dp[rb][i] - d4[i]));
       }
     }
+    // dV^T += dO^T P and dK^T += Q^T dS over the two 32-row halves
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        dv[d] = bw_mfma16(tr_fragment16<kRow>(dt, hf, d, lane), pf[hf], dv[d]);
+        dk[d] = bw_mfma16(tr_fragment16<kRow>(qt, hf, d, lane), dsf[hf], dk[d]);
+      }
     if (n + 1 < nsteps) {
       FA_WAIT_VMCNT(0);
       publish(sb ^ 1);
@@ -617,12 +672,22 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
 
   RowStager<D> st;
   st.init(wave, lane);
+  // whole tiles share one set of 32-bit offsets (K and V rows have the same
+  // stride here: D_qk = D_v)
+  unsigned offk[RowStager<D>::kPerWave];
+  st.offsets(a.k_st, offk);
+  const bool whole_ok = a.k_st == a.v_st && a.k_st < (1 << 24);
   auto stage_ptr = [&](int i) { return lds + i * kStage; };
   const bf16* kbase = a.k + sv.kstart * a.k_st + (int64_t)g * a.k_sh;
   const bf16* vbase = a.v + sv.kstart * a.v_st + (int64_t)g * a.v_sh;
   auto issue = [&](int t, int sb) {
-    st.issue(kbase, a.k_st, t * kBwTile, sv.skv, stage_ptr(sb), wave);
-    st.issue(vbase, a.v_st, t * kBwTile, sv.skv, stage_ptr(sb) + kTileB, wave);
+    if (whole_ok && (t + 1) * kBwTile <= sv.skv) {
+      st.issue_whole(kbase, a.k_st, t * kBwTile, offk, stage_ptr(sb), wave);
+      st.issue_whole(vbase, a.v_st, t * kBwTile, offk, stage_ptr(sb) + kTileB, wave);
+    } else {
+      st.issue(kbase, a.k_st, t * kBwTile, sv.skv, stage_ptr(sb), wave);
+      st.issue(vbase, a.v_st, t * kBwTile, sv.skv, stage_ptr(sb) + kTileB, wave);
+    }
   };
   if (t_begin <= t_end) {
     issue(t_begin, 0);
