@@ -69,10 +69,12 @@ __device__ __forceinline__ int64_t bw_lse_index(const BwdArgs& a, int b, int h, 
 }
 
 // Row swizzle of the Q / dO tiles of the 16-key dK/dV kernel (256-byte
-// rows): its transposed reads take 8 consecutive rows x 2 adjacent chunks
-// per 32-lane pass, its A fragments 16 rows x 1 chunk per 16 lanes.  Bits
-// 1-3 from r mod 8 and bit 0 from bit 3 of r keep both conflict-free (the
-// forward's map sends rows r and r + 4 to the same chunk pair).
+// rows): its transposed reads take 8 rows (two groups of four) x 2 adjacent
+// chunks per pass, its A fragments 16 rows x 1 chunk per 16 lanes.  With
+// r = 4 g + i (i < 4) inside 16 rows, the chunk pair index is 2 i + the
+// parity of g and g / 2 and bit 0 is bit 1 of g: any two of the four
+// groups then fill 8 different chunk pairs, and the 16 rows 16 different
+// chunks (the forward's map sends rows r and r + 4 to the same pair).
 __device__ __forceinline__ int swz_bw16(int r) {
   const int g = (r >> 2) & 3, i = r & 3;
   return ((2 * i + ((g ^ (g >> 1)) & 1)) << 1) | ((g >> 1) & 1);
