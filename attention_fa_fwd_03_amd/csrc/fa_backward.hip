@@ -666,6 +666,7 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
   const int t_begin = lo_min / kBwTile;
   const int t_end = hi_max >= lo_min ? hi_max / kBwTile : t_begin - 1;
   const int my_lo = row_lo(qrow), my_hi = row_hi(qrow);
+  const unsigned my_cnt = qvalid ? (unsigned)max(my_hi - my_lo + 1, 0) : 0u;   // keys [my_lo, my_lo + my_cnt)
   // this wavefront's rows [wq0, wq1]: the intersection of their key ranges
   const int wq0 = q0 + wave * 32, wq1 = wq0 + 31;
   const bool wave_rows_full = wq1 < sv.sq;
@@ -715,22 +716,31 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
         dp[kb] = mfma32(lds_read_b128(vt + off), of[stp], dp[kb]);
       }
     }
-    // dS^T (register i of key block kb: key 32 kb + 8 (i/4) + 4 (lane/32) + i%4);
-    // tiles inside every row's key range of this wavefront skip the mask
+    // P^T in place of S^T (register i of key block kb: key 32 kb + 8 (i/4) +
+    // 4 (lane/32) + i%4), then the mask, then dS^T; tiles inside every row's
+    // key range of this wavefront skip the mask
     const bool full = wave_rows_full && k0 >= wave_lo_max && k0 + kBwTile - 1 <= wave_hi_min;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = exp2_hw(fmaf(s[kb][i], C, -lse2));
+    if (!full) {
+      // the bounds pass through an opaque copy made here, so the selects stay
+      // inside this branch instead of being speculated onto every tile
+      int base = k0 + (lane >> 5) * 4 - my_lo;
+      unsigned cnt = my_cnt;
+      asm volatile("" : "+v"(base), "+v"(cnt));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          s[kb][i] = (unsigned)(base + kb * 32 + (i >> 2) * 8 + (i & 3)) < cnt ? s[kb][i] : 0.0f;
+    }
     bf16x8 dsf[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = exp2_hw(fmaf(s[kb][i], C, -lse2));
-        if (!full) {
-          const int j = k0 + kb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-          p = (qvalid && j >= my_lo && j <= my_hi) ? p : 0.0f;
-        }
-        dsf[kb * 2 + (i >> 3)][i & 7] = (bf16)(p * (dp[kb][i] - dlt));
-      }
-    }
+      for (int i = 0; i < 16; ++i) dsf[kb * 2 + (i >> 3)][i & 7] = (bf16)(s[kb][i] * (dp[kb][i] - dlt));
     // dQ^T += K^T dS^T over the tile's 64 keys
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
