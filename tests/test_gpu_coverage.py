@@ -260,6 +260,59 @@ def test_paged_fp8_score_mods_variants(shape, name):
     assert torch.equal(o, o2) and torch.equal(lse, l2), f"v192 vec {shape} {name}"
 
 
+def _paged_sweep_case(i):
+    """Seeded paged call: lengths (prefill, chunked or decode rows), page size,
+    head dims, GQA, query type, page format, mods and block mask, all drawn
+    from the exported paged surface."""
+    g = torch.Generator().manual_seed(9000 + i)
+    ri = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=g))
+    B = ri(1, 5)
+    shape = ("prefill", "chunked", "decode")[ri(0, 2)]
+    lk = [ri(0, 700) for _ in range(B)]
+    if shape == "prefill":
+        lq = list(lk)
+    elif shape == "chunked":
+        lq = [min(n, ri(0, 150)) for n in lk]
+    else:
+        lq = [ri(0, 2) if n > 0 else 0 for n in lk]
+    Dqk, Dv = ((192, 128), (128, 128), (192, 192))[ri(0, 2)]
+    Hkv = ri(1, 2)
+    Hq = Hkv * (1, 2, 8)[ri(0, 2)]
+    vec = ri(0, 1) == 1
+    ps = (16, 64, 256)[ri(0, 2)] if vec else (1, 8, 16, 64, 256)[ri(0, 4)]
+    q8 = ri(0, 2) == 0
+    kind = ri(0, 6)
+    mods = [dict(causal=True), dict(), dict(window=(ri(0, 200), ri(0, 20))), dict(causal=True, alibi_slope=0.0625),
+            dict(softcap=15.0), dict(causal=True, softcap=30.0, alibi_slope=0.03), dict(causal=True, bmask=True)][kind]
+    return lq, lk, Hq, Hkv, Dqk, Dv, ps, vec, q8, mods
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_seeded_paged_sweep(i):
+    """FP8 caches over the whole paged surface against the oracle on the
+    dequantised cache (NaN-poisoned unused pages and page tails)."""
+    lq, lk, Hq, Hkv, Dqk, Dv, ps, vec, q8, mods = _paged_sweep_case(i)
+    if sum(lq) == 0:
+        lq[0] = 1 if lk[0] > 0 else 0
+    d = synth.make_paged(lq, lk, Hq, Hkv, Dqk, Dv, page_size=ps, seed=9100 + i, extra_pages=3,
+                         q_dtype="fp8" if q8 else "bf16")
+    m = dict(mods)
+    if m.pop("bmask", False):
+        nqb = max(1, math.ceil(max(lq) / 128))
+        nkb = max(1, math.ceil(max(lk) / 64))
+        m["block_mask"] = synth.bernoulli_block_mask(len(lk) * Hq, nqb, nkb, 0.6, seed=9200 + i).to(DEV)
+        m["mask_block"] = (128, 64)
+    what = f"paged sweep {i}: lq {lq} lk {lk} Hq {Hq} Hkv {Hkv} D {Dqk}/{Dv} ps {ps} vec {vec} q8 {q8} {mods}"
+    if q8:
+        o, lse = _paged_q8_run(d, m, Dv, vec=vec)
+    elif vec:
+        o, lse = _paged_vec_run(d, m, Dv)
+    else:
+        o, lse = _paged_run(d, m, Dv)
+    o_ref, l_ref = _fp8_ref(d, m, q8=q8)
+    _cmp_packed(o, lse, o_ref, l_ref, TOL_O_FP8, what)
+
+
 def _sweep_case(i):
     """Case i of the sweep: seeded lengths (zero, short, tile-straddling),
     head dims, GQA ratio and mods, chosen by a generator of its own."""
