@@ -142,3 +142,44 @@ def test_bwd_full_size_sampled():
         _check_grad(dq[s0:s0 + L, h][rows], gq[rows], f"full dq h{h}")
         _check_grad(dk[s0:s0 + L, h][rows], gk[rows], f"full dk h{h}")
         _check_grad(dv[s0:s0 + L, h][rows], gv[rows], f"full dv h{h}")
+
+
+def _bwd_sweep_case(i):
+    g = torch.Generator().manual_seed(9500 + i)
+    ri = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=g))
+    B = ri(1, 4)
+    cross = ri(0, 1) == 1
+    lq = [ri(0, 330) for _ in range(B)]
+    lk = [ri(0, 330) if cross else n for n in lq]
+    D = (64, 128)[ri(0, 1)]
+    Hkv = ri(1, 2)
+    Hq = Hkv * (1, 2, 4)[ri(0, 2)]
+    mods = [dict(causal=True), dict(), dict(window=(ri(0, 120), ri(0, 30))), dict(causal=True, window=(ri(0, 90), 0))][ri(0, 3)]
+    return lq, lk, Hq, Hkv, D, mods
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_bwd_seeded_varlen_sweep(i):
+    """Seeded ragged batches (lengths 0-330, cross lengths, GQA 1-4, D 64 and
+    128, causal / windows) through the forward and the backward, against
+    the oracle's gradients."""
+    lq, lk, Hq, Hkv, D, mods = _bwd_sweep_case(i)
+    if sum(lq) == 0 or sum(lk) == 0:
+        lq[0], lk[0] = 5, 7
+    d = synth.make_varlen(lq, lk, Hq, Hkv, D, D, seed=9600 + i)
+    q, k, v = (d[x].to(DEV) for x in ("q", "k", "v"))
+    cu_q, cu_k = d["cu_q"].to(DEV), d["cu_k"].to(DEV)
+    Tq = q.shape[0]
+    do = synth.randn_bf16((Tq, Hq, D), 9700 + i)
+    o = torch.empty((Tq, Hq, D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((Hq, Tq), dtype=torch.float32, device=DEV)
+    fa.fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, max(lq), max(lk), fa.Mods(**mods))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(fa.fa_bwd_workspace_size(Tq, Hq), 4), dtype=torch.uint8, device=DEV)
+    fa.fa_bwd_varlen(q, k, v, o, do.to(DEV), lse, dq, dk, dv, cu_q, cu_k, max(lq), max(lk), fa.Mods(**mods),
+                     workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.attention_bwd_varlen(f64(d["q"]), f64(d["k"]), f64(d["v"]), f64(do), d["cu_q"].numpy(),
+                                      d["cu_k"].numpy(), mods)
+    for gr, r, n in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
+        _check_grad(gr, r, f"bwd sweep {i}: lq {lq} lk {lk} Hq {Hq} Hkv {Hkv} D {D} {mods} {n}")
