@@ -14,8 +14,8 @@
 // less (measured on the hardware).  So each tile step pairs matrix work of
 // one tile with the vector work of another:
 //
-//   A(n):  S_{n+1} = K_{n+1} Q^T          ||  P_n = exp2(X_n) -> bf16
-//   B(n):  O^T += V_n^T P_n^T             ||  row max of S_{n+1}, row sums of P_n,
+//   A(n):  S_{n+1} = K_{n+1} Q^T          ||  P_n = exp2(X_n) -> bf16, row sums of P_n
+//   B(n):  O^T += V_n^T P_n^T             ||  row max of S_{n+1},
 //                                              X_{n+1} = S_{n+1} * C - m
 //
 // where X is the score already centred on the running max m (log2 domain,
@@ -238,9 +238,12 @@ void fa_prefill_bf16_kernel(const PrefillArgs a) {
     return r;
   };
 
-  // A(n): products of S_{n+1} (HAS_NEXT) paired with P_n = exp2(X_n)
+  // A(n): products of S_{n+1} (HAS_NEXT) paired with P_n = exp2(X_n) and its
+  // row sums (two-element dot products of the bf16 pairs, which B's products
+  // use as they are)
   auto phase_a = [&](auto has_next, const char FA_LDS* kt) {
     constexpr bool HN = decltype(has_next)::value;
+    float lsa0 = 0.0f, lsa1 = 0.0f;
     bf16x8 kf[NQK];
     if (HN) {
       sn[0] = f32x16{};
@@ -264,20 +267,23 @@ void fa_prefill_bf16_kernel(const PrefillArgs a) {
         bf16x2 pr = {(bf16)exp2_hw(xs[kb][i]), (bf16)exp2_hw(xs[kb][i + 1])};
         asm volatile("" : "+v"(pr));
         pw[e >> 1] = pr;
+        if ((e >> 1) & 1) lsa1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsa1, false);
+        else lsa0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsa0, false);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    l_run += lsa0 + lsa1;
   };
 
-  // B(n): O^T += V_n^T P_n^T paired with the row sums of P_n and, when a
-  // next tile exists, its row max and centring; returns nothing, updates
-  // xs (= X_{n+1}), m_run, l_run and the output scale
+  // B(n): O^T += V_n^T P_n^T paired, when a next tile exists, with its row
+  // max and centring; returns nothing, updates xs (= X_{n+1}), m_run, l_run
+  // and the output scale
   auto phase_b = [&](auto has_next, const char FA_LDS* vt) {
     constexpr bool HN = decltype(has_next)::value;
     bf16x8 vf[NPV];
 #pragma unroll
     for (int n = 0; n < kAheadV && n < NPV; ++n) vf[n] = vread(vt, n);
-    float mx0 = -INFINITY, mx1 = -INFINITY, ls0 = 0.0f, ls1 = 0.0f;
+    float mx0 = -INFINITY, mx1 = -INFINITY;
     float m_use = m_run;
     bool resc = false;
     constexpr int HALF = NPV / 2;
@@ -285,12 +291,6 @@ void fa_prefill_bf16_kernel(const PrefillArgs a) {
     for (int n = 0; n < NPV; ++n) {
       if (n + kAheadV < NPV) vf[n + kAheadV] = vread(vt, n + kAheadV);
       oacc[n % ND] = mfma32(vf[n], pstep(n / ND), oacc[n % ND]);
-      // row sums of P_n: 16 bf16 pairs
-#pragma unroll
-      for (int e = n * 16 / NPV; e < (n + 1) * 16 / NPV; ++e) {
-        if (e & 1) ls1 = __builtin_amdgcn_fdot2_f32_bf16(pw[e], ones, ls1, false);
-        else ls0 = __builtin_amdgcn_fdot2_f32_bf16(pw[e], ones, ls0, false);
-      }
       if (HN) {
         if (n < HALF) {
           // row max of S_{n+1}: 32 values over the first half
@@ -319,7 +319,6 @@ void fa_prefill_bf16_kernel(const PrefillArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    l_run += ls0 + ls1;
     if (HN) {
       if (resc) {
         const float alpha = exp2_hw(m_run - m_use);
