@@ -1,8 +1,9 @@
 // Attention backward pass (dQ, dK, dV) for gfx950, recomputing the
 // probabilities from the forward's saved LSE.
 //
-// Method (SM90 FlashAttention page, backward commit; LSE page, Summary): a
-// preprocess computes Delta_i = dO_i . O_i per row and head; with
+// Method (SM90 FlashAttention page, backward commit; LSE page, Summary):
+// Delta_i = dO_i . O_i per row and head (the page's preprocess; here the dQ
+// kernel computes it for its own rows and runs first); with
 // P = exp(scale q.k - LSE) the gradients are
 //   dV = P^T dO,  dS = P * (dO V^T - Delta),  dK = scale dS^T Q,  dQ = scale dS K.
 // The page's kernel walks key tiles, loops over query tiles and adds dQ
@@ -141,41 +142,6 @@ __device__ __forceinline__ bf16x8 tr_fragment(const char FA_LDS* tile, int u, in
 
 // natural-log LSE -> log2 domain, with rows that see no key sent to +inf
 __device__ __forceinline__ float lse_log2(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
-
-// ---------------------------------------------------------------- Delta
-// Delta = dO . O in fp32 per (row, head): D / 8 lanes per (row, head), one
-// 16-byte piece of O and of dO each, summed over the lanes of the row.
-template <int D>
-struct DeltaShape {
-  static constexpr int kLanes = D / 8;                 // lanes per (row, head)
-  static constexpr int kRows = 64 / kLanes;            // (row, head) items per wavefront
-};
-
-template <int D>
-__global__ __launch_bounds__(kBwThreads) void fa_bwd_delta_kernel(const BwdArgs a) {
-  using S = DeltaShape<D>;
-  const int lane = threadIdx.x & 63;
-  const int64_t item = ((int64_t)blockIdx.x * kBwWaves + (threadIdx.x >> 6)) * S::kRows + lane / S::kLanes;
-  const int piece = lane % S::kLanes;
-  const bool ok = item < a.total_rows * a.Hq;
-  const int64_t t = ok ? item / a.Hq : 0;
-  const int h = ok ? (int)(item - t * a.Hq) : 0;
-  float acc = 0.0f;
-  if (ok) {
-    const bf16x8 o = *reinterpret_cast<const bf16x8*>(a.o + t * a.o_st + (int64_t)h * a.o_sh + piece * 8);
-    const bf16x8 g = *reinterpret_cast<const bf16x8*>(a.dout + t * a.o_st + (int64_t)h * a.o_sh + piece * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc += (float)o[e] * (float)g[e];
-  }
-#pragma unroll
-  for (int off = S::kLanes / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (ok && piece == 0) {
-    int64_t li;
-    if (a.cu_q) li = (int64_t)h * a.lse_tq + t;
-    else li = ((t / a.Sq) * a.Hq + h) * a.Sq + t % a.Sq;
-    a.delta[li] = acc;
-  }
-}
 
 // ---------------------------------------------------------------- dK, dV
 // Workgroup = (sequence, kv-head, 128 keys); wavefront w owns keys
@@ -599,7 +565,8 @@ void fa_bwd_dkdv16_kernel(const BwdArgs a) {
 
 // ---------------------------------------------------------------- dQ
 // Workgroup = (sequence, q-head, 128 query rows), as the forward kernel;
-// 64-key K / V tiles stream through two LDS stages.
+// 64-key K / V tiles stream through two LDS stages.  It also computes and
+// stores Delta of its rows, so it runs before the dK / dV kernel.
 template <int D>
 __global__ __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_bwd_dq_kernel(const BwdArgs a) {
@@ -640,11 +607,26 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
       of[s] = qvalid ? *reinterpret_cast<const bf16x8*>(op + 16 * s) : bf16x8{};
     }
   }
-  float lse2 = INFINITY, dlt = 0.0f;
+  // Delta of this lane's row: its half of dO . O (the d values of of[]),
+  // plus the other half from lane ^ 32; written for the dK / dV kernel,
+  // which runs after this one
+  float dlt = 0.0f;
+  {
+    const int64_t t = sv.qstart + (qvalid ? qrow : 0);
+    const bf16* opo = a.o + t * a.o_st + (int64_t)h * a.o_sh + (lane >> 5) * 8;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const bf16x8 ov = qvalid ? *reinterpret_cast<const bf16x8*>(opo + 16 * s) : bf16x8{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dlt = fmaf((float)ov[e], (float)of[s][e], dlt);
+    }
+    dlt += __shfl_xor(dlt, 32);
+  }
+  float lse2 = INFINITY;
   if (qvalid) {
     const int64_t li = bw_lse_index(a, b, h, sv.qstart, qrow);
     lse2 = lse_log2(a.lse[li]);
-    dlt = a.delta[li];
+    if (lane < 32) a.delta[li] = dlt;
   }
   f32x16 dq[D / 32];
 #pragma unroll
@@ -767,11 +749,10 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
 
 template <int D>
 static hipError_t launch_bwd(const BwdArgs& a, int max_sq, int max_skv, hipStream_t stream) {
-  const int64_t rows = a.total_rows * a.Hq;
-  if (rows > 0) {
-    const int64_t per_wg = (int64_t)kBwWaves * DeltaShape<D>::kRows;
-    hipLaunchKernelGGL(fa_bwd_delta_kernel<D>, dim3((unsigned)((rows + per_wg - 1) / per_wg)), dim3(kBwThreads), 0,
-                       stream, a);
+  // dQ first: it also writes Delta, which the dK / dV kernel reads
+  if (max_sq > 0) {
+    hipLaunchKernelGGL(fa_bwd_dq_kernel<D>, dim3(a.B * a.Hq, (max_sq + kBwRowsQ - 1) / kBwRowsQ),
+                       dim3(kBwThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -783,12 +764,6 @@ static hipError_t launch_bwd(const BwdArgs& a, int max_sq, int max_skv, hipStrea
       const dim3 grid(a.B * a.Hkv, (max_skv + kBwKeys - 1) / kBwKeys);
       hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, 0>), grid, dim3(kBwThreads), 0, stream, a);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (max_sq > 0) {
-    hipLaunchKernelGGL(fa_bwd_dq_kernel<D>, dim3(a.B * a.Hq, (max_sq + kBwRowsQ - 1) / kBwRowsQ),
-                       dim3(kBwThreads), 0, stream, a);
   }
   return hipGetLastError();
 }

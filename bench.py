@@ -279,7 +279,7 @@ def build_workload(cfg: int, flex: str, torch, synth, fa, page_size: int = 64, l
             {"B": B, "H": H, "S": S, "D": D, "mod": flex}, None
     if cfg == 7:
         # backward of the default batch: the forward runs once beforehand for
-        # O and LSE; a step is one fa_bwd_varlen call (Delta, dK/dV, dQ)
+        # O and LSE; a step is one fa_bwd_varlen call (dQ with Delta, then dK/dV)
         lens = synth.varlen_lengths(synth.seed_for(2))
         d = synth.make_varlen(lens, lens, 16, 16, 128, 128, seed=synth.seed_for(2), device=dev)
         T = sum(lens)
