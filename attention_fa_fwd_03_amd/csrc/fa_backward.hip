@@ -218,14 +218,14 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
     if (tid < kBwTile) {
       const int r = min(r0 + tid, sv.sq - 1);
       const int64_t li = bw_lse_index(a, b, h, sv.qstart, r);
-      ld_lse = lse_log2(a.lse[li]);
+      ld_lse = a.lse[li];
       ld_delta = a.delta[li];
     }
   };
   auto publish = [&](int sb) {
     if (tid < kBwTile) {
       float FA_LDS* lp = reinterpret_cast<float FA_LDS*>(stage_ptr(sb) + 2 * kTileB);
-      lp[tid] = ld_lse;
+      lp[tid] = lse_log2(ld_lse);
       lp[kBwTile + tid] = ld_delta;
     }
   };
@@ -451,14 +451,14 @@ void fa_bwd_dkdv16_kernel(const BwdArgs a) {
     if (tid < kBwTile) {
       const int64_t l0 = bw_lse_index(a, b, h, sv.qstart, 0);   // rows of one (sequence, head) are contiguous
       const int r = min(r0 + tid, sv.sq - 1);
-      ld_lse = lse_log2(a.lse[l0 + r]);
+      ld_lse = a.lse[l0 + r];
       ld_delta = a.delta[l0 + r];
     }
   };
   auto publish = [&](int sb) {
     if (tid < kBwTile) {
       float FA_LDS* lp = reinterpret_cast<float FA_LDS*>(stage_ptr(sb) + 2 * kTileB);
-      lp[tid] = ld_lse;
+      lp[tid] = lse_log2(ld_lse);
       lp[kBwTile + tid] = ld_delta;
     }
   };
