@@ -708,6 +708,9 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   if (total_q >= kI32 || total_k >= kI32) return fail(FA_ERR_LIMIT, "token counts must stay below 2^31");
   if (B * Hq >= kI32 || B * Hkv >= 65536 * 16384) return fail(FA_ERR_LIMIT, "B*H exceeds the grid limit");
   if (max_sq / 128 >= 65535 || max_sk / 64 >= 65535) return fail(FA_ERR_LIMIT, "sequence length exceeds the grid limit");
+  // the kernels' tile copies take 32-bit offsets of up to 63 rows
+  if (Hq * std::max(d_qk, d_v) >= (1 << 24))
+    return fail(FA_ERR_LIMIT, "Hq * head dim must stay below 2^24 for the backward");
   Mods m;
   if ((rc = read_mods(mods, d_qk, max_sq, max_sk, &m))) return rc;
   if (m.flags & (FA_ALIBI | FA_SOFTCAP | FA_BLOCK_MASK))

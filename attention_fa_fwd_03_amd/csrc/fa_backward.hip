@@ -82,7 +82,7 @@ __device__ __forceinline__ int swz_bw16(int r) {
 }
 
 // 64 rows x D bf16 of a packed tensor -> swizzled LDS tile, one 1 KB
-// global_load_lds per wavefront instruction (lane l fills 16 bytes at
+// buffer load to LDS per wavefront instruction (lane l fills 16 bytes at
 // 16 l of its KB: tile row r, stored chunk pos = source chunk pos ^ swz(r),
 // swz_bw16 when ALT).  Rows at or past nrows re-read the last row (their
 // results are masked).
@@ -113,13 +113,19 @@ struct RowStager {
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) buffer_to_lds16(rs, off[i], tile + (wave * kPerWave + i) * 1024);
   }
-  __device__ __forceinline__ void issue(const bf16* base, int64_t st, int r0, int nrows, char FA_LDS* tile,
-                                        int wave) const {
+  // Tiles that may run past the sequence's end: the same buffer copies, rows
+  // at or past nrows re-reading row nrows - 1.  Offsets count from row r0
+  // (at most 63 rows of a stride below 2^24 elements: below 2^31 bytes).
+  // Only buffer copies are used: a global_load_lds anywhere in a loop makes
+  // the compiler wait for every LDS read in it with lgkmcnt(0).
+  __device__ __forceinline__ void issue_clamped(const bf16* base, int64_t st, int r0, int nrows, char FA_LDS* tile,
+                                                int wave) const {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)r0 * st);
+    const int last = nrows - 1 - r0;
 #pragma unroll
-    for (int i = 0; i < kPerWave; ++i) {
-      const int r = min(r0 + row[i], nrows - 1);
-      global_to_lds16(base + (int64_t)r * st + col[i], tile + (wave * kPerWave + i) * 1024);
-    }
+    for (int i = 0; i < kPerWave; ++i)
+      buffer_to_lds16(rs, ((unsigned)min(row[i], last) * (unsigned)st + (unsigned)col[i]) * 2u,
+                      tile + (wave * kPerWave + i) * 1024);
   }
 };
 
@@ -213,8 +219,8 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
     const int h = g * a.group + n / nqb;
     const int r0 = (qb0 + n % nqb) * kBwTile;
     char FA_LDS* sp = stage_ptr(sb);
-    st.issue(a.q + sv.qstart * a.q_st + (int64_t)h * a.q_sh, a.q_st, r0, sv.sq, sp, wave);
-    st.issue(a.dout + sv.qstart * a.o_st + (int64_t)h * a.o_sh, a.o_st, r0, sv.sq, sp + kTileB, wave);
+    st.issue_clamped(a.q + sv.qstart * a.q_st + (int64_t)h * a.q_sh, a.q_st, r0, sv.sq, sp, wave);
+    st.issue_clamped(a.dout + sv.qstart * a.o_st + (int64_t)h * a.o_sh, a.o_st, r0, sv.sq, sp + kTileB, wave);
     if (tid < kBwTile) {
       const int r = min(r0 + tid, sv.sq - 1);
       const int64_t li = bw_lse_index(a, b, h, sv.qstart, r);
@@ -432,7 +438,6 @@ void fa_bwd_dkdv16_kernel(const BwdArgs a) {
   unsigned offq[RowStager<D, true>::kPerWave], offo[RowStager<D, true>::kPerWave];
   st.offsets(a.q_st, offq);
   st.offsets(a.o_st, offo);
-  const bool whole_ok = a.q_st < (1 << 24) && a.o_st < (1 << 24);
   auto stage_ptr = [&](int i) { return lds + i * kStage; };
   float ld_lse = 0.0f, ld_delta = 0.0f;
   auto issue = [&](int n, int sb) {
@@ -441,12 +446,12 @@ void fa_bwd_dkdv16_kernel(const BwdArgs a) {
     char FA_LDS* sp = stage_ptr(sb);
     const bf16* qb = a.q + sv.qstart * a.q_st + (int64_t)h * a.q_sh;
     const bf16* ob = a.dout + sv.qstart * a.o_st + (int64_t)h * a.o_sh;
-    if (whole_ok && r0 + kBwTile <= sv.sq) {
+    if (r0 + kBwTile <= sv.sq) {
       st.issue_whole(qb, a.q_st, r0, offq, sp, wave);
       st.issue_whole(ob, a.o_st, r0, offo, sp + kTileB, wave);
     } else {
-      st.issue(qb, a.q_st, r0, sv.sq, sp, wave);
-      st.issue(ob, a.o_st, r0, sv.sq, sp + kTileB, wave);
+      st.issue_clamped(qb, a.q_st, r0, sv.sq, sp, wave);
+      st.issue_clamped(ob, a.o_st, r0, sv.sq, sp + kTileB, wave);
     }
     if (tid < kBwTile) {
       const int64_t l0 = bw_lse_index(a, b, h, sv.qstart, 0);   // rows of one (sequence, head) are contiguous
@@ -485,20 +490,34 @@ void fa_bwd_dkdv16_kernel(const BwdArgs a) {
     if (a.win_right >= 0) full = full && kw1 <= r0 + delta_al + a.win_right;
     if (a.win_left >= 0) full = full && kw0 >= r0 + kBwTile - 1 + delta_al - a.win_left;
     // S and dP of all 64 rows (four 16-row blocks) first, then P and dS,
-    // then the dV / dK products: the vector work of one half can run under
-    // the products of the other
+    // then the dV / dK products.  Each product's A fragment is read kAhead
+    // products before it, in a fixed order (one scheduling barrier per
+    // product), so a wavefront waits only for reads kAhead products old.
+    constexpr int NSP = 2 * 4 * NS;            // S and dP products: (block rb, step, S | dP)
+    constexpr int NKV = 2 * 2 * ND;            // dV and dK products: (half, block d, dV | dK)
+    constexpr int kAhead = 4;
+    auto sp_read = [&](int i) {
+      const int rb = i / (2 * NS), stp = (i >> 1) % NS;
+      const int r = rb * 16 + (lane & 15);
+      return lds_read_b128(((i & 1) ? dt : qt) + r * kRow + (((4 * stp + grp) ^ swz_bw16(r)) << 4));
+    };
+    auto kv_read = [&](int i) {
+      return tr_fragment16<kRow>((i & 1) ? qt : dt, i / (2 * ND), (i >> 1) % ND, lane);
+    };
     f32x4 s[4], dp[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) s[rb] = dp[rb] = f32x4{};
+    bf16x8 af[NSP];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int i = 0; i < kAhead; ++i) af[i] = sp_read(i);
 #pragma unroll
-      for (int stp = 0; stp < NS; ++stp) {
-        const int r = rb * 16 + (lane & 15);
-        const int off = r * kRow + (((4 * stp + grp) ^ swz_bw16(r)) << 4);
-        s[rb] = bw_mfma16(lds_read_b128(qt + off), kf[stp], s[rb]);
-        dp[rb] = bw_mfma16(lds_read_b128(dt + off), vf[stp], dp[rb]);
-      }
+    for (int i = 0; i < NSP; ++i) {
+      if (i + kAhead < NSP) af[i + kAhead] = sp_read(i + kAhead);
+      const int rb = i / (2 * NS), stp = (i >> 1) % NS;
+      if (i & 1) dp[rb] = bw_mfma16(af[i], vf[stp], dp[rb]);
+      else s[rb] = bw_mfma16(af[i], kf[stp], s[rb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // P (in place of S): accumulator register i of block rb is row
     // 16 rb + 4 grp + i
 #pragma unroll
@@ -530,14 +549,19 @@ void fa_bwd_dkdv16_kernel(const BwdArgs a) {
         dsf[rb >> 1][(rb & 1) * 4 + i] = (bf16)(s[rb][i] * (dp[rb][i] - d4[i]));
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 tf[NKV];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) tf[i] = kv_read(i);
     // dV^T += dO^T P and dK^T += Q^T dS over the two 32-row halves
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        dv[d] = bw_mfma16(tr_fragment16<kRow>(dt, hf, d, lane), pf[hf], dv[d]);
-        dk[d] = bw_mfma16(tr_fragment16<kRow>(qt, hf, d, lane), dsf[hf], dk[d]);
-      }
+    for (int i = 0; i < NKV; ++i) {
+      if (i + kAhead < NKV) tf[i + kAhead] = kv_read(i + kAhead);
+      const int hf = i / (2 * ND), d = (i >> 1) % ND;
+      if (i & 1) dk[d] = bw_mfma16(tf[i], dsf[hf], dk[d]);
+      else dv[d] = bw_mfma16(tf[i], pf[hf], dv[d]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (n + 1 < nsteps) {
       FA_WAIT_VMCNT(0);
       publish(sb ^ 1);
@@ -661,7 +685,7 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
   // stride here: D_qk = D_v)
   unsigned offk[RowStager<D>::kPerWave];
   st.offsets(a.k_st, offk);
-  const bool whole_ok = a.k_st == a.v_st && a.k_st < (1 << 24);
+  const bool whole_ok = a.k_st == a.v_st;
   auto stage_ptr = [&](int i) { return lds + i * kStage; };
   const bf16* kbase = a.k + sv.kstart * a.k_st + (int64_t)g * a.k_sh;
   const bf16* vbase = a.v + sv.kstart * a.v_st + (int64_t)g * a.v_sh;
@@ -670,8 +694,8 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
       st.issue_whole(kbase, a.k_st, t * kBwTile, offk, stage_ptr(sb), wave);
       st.issue_whole(vbase, a.v_st, t * kBwTile, offk, stage_ptr(sb) + kTileB, wave);
     } else {
-      st.issue(kbase, a.k_st, t * kBwTile, sv.skv, stage_ptr(sb), wave);
-      st.issue(vbase, a.v_st, t * kBwTile, sv.skv, stage_ptr(sb) + kTileB, wave);
+      st.issue_clamped(kbase, a.k_st, t * kBwTile, sv.skv, stage_ptr(sb), wave);
+      st.issue_clamped(vbase, a.v_st, t * kBwTile, sv.skv, stage_ptr(sb) + kTileB, wave);
     }
   };
   if (t_begin <= t_end) {

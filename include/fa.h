@@ -248,6 +248,7 @@ size_t fa_fwd_paged_workspace_size(int64_t B, int64_t total_q, int64_t max_seqle
  * dK and dV is written (zeros where no gradient flows).  Needs a device
  * workspace of fa_bwd_workspace_size(...) bytes (Delta, fp32), else
  * FA_ERR_WORKSPACE; outputs must not overlap the inputs or each other.
+ * Hq * d must stay below 2^24 (FA_ERR_LIMIT).
  * Deterministic: every output element is summed in a fixed order.
  */
 int fa_bwd_dense(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,

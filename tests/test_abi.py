@@ -290,6 +290,7 @@ def _bwd(**kw):
     (dict(wsb=8), -4, "workspace"),
     (dict(Hq=3, Hkv=2), -1, "multiple"),
     (dict(Sq=-1), -1, ">= 0"),
+    (dict(Hq=131072, Hkv=131072, dqk=128, dv=128), -3, "2^24"),
 ])
 def test_bwd_rejects(kw, code, frag):
     rc, msg = _bwd(**kw)
