@@ -135,10 +135,14 @@ struct Fp8Stager {
 // registers, no conversion): instruction n covers LDS bytes [1024 n, +1024),
 // lane l fills 16 bytes at 16 l: tile row r, stored chunk pos = source
 // chunk pos ^ swz8(r).  Head-major pages read the chunk from the key's row;
-// vectorised pages from column pos ^ swz8(r) of the page.  Whole tiles
-// inside one page take one scalar page lookup, other tiles a per-row one
-// (rows past the sequence re-read its last key).
-template <int D, bool VEC>
+// vectorised pages from column pos ^ swz8(r) of the page.  Rows past the
+// sequence re-read its last key.  BIGP (pages of at least BN keys): every
+// tile lies in one page, found by one scalar lookup, and is copied by
+// buffer loads with 32-bit offsets from that page.  Smaller pages take a
+// per-row lookup and 64-bit addresses (global_load_lds); a kernel that
+// contains one waits for all its LDS reads with lgkmcnt(0), so the two
+// cases are separate kernels.
+template <int D, bool VEC, bool BIGP>
 struct Fp8KDma {
   static constexpr int kPerWave = BN * D / 1024 / NWAVES;
   static_assert(kPerWave >= 1 && (BN * D) % (1024 * NWAVES) == 0, "whole 1 KB pieces per wavefront");
@@ -159,7 +163,26 @@ struct Fp8KDma {
   __device__ __forceinline__ void issue(const PrefillArgs& a, const SeqView& sv, const uint8_t* base, int k0,
                                         bool fast, char FA_LDS* tile, int wave, int lane) const {
     const int pmask = (1 << a.page_shift) - 1;
-    if (fast) {
+    if (BIGP) {
+      int page = load_uniform_i32(a.block_table, (int64_t)sv.b * a.max_pages + (k0 >> a.page_shift));
+      page = min(max(page, 0), a.num_pages - 1);
+      const uint8_t* pb = base + (int64_t)page * a.k_pg + (int64_t)sv.g * a.k_sh;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(pb);
+      if (fast) {
+        const unsigned tb = (unsigned)(k0 & pmask) * (VEC ? 16 : D);
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i) buffer_to_lds16(rs, tb + off[i], tile + (wave * kPerWave + i) * 1024);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i) {
+          int row, col;
+          place(i, wave, lane, row, col);
+          const unsigned j = (unsigned)(min(k0 + row, sv.skv - 1) & pmask);
+          buffer_to_lds16(rs, VEC ? ((unsigned)col << (a.page_shift + 4)) + j * 16 : j * D + col * 16,
+                          tile + (wave * kPerWave + i) * 1024);
+        }
+      }
+    } else if (fast) {
       int page = load_uniform_i32(a.block_table, (int64_t)sv.b * a.max_pages + (k0 >> a.page_shift));
       page = min(max(page, 0), a.num_pages - 1);
       const uint8_t* tb = base + (int64_t)page * a.k_pg + (int64_t)sv.g * a.k_sh + (k0 & pmask) * (VEC ? 16 : D);
@@ -241,10 +264,9 @@ struct Fp8VecV {
 
 // FP8 V tile of head-major pages, staged by LDS DMA as E4M3 bytes: tile
 // rows of D bytes (key-major), chunk c of row r at c ^ swzv8<D>(r), read with
-// the transposing byte read.  Whole tiles inside one page take one scalar
-// page lookup, other tiles a per-row one (rows past the sequence re-read its
-// last key, whose p is 0).
-template <int D>
+// the transposing byte read.  Rows past the sequence re-read its last key,
+// whose p is 0.  Page lookups and BIGP as for K.
+template <int D, bool BIGP>
 struct Fp8VDma {
   static constexpr int kPerWave = BN * D / 1024 / NWAVES;
   static_assert(kPerWave >= 1 && (BN * D) % (1024 * NWAVES) == 0, "whole 1 KB pieces per wavefront");
@@ -265,7 +287,24 @@ struct Fp8VDma {
   __device__ __forceinline__ void issue(const PrefillArgs& a, const SeqView& sv, const uint8_t* base, int k0,
                                         bool fast, char FA_LDS* tile, int wave, int lane) const {
     const int pmask = (1 << a.page_shift) - 1;
-    if (fast) {
+    if (BIGP) {
+      int page = load_uniform_i32(a.block_table, (int64_t)sv.b * a.max_pages + (k0 >> a.page_shift));
+      page = min(max(page, 0), a.num_pages - 1);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)page * a.v_pg + (int64_t)sv.g * a.v_sh);
+      if (fast) {
+        const unsigned tb = (unsigned)(k0 & pmask) * D;
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i) buffer_to_lds16(rs, tb + off[i], tile + (wave * kPerWave + i) * 1024);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i) {
+          int row, col;
+          place(i, wave, lane, row, col);
+          const unsigned j = (unsigned)(min(k0 + row, sv.skv - 1) & pmask);
+          buffer_to_lds16(rs, j * D + col * 16, tile + (wave * kPerWave + i) * 1024);
+        }
+      }
+    } else if (fast) {
       int page = load_uniform_i32(a.block_table, (int64_t)sv.b * a.max_pages + (k0 >> a.page_shift));
       page = min(max(page, 0), a.num_pages - 1);
       const uint8_t* tb = base + (int64_t)page * a.v_pg + (int64_t)sv.g * a.v_sh + (k0 & pmask) * D;
@@ -301,7 +340,7 @@ __device__ __forceinline__ i32x8 cat8(i32x4 x, i32x4 y) {
   return i32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
 }
 
-template <int DQK, int DV, bool FP8, bool PAGED, bool VEC, bool Q8, int MODS>
+template <int DQK, int DV, bool FP8, bool PAGED, bool VEC, bool Q8, int MODS, bool BIGP>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_prefill_kernel(const PrefillArgs a) {
   // bf16 K/V go to fa_prefill_bf16_kernel.  Score mods come in one variant
@@ -463,14 +502,15 @@ void fa_prefill_kernel(const PrefillArgs a) {
   };
 
   const int64_t vpg = a.v_pg;
-  const bool small_pages = PAGED && a.page_shift < 6;
+  // pages of fewer than BN keys (not BIGP): per-row page lookups
+  constexpr bool small_pages = PAGED && !BIGP;
   auto fast_tile = [&](int k0) { return k0 + BN <= sv.skv && !small_pages; };
 
-  Fp8KDma<DQK, VEC> k8;
-  Fp8VDma<DV> v8d;
+  Fp8KDma<DQK, VEC, BIGP> k8;
+  Fp8VDma<DV, BIGP> v8d;
   Fp8Stager<DV, PAGED> v8r;
   Fp8VecV<DV> vv8;
-  constexpr int kDmaPerTile = Fp8KDma<DQK, VEC>::kPerWave + (VREG ? 0 : Fp8VDma<DV>::kPerWave);
+  constexpr int kDmaPerTile = Fp8KDma<DQK, VEC, BIGP>::kPerWave + (VREG ? 0 : Fp8VDma<DV, BIGP>::kPerWave);
   k8.init(a.page_shift, wave, lane);
   if (!VREG) v8d.init(wave, lane);
   else if (!VEC) v8r.init(a.v_st, tid);
@@ -762,10 +802,15 @@ void fa_prefill_kernel(const PrefillArgs a) {
 template <int DQK, int DV, bool FP8, bool PAGED, bool VEC, int MODS>
 static hipError_t launch_prefill(const PrefillArgs& a, int n_bh, int n_qtiles, hipStream_t stream) {
   dim3 grid((n_bh + 7) / 8 * 8, n_qtiles);
-  if (FP8 && a.q_descale)
-    hipLaunchKernelGGL((fa_prefill_kernel<DQK, DV, FP8, PAGED, VEC, FP8, MODS>), grid, dim3(NTHREADS), 0, stream, a);
+  const bool q8 = FP8 && a.q_descale, bigp = a.page_shift >= 6;
+  if (q8 && bigp)
+    hipLaunchKernelGGL((fa_prefill_kernel<DQK, DV, FP8, PAGED, VEC, FP8, MODS, true>), grid, dim3(NTHREADS), 0, stream, a);
+  else if (q8)
+    hipLaunchKernelGGL((fa_prefill_kernel<DQK, DV, FP8, PAGED, VEC, FP8, MODS, false>), grid, dim3(NTHREADS), 0, stream, a);
+  else if (bigp)
+    hipLaunchKernelGGL((fa_prefill_kernel<DQK, DV, FP8, PAGED, VEC, false, MODS, true>), grid, dim3(NTHREADS), 0, stream, a);
   else
-    hipLaunchKernelGGL((fa_prefill_kernel<DQK, DV, FP8, PAGED, VEC, false, MODS>), grid, dim3(NTHREADS), 0, stream, a);
+    hipLaunchKernelGGL((fa_prefill_kernel<DQK, DV, FP8, PAGED, VEC, false, MODS, false>), grid, dim3(NTHREADS), 0, stream, a);
   return hipGetLastError();
 }
 
