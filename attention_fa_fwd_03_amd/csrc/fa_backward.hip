@@ -710,17 +710,26 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
     const char FA_LDS* vt = kt + kTileB;
     const int k0 = t * kBwTile;
 
-    // S^T and dP^T for keys [32 kb, +32) of the tile
+    // S^T and dP^T for keys [32 kb, +32) of the tile; each product's K / V
+    // fragment is read kAheadQ products before it, in a fixed order
+    constexpr int NP = 4 * (D / 16);           // (step, key block, S | dP)
+    constexpr int kAheadQ = 2;                 // 4 measured the same, 6 spills
+    auto kv_frag = [&](int i) {
+      const int stp = i >> 2, kb = (i >> 1) & 1;
+      const int r = kb * 32 + (lane & 31);
+      return lds_read_b128(((i & 1) ? vt : kt) + r * kRow + (((2 * stp + (lane >> 5)) ^ swz<kRow>(r)) << 4));
+    };
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    bf16x8 fr[NP];
 #pragma unroll
-    for (int stp = 0; stp < D / 16; ++stp) {
+    for (int i = 0; i < kAheadQ; ++i) fr[i] = kv_frag(i);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int r = kb * 32 + (lane & 31);
-        const int off = r * kRow + (((2 * stp + (lane >> 5)) ^ swz<kRow>(r)) << 4);
-        s[kb] = mfma32(lds_read_b128(kt + off), qf[stp], s[kb]);
-        dp[kb] = mfma32(lds_read_b128(vt + off), of[stp], dp[kb]);
-      }
+    for (int i = 0; i < NP; ++i) {
+      if (i + kAheadQ < NP) fr[i + kAheadQ] = kv_frag(i + kAheadQ);
+      const int stp = i >> 2, kb = (i >> 1) & 1;
+      if (i & 1) dp[kb] = mfma32(fr[i], of[stp], dp[kb]);
+      else s[kb] = mfma32(fr[i], qf[stp], s[kb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // P^T in place of S^T (register i of key block kb: key 32 kb + 8 (i/4) +
     // 4 (lane/32) + i%4), then the mask, then dS^T; tiles inside every row's
