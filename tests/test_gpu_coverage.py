@@ -354,3 +354,20 @@ def test_seeded_varlen_sweep(i):
     o, lse = _varlen_run(d, mods, D)
     o_ref, l_ref = oracle.attention_varlen(f64(d["q"]), f64(d["k"]), f64(d["v"]), d["cu_q"], d["cu_k"], dict(mods))
     _cmp_packed(o, lse, o_ref, l_ref, TOL_O_BF16, f"sweep {i}: lq={lq} lk={lk} Hq={Hq} Hkv={Hkv} D={D} {mods}")
+
+
+@pytest.mark.parametrize("vec", [False, True])
+@pytest.mark.parametrize("small,big", [(16, 64), (32, 128)])
+def test_paged_fp8_prefill_page_size_is_bitwise_invariant(small, big, vec):
+    """Pages of fewer than 64 keys take per-row page lookups, pages of 64 or
+    more one buffer descriptor per tile (two kernel variants): the same
+    logical cache (same seed, so the same E4M3 bytes, queries and descales)
+    in either page size gives the same bytes of O and LSE.  Lengths leave
+    ragged tails; one query chunk is shorter than its keys."""
+    lq, lk = [200, 64, 1, 130], [200, 300, 65, 130]
+    runs = []
+    for ps in (small, big):
+        d = synth.make_paged(lq, lk, 8, 2, 192, 128, page_size=ps, seed=463, extra_pages=4)
+        runs.append((_paged_vec_run if vec else _paged_run)(d, dict(causal=True), 128))
+    (o1, l1), (o2, l2) = runs
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), f"pages {small} vs {big} vec={vec}"
