@@ -171,13 +171,16 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  // causal: key blocks near the start see the most rows and come first (y
-  // ascending); the head rotates by one slot of 8 per level as in the dQ grid
-  const int bg = a.causal ? ((int)blockIdx.x + 8 * (int)blockIdx.y) % (int)gridDim.x : (int)blockIdx.x;
+  // the forward's workgroup order (wg_tile) with key blocks for query
+  // tiles: causal calls take key blocks near the start first (they see the
+  // most rows), an XCD's (sequence, kv-head) slots in groups of 8 with the
+  // slot rotated per level; otherwise all key blocks of one slot in a row
+  int bg, lvl;
+  wg_tile(a.causal != 0, bg, lvl);
   if (bg >= a.B * a.Hkv) return;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const BwSeq sv = bw_seq(a, b);
-  const int k0 = blockIdx.y * kBwKeys;
+  const int k0 = ((int)gridDim.y - 1 - lvl) * kBwKeys;
   if (k0 >= sv.skv) return;
   const int key = k0 + wave * 32 + (lane & 31);
   const bool kvalid = key < sv.skv;
@@ -386,13 +389,14 @@ void fa_bwd_dkdv16_kernel(const BwdArgs a) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int grp = lane >> 4;
-  // causal: key blocks near the start see the most rows and come first (y
-  // ascending); the head rotates by one slot of 8 per level
-  const int bg = a.causal ? ((int)blockIdx.x + 8 * (int)blockIdx.y) % (int)gridDim.x : (int)blockIdx.x;
+  // workgroup order as in the 32-key kernel (wg_tile, key blocks near the
+  // start first for causal calls)
+  int bg, lvl;
+  wg_tile(a.causal != 0, bg, lvl);
   if (bg >= a.B * a.Hkv) return;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const BwSeq sv = bw_seq(a, b);
-  const int k0 = blockIdx.y * kBw16Keys;
+  const int k0 = ((int)gridDim.y - 1 - lvl) * kBw16Keys;
   if (k0 >= sv.skv) return;
   const int key = k0 + wave * 16 + (lane & 15);
   const bool kvalid = key < sv.skv;
@@ -602,15 +606,15 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  // causal: the head rotates by one slot of 8 per level, so that a CU does
-  // not meet the same (sequence, head) at every level it serves
-  const int bh = a.causal ? ((int)blockIdx.x + 8 * (int)blockIdx.y) % (int)gridDim.x : (int)blockIdx.x;
+  // the forward's workgroup order (wg_tile): causal calls start with the
+  // longest query tiles (the last ones), so the grid ends on short tiles,
+  // an XCD's (sequence, head) slots in groups of 8 with the slot rotated per
+  // level; otherwise all query tiles of one slot in a row
+  int bh, qt;
+  wg_tile(a.causal != 0, bh, qt);
   if (bh >= a.B * a.Hq) return;
   const int b = bh / a.Hq, h = bh % a.Hq, g = h / a.group;
   const BwSeq sv = bw_seq(a, b);
-  // causal: the longest query tiles (the last ones) start first, so the
-  // grid ends on short tiles instead of long ones
-  const int qt = a.causal ? (int)gridDim.y - 1 - (int)blockIdx.y : (int)blockIdx.y;
   const int q0 = qt * kBwRowsQ;
   if (q0 >= sv.sq) return;
   const int q1 = min(q0 + kBwRowsQ, sv.sq);
@@ -784,17 +788,18 @@ template <int D>
 static hipError_t launch_bwd(const BwdArgs& a, int max_sq, int max_skv, hipStream_t stream) {
   // dQ first: it also writes Delta, which the dK / dV kernel reads
   if (max_sq > 0) {
-    hipLaunchKernelGGL(fa_bwd_dq_kernel<D>, dim3(a.B * a.Hq, (max_sq + kBwRowsQ - 1) / kBwRowsQ),
+    // grid x: slots rounded up to a multiple of the 8 XCDs (wg_tile's map)
+    hipLaunchKernelGGL(fa_bwd_dq_kernel<D>, dim3((a.B * a.Hq + 7) / 8 * 8, (max_sq + kBwRowsQ - 1) / kBwRowsQ),
                        dim3(kBwThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (max_skv > 0) {
     if constexpr (D > 64) {
-      const dim3 grid(a.B * a.Hkv, (max_skv + kBw16Keys - 1) / kBw16Keys);
+      const dim3 grid((a.B * a.Hkv + 7) / 8 * 8, (max_skv + kBw16Keys - 1) / kBw16Keys);
       hipLaunchKernelGGL((fa_bwd_dkdv16_kernel<D>), grid, dim3(kBwThreads), 0, stream, a);
     } else {
-      const dim3 grid(a.B * a.Hkv, (max_skv + kBwKeys - 1) / kBwKeys);
+      const dim3 grid((a.B * a.Hkv + 7) / 8 * 8, (max_skv + kBwKeys - 1) / kBwKeys);
       hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, 0>), grid, dim3(kBwThreads), 0, stream, a);
     }
   }

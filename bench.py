@@ -57,7 +57,7 @@ COPY_BYTES = 256 << 20        # calibration copy for the HBM byte counters
 # dominant kernel of each kind, matched as a substring of the kernel name
 # (the bf16 prefill is fa_prefill_bf16_kernel, the FP8-cache one fa_prefill_kernel)
 DOMINANT = {"prefill": "fa_prefill_bf16_kernel", "prefill_fp8": "fa_prefill_kernel", "decode": "fa_decode_kernel",
-            "kvwrite": "fa_kv_write_kernel", "backward": "fa_bwd_dkdv_kernel"}
+            "kvwrite": "fa_kv_write_kernel", "backward": "fa_bwd_dkdv"}
 KERNEL_SOURCES = {
     "prefill": ["attention_fa_fwd_03_amd/csrc/fa_prefill_bf16.hip", "attention_fa_fwd_03_amd/csrc/fa_prefill_common.h",
                 "attention_fa_fwd_03_amd/csrc/fa_device.h", "attention_fa_fwd_03_amd/csrc/fa_kernels.h"],
