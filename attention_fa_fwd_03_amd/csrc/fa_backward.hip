@@ -173,10 +173,12 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   // the forward's workgroup order (wg_tile) with key blocks for query
   // tiles: causal calls take key blocks near the start first (they see the
-  // most rows), an XCD's (sequence, kv-head) slots in groups of 8 with the
-  // slot rotated per level; otherwise all key blocks of one slot in a row
+  // most rows), an XCD's (sequence, kv-head) slots in groups of 4 (the
+  // backward's units are small enough to balance in smaller groups, which
+  // keep fewer slots' Q / dO tiles streaming through an L2) with the slot
+  // rotated per level; otherwise all key blocks of one slot in a row
   int bg, lvl;
-  wg_tile(a.causal != 0, bg, lvl);
+  wg_tile<4>(a.causal != 0, bg, lvl);
   if (bg >= a.B * a.Hkv) return;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const BwSeq sv = bw_seq(a, b);
@@ -392,7 +394,7 @@ void fa_bwd_dkdv16_kernel(const BwdArgs a) {
   // workgroup order as in the 32-key kernel (wg_tile, key blocks near the
   // start first for causal calls)
   int bg, lvl;
-  wg_tile(a.causal != 0, bg, lvl);
+  wg_tile<4>(a.causal != 0, bg, lvl);
   if (bg >= a.B * a.Hkv) return;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const BwSeq sv = bw_seq(a, b);
@@ -608,10 +610,10 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   // the forward's workgroup order (wg_tile): causal calls start with the
   // longest query tiles (the last ones), so the grid ends on short tiles,
-  // an XCD's (sequence, head) slots in groups of 8 with the slot rotated per
+  // an XCD's (sequence, head) slots in groups of 4 with the slot rotated per
   // level; otherwise all query tiles of one slot in a row
   int bh, qt;
-  wg_tile(a.causal != 0, bh, qt);
+  wg_tile<4>(a.causal != 0, bh, qt);
   if (bh >= a.B * a.Hq) return;
   const int b = bh / a.Hq, h = bh % a.Hq, g = h / a.group;
   const BwSeq sv = bw_seq(a, b);

@@ -130,6 +130,9 @@ __device__ __forceinline__ int64_t tile_base(const PrefillArgs& a, const SeqView
 //    so the head of each slot rotates per level.
 //  - otherwise (equal cost): head major, all query tiles of one head in a
 //    row, so the workgroups that read the same K/V share one XCD's L2.
+// G is the group size: 8 for the forward kernels; the backward's smaller
+// units balance in groups of 4.
+template <int G = 8>
 __device__ __forceinline__ void wg_tile(bool causal, int& bh, int& qt) {
   const int gx = (int)gridDim.x, gy = (int)gridDim.y;
   if (causal) {
@@ -137,7 +140,6 @@ __device__ __forceinline__ void wg_tile(bool causal, int& bh, int& qt) {
     // within it, and the slot rotated by one per level (without the rotation
     // a CU would meet the same (sequence, head) at every level it serves and
     // inherit that sequence's length as its load)
-    constexpr int G = 8;
     const int i = (int)blockIdx.y * gx + (int)blockIdx.x;
     const int x = i & 7, k = i >> 3;
     const int g = k / (G * gy);
